@@ -1,0 +1,184 @@
+/*
+ * tide.h -- C ABI of a one-GPU (MI355X, gfx950) implementation of two steps of
+ * TIDE's layout-aware FSDP2 collectives:
+ *
+ *   1. the level-1 (node-local) mixed-precision reduce-scatter: L contributor
+ *      sets of per-parameter bf16 gradients, read where they lie, summed in
+ *      fp32 into zero-padded rank-major fp32 shards
+ *      (page 1 "Reduce-scatter: two levels of addition"; page 2 "What shipped";
+ *      page 3 abstract and Figure 6(a));
+ *   2. the all-gather placement step: rank-major bf16 shards written straight
+ *      to their final parameter-major addresses
+ *      (page 1 "All-gather: parameters land at their final address";
+ *      page 3 Figure 5(b), one strided copy per parameter).
+ *
+ * Notation (page 3 "Table 2. Notation"): a parameter group of P tensors,
+ * N ranks, L contributors. Parameter p has T_p true rows along dim 0 and row
+ * length K_p (the product of its remaining dims; 1 for a 1-D tensor). Dim-0
+ * sharding gives every rank R_p = ceil(T_p / N) rows, zero-padded past T_p,
+ * so rank r's piece of p has s_p = R_p * K_p elements; o_p is the prefix sum
+ * of s_q over q < p in the order the parameters were given, and the per-rank
+ * shard has S = sum of s_p elements. Rank r's piece of p sits at element
+ * r * stride + o_p of a rank-major buffer (the order of page 1's worked
+ * example), and holds true rows r * R_p .. min(T_p, (r+1) * R_p) - 1.
+ *
+ * All sizes and offsets are in ELEMENTS (bf16 or fp32 as stated), 64-bit.
+ *
+ * Conventions shared by every call:
+ *   - Every function returns a tide_status; nothing aborts and no C++
+ *     exception crosses this boundary. On a non-OK status,
+ *     tide_last_error_detail() gives a thread-local description.
+ *   - All argument checks happen on the host before anything is enqueued: a
+ *     call that fails has enqueued nothing.
+ *   - Device buffers are owned by the caller and must stay alive until the
+ *     stream has executed the call. The library owns the plan and the small
+ *     device tables it creates for it (freed by tide_plan_destroy).
+ *   - Pointer arrays (grads, params) are host arrays, read during the call
+ *     only. The pointers in them are device pointers.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). The
+ *     device used is the stream's device. The compute calls only enqueue.
+ *   - A plan may be used from several threads and streams at once; it is
+ *     immutable after creation except for internally locked caches.
+ */
+#ifndef TIDE_H
+#define TIDE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tide_plan tide_plan;
+
+typedef enum tide_status {
+    TIDE_OK = 0,
+    TIDE_ERR_INVALID_ARG = 1,   /* null/negative/out-of-range argument, overlapping buffers */
+    TIDE_ERR_ALIGNMENT = 2,     /* bf16 pointer not 2-byte aligned, fp32 pointer not 4-byte aligned */
+    TIDE_ERR_OVERFLOW = 3,      /* a size or offset does not fit int64 */
+    TIDE_ERR_UNSUPPORTED = 4,   /* valid request this library does not serve; caller falls back */
+    TIDE_ERR_NO_MEMORY = 5,     /* host or device allocation failed */
+    TIDE_ERR_HIP = 6            /* a HIP runtime call failed (no GPU, bad stream, launch error) */
+} tide_status;
+
+/* Placement engine (page 1: the all-gather's data movement runs on copy
+ * engines and uses no compute units; page 3 Table 1, AG SM budget 0). */
+typedef enum tide_engine {
+    TIDE_ENGINE_KERNEL = 0,     /* a HIP placement kernel */
+    TIDE_ENGINE_SDMA = 1        /* one hipMemcpy2DAsync per parameter (+1 for a partial rank) */
+} tide_engine;
+
+typedef enum tide_launch_mode {
+    TIDE_LAUNCH_FULL = 0,       /* enough workgroups to fill the GPU */
+    TIDE_LAUNCH_BUDGETED = 1    /* few, short-lived workgroups (page 1 "Why does a communication
+                                   kernel slow a matrix multiply by 69%?": 16 summing + 4 landing
+                                   blocks, single blocks, each living 0.2-0.4 ms) */
+} tide_launch_mode;
+
+/* Launch options. A zero-filled struct (or a NULL pointer) means: full grid,
+ * all ranks. Fields equal to 0 take their defaults. */
+typedef struct tide_launch {
+    int32_t mode;            /* tide_launch_mode */
+    int32_t reduce_blocks;   /* BUDGETED: workgroups of each reduce launch (0 -> 16) */
+    int32_t place_blocks;    /* BUDGETED: workgroups of each placement launch (0 -> 4) */
+    int32_t max_launch_us;   /* BUDGETED: work per launch sized so a workgroup lives about
+                                this long (0 -> 300). Each launch is a separate kernel; no
+                                workgroup ever waits on another. */
+    int32_t rank_begin;      /* first rank whose shard is processed (default 0) */
+    int32_t rank_end;        /* one past the last rank; 0 -> N */
+    int32_t flags;           /* TIDE_FLAG_* */
+    int32_t reserved;        /* must be 0 */
+} tide_launch;
+
+/* Force the element-at-a-time path everywhere (for testing the slow path). */
+#define TIDE_FLAG_SCALAR_PATH 0x1
+
+/*
+ * Build the layout of one parameter group (page 3 Table 2 notation).
+ *   rows[p]    = T_p >= 0 true dim-0 rows of parameter p (P entries)
+ *   row_len[p] = K_p >= 1 (P entries)
+ *   P >= 0 parameters (no upper cap: groups of several hundred tensors are served),
+ *   N >= 1 ranks, L >= 1 contributors (L <= 64).
+ * Host-only: allocates nothing on the GPU (device tables are made on first use
+ * on each device). *out_plan receives a plan to free with tide_plan_destroy.
+ * Errors: INVALID_ARG (bad counts, null arrays when P > 0), OVERFLOW (N*S or a
+ * per-parameter size beyond int64), NO_MEMORY.
+ */
+tide_status tide_plan_create(const int64_t* rows, const int64_t* row_len, int32_t P,
+                             int32_t N, int32_t L, tide_plan** out_plan);
+
+/* Free a plan and its device tables. NULL-safe. No call using it may be in flight. */
+void tide_plan_destroy(tide_plan* plan);
+
+/* Group dimensions: P, N, L and S (per-rank shard elements). Any out pointer may be NULL. */
+tide_status tide_plan_dims(const tide_plan* plan, int32_t* P, int32_t* N, int32_t* L, int64_t* S);
+
+/* Per-parameter layout (page 3 Table 2): T_p, K_p, R_p, s_p, o_p in elements.
+ * Any out pointer may be NULL. INVALID_ARG if p is out of range. */
+tide_status tide_plan_param(const tide_plan* plan, int32_t p, int64_t* rows, int64_t* row_len,
+                            int64_t* R_p, int64_t* s_p, int64_t* o_p);
+
+/* The two addressings of rank r's piece of parameter p (page 1 worked example):
+ *   rank_major  = r * S + o_p            start in a packed rank-major buffer
+ *   param_major = N * o_p + r * s_p      start in the group's parameters laid end to
+ *                                        end, each padded to N * R_p rows
+ *   valid       = true elements in the piece (s_p minus its zero padding)
+ * Any out pointer may be NULL. */
+tide_status tide_plan_map(const tide_plan* plan, int32_t r, int32_t p, int64_t* rank_major,
+                          int64_t* param_major, int64_t* valid);
+
+/*
+ * Level-1 reduce-scatter, bf16 in, fp32 out.
+ *   grads[c * P + p]: device pointer to contributor c's bf16 gradient of parameter
+ *       p, T_p x K_p contiguous, 2-byte aligned (may be NULL when T_p * K_p == 0).
+ *       Read only; gradients are read in place, with no packed copy.
+ *   out: device pointer to N fp32 shards; shard r starts at out + r * out_stride
+ *       (out_stride >= S), 4-byte aligned.
+ * For every rank r in [rank_begin, rank_end), every element of out[r][0..S) is
+ * written exactly once: the fp32 sum over c = 0..L-1, in that order (a left
+ * fold, binary32 round-to-nearest-even, subnormals kept), of the widened bf16
+ * values of the element's true row, or +0.0f for a padded row. Elements
+ * out[r][S..out_stride) and shards outside the range are not touched.
+ * The inputs must not overlap the written output (INVALID_ARG).
+ * Uses one small per-call table uploaded with an async host-to-device copy on
+ * `stream` (skipped when the pointers equal the previous call's).
+ */
+tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t* const* grads,
+                                          float* out, int64_t out_stride, void* stream,
+                                          const tide_launch* launch);
+
+/*
+ * All-gather placement, bf16.
+ *   shards: device pointer to N rank-major bf16 shards, shard r at
+ *       shards + r * shard_stride (shard_stride >= S), 2-byte aligned. Read only.
+ *   params[p]: device pointer to parameter p's storage, T_p x K_p contiguous,
+ *       2-byte aligned (may be NULL when T_p * K_p == 0).
+ * For every rank r in [rank_begin, rank_end), the true rows of rank r's piece
+ * of every parameter are copied bit for bit to rows r * R_p.. of params[p];
+ * padded rows are not written, and nothing else in params is touched.
+ * engine selects the HIP kernel or the SDMA copy path; both write the same
+ * bytes. The parameters must not overlap each other or the shards read.
+ */
+tide_status tide_allgather_place(const tide_plan* plan, const uint16_t* shards,
+                                 int64_t shard_stride, uint16_t* const* params, void* stream,
+                                 int32_t engine, const tide_launch* launch);
+
+/* Kernel launches a call with these options makes (op 0 = reduce-scatter,
+ * 1 = placement with the kernel engine). Host-only. */
+tide_status tide_plan_launch_count(const tide_plan* plan, int32_t op, const tide_launch* launch,
+                                   int64_t* launches);
+
+/* Static text for a status code. */
+const char* tide_status_string(tide_status status);
+
+/* Thread-local description of the last non-OK status returned on this thread. */
+const char* tide_last_error_detail(void);
+
+/* Library ABI version, (major << 16) | minor. */
+int32_t tide_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TIDE_H */

@@ -1,0 +1,25 @@
+"""MI355X-native implementation of TIDE's one-GPU hot path: the level-1
+bf16 -> fp32 reduce-scatter into padded rank-major shards and the all-gather
+placement into parameter storage (C ABI in include/tide.h, HIP kernels for
+gfx950 in csrc/). Importing this package loads libtide.so and fails loudly if
+it has not been built."""
+from ._lib import (  # noqa: F401
+    ENGINE_KERNEL,
+    ENGINE_SDMA,
+    EXPORTS,
+    FLAG_SCALAR_PATH,
+    LAUNCH_BUDGETED,
+    LAUNCH_FULL,
+    LIB_PATH,
+    Launch,
+    Plan,
+    TideError,
+    allgather_place,
+    budgeted,
+    lib,
+    plan_create,
+    reduce_scatter_bf16_fp32,
+    version,
+)
+
+lib()  # load now: no silent fallback exists

@@ -1,0 +1,235 @@
+"""ctypes binding of libtide.so (declared in include/tide.h).
+
+Argument marshalling only: every step of the reduce-scatter and of the
+placement runs in the HIP library. PyTorch supplies device memory and streams.
+The binding refuses to work without the built library; there is no fallback.
+"""
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple, Union
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtide.so")
+
+TIDE_OK = 0
+STATUS_NAMES = {0: "TIDE_OK", 1: "TIDE_ERR_INVALID_ARG", 2: "TIDE_ERR_ALIGNMENT",
+                3: "TIDE_ERR_OVERFLOW", 4: "TIDE_ERR_UNSUPPORTED", 5: "TIDE_ERR_NO_MEMORY",
+                6: "TIDE_ERR_HIP"}
+ENGINE_KERNEL = 0
+ENGINE_SDMA = 1
+LAUNCH_FULL = 0
+LAUNCH_BUDGETED = 1
+FLAG_SCALAR_PATH = 0x1
+
+# Every symbol include/tide.h declares.
+EXPORTS = ["tide_plan_create", "tide_plan_destroy", "tide_plan_dims", "tide_plan_param",
+           "tide_plan_map", "tide_reduce_scatter_bf16_fp32", "tide_allgather_place",
+           "tide_plan_launch_count", "tide_status_string", "tide_last_error_detail",
+           "tide_version"]
+
+
+class TideError(RuntimeError):
+    def __init__(self, status: int, detail: str, call: str):
+        self.status = status
+        self.status_name = STATUS_NAMES.get(status, "TIDE_ERR_%d" % status)
+        self.detail = detail
+        super().__init__("%s failed: %s: %s" % (call, self.status_name, detail))
+
+
+class Launch(ctypes.Structure):
+    """tide_launch. All-zero = full grid, all ranks."""
+    _fields_ = [("mode", ctypes.c_int32), ("reduce_blocks", ctypes.c_int32),
+                ("place_blocks", ctypes.c_int32), ("max_launch_us", ctypes.c_int32),
+                ("rank_begin", ctypes.c_int32), ("rank_end", ctypes.c_int32),
+                ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+def budgeted(reduce_blocks=16, place_blocks=4, max_launch_us=300, **kw) -> Launch:
+    return Launch(mode=LAUNCH_BUDGETED, reduce_blocks=reduce_blocks, place_blocks=place_blocks,
+                  max_launch_us=max_launch_us, **kw)
+
+
+_I64P = ctypes.POINTER(ctypes.c_int64)
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_VPP = ctypes.POINTER(ctypes.c_void_p)
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libtide.so is not built (%s). Build it with "
+            "`python -c 'import __graft_entry__ as g; g.build()'` or "
+            "`python mixed_precision_rs_amd/_build.py`." % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.tide_plan_create.argtypes = [_I64P, _I64P, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]
+    lib.tide_plan_destroy.argtypes = [ctypes.c_void_p]
+    lib.tide_plan_destroy.restype = None
+    lib.tide_plan_dims.argtypes = [ctypes.c_void_p, _I32P, _I32P, _I32P, _I64P]
+    lib.tide_plan_param.argtypes = [ctypes.c_void_p, ctypes.c_int32, _I64P, _I64P, _I64P,
+                                    _I64P, _I64P]
+    lib.tide_plan_map.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, _I64P,
+                                  _I64P, _I64P]
+    lib.tide_reduce_scatter_bf16_fp32.argtypes = [ctypes.c_void_p, _VPP, ctypes.c_void_p,
+                                                  ctypes.c_int64, ctypes.c_void_p,
+                                                  ctypes.POINTER(Launch)]
+    lib.tide_allgather_place.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                         _VPP, ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.POINTER(Launch)]
+    lib.tide_plan_launch_count.argtypes = [ctypes.c_void_p, ctypes.c_int32,
+                                           ctypes.POINTER(Launch), _I64P]
+    lib.tide_status_string.argtypes = [ctypes.c_int]
+    lib.tide_status_string.restype = ctypes.c_char_p
+    lib.tide_last_error_detail.argtypes = []
+    lib.tide_last_error_detail.restype = ctypes.c_char_p
+    lib.tide_version.argtypes = []
+    lib.tide_version.restype = ctypes.c_int32
+    for f in ("tide_plan_create", "tide_plan_dims", "tide_plan_param", "tide_plan_map",
+              "tide_reduce_scatter_bf16_fp32", "tide_allgather_place", "tide_plan_launch_count"):
+        getattr(lib, f).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def lib():
+    return _load()
+
+
+def _check(status: int, call: str):
+    if status != TIDE_OK:
+        detail = _load().tide_last_error_detail().decode(errors="replace")
+        raise TideError(status, detail, call)
+
+
+def _ptr(x) -> int:
+    """Device address of a tensor (or a raw integer address)."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream_handle(stream) -> Tuple[int, object]:
+    import torch
+    if stream is None:
+        s = torch.cuda.current_stream()
+    elif isinstance(stream, int):
+        return stream, None
+    else:
+        s = stream
+    return int(s.cuda_stream), s
+
+
+class Plan:
+    """A parameter group's layout (tide_plan_create); freed on close()/GC."""
+
+    def __init__(self, shapes: Sequence[Tuple[int, int]], N: int, L: int):
+        lib_ = _load()
+        self.shapes = [(int(t), int(k)) for t, k in shapes]
+        P = len(self.shapes)
+        rows = (ctypes.c_int64 * max(P, 1))(*[t for t, _ in self.shapes])
+        rlen = (ctypes.c_int64 * max(P, 1))(*[k for _, k in self.shapes])
+        h = ctypes.c_void_p()
+        _check(lib_.tide_plan_create(rows, rlen, P, N, L, ctypes.byref(h)), "tide_plan_create")
+        self._h = h
+        self.P, self.N, self.L = P, N, L
+        S = ctypes.c_int64()
+        _check(lib_.tide_plan_dims(h, None, None, None, ctypes.byref(S)), "tide_plan_dims")
+        self.S = int(S.value)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            _load().tide_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def param(self, p: int):
+        """(T_p, K_p, R_p, s_p, o_p)."""
+        v = [ctypes.c_int64() for _ in range(5)]
+        _check(_load().tide_plan_param(self._h, p, *[ctypes.byref(x) for x in v]),
+               "tide_plan_param")
+        return tuple(int(x.value) for x in v)
+
+    def map(self, r: int, p: int):
+        """(rank_major, param_major, valid) of rank r's piece of parameter p."""
+        v = [ctypes.c_int64() for _ in range(3)]
+        _check(_load().tide_plan_map(self._h, r, p, *[ctypes.byref(x) for x in v]),
+               "tide_plan_map")
+        return tuple(int(x.value) for x in v)
+
+    def launch_count(self, op: int, launch: Optional[Launch] = None) -> int:
+        n = ctypes.c_int64()
+        _check(_load().tide_plan_launch_count(
+            self._h, op, ctypes.byref(launch) if launch is not None else None, ctypes.byref(n)),
+            "tide_plan_launch_count")
+        return int(n.value)
+
+
+def plan_create(shapes: Sequence[Tuple[int, int]], N: int, L: int) -> Plan:
+    return Plan(shapes, N, L)
+
+
+def _record(tensors, stream_obj):
+    import torch
+    if stream_obj is None:
+        return
+    if stream_obj == torch.cuda.current_stream(stream_obj.device):
+        return
+    for t in tensors:
+        if t is not None and not isinstance(t, int):
+            t.record_stream(stream_obj)
+
+
+def reduce_scatter_bf16_fp32(plan: Plan, grads: Sequence[Sequence[object]], out,
+                             out_stride: Optional[int] = None, stream=None,
+                             launch: Optional[Launch] = None) -> None:
+    """grads[c][p]: bf16 (T_p, K_p) device tensors (or raw addresses); out: fp32
+    device tensor holding N shards of out_stride elements (default S)."""
+    if len(grads) != plan.L or any(len(g) != plan.P for g in grads):
+        raise ValueError("grads must be L=%d lists of P=%d tensors" % (plan.L, plan.P))
+    flat = [grads[c][p] for c in range(plan.L) for p in range(plan.P)]
+    arr = (ctypes.c_void_p * max(len(flat), 1))(*[_ptr(t) for t in flat])
+    stride = plan.S if out_stride is None else int(out_stride)
+    sh, sobj = _stream_handle(stream)
+    st = _load().tide_reduce_scatter_bf16_fp32(
+        plan.handle, arr, _ptr(out), stride, sh,
+        ctypes.byref(launch) if launch is not None else None)
+    _check(st, "tide_reduce_scatter_bf16_fp32")
+    _record(flat + [out], sobj)
+
+
+def allgather_place(plan: Plan, shards, params: Sequence[object],
+                    shard_stride: Optional[int] = None, stream=None,
+                    engine: Union[int, str] = ENGINE_KERNEL,
+                    launch: Optional[Launch] = None) -> None:
+    """shards: bf16 device tensor of N rank-major shards (shard_stride elements
+    apart, default S); params[p]: bf16 (T_p, K_p) device tensors."""
+    if len(params) != plan.P:
+        raise ValueError("params must hold P=%d tensors" % plan.P)
+    if isinstance(engine, str):
+        engine = {"kernel": ENGINE_KERNEL, "sdma": ENGINE_SDMA}[engine]
+    arr = (ctypes.c_void_p * max(plan.P, 1))(*[_ptr(t) for t in params])
+    stride = plan.S if shard_stride is None else int(shard_stride)
+    sh, sobj = _stream_handle(stream)
+    st = _load().tide_allgather_place(plan.handle, _ptr(shards), stride, arr, sh, int(engine),
+                                      ctypes.byref(launch) if launch is not None else None)
+    _check(st, "tide_allgather_place")
+    _record(list(params) + [shards], sobj)
+
+
+def version() -> int:
+    return int(_load().tide_version())

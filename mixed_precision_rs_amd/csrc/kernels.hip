@@ -1,0 +1,304 @@
+// HIP kernels for gfx950 (CDNA4): the level-1 bf16 -> fp32 reduce of TIDE's
+// reduce-scatter and the all-gather placement step.
+//
+// Both are HBM streams with no reuse, so the design is about bytes in flight
+// and access width, not arithmetic:
+//   * each thread owns kVec = 8 consecutive elements of a parameter's flat
+//     index space, so a wave64 touches 1 KiB of contiguous bf16 per
+//     contributor per instruction (global_load_dwordx4);
+//   * the reduce keeps kRsUnroll steps x L contributors of loads in flight
+//     before it adds, the placement kAgUnroll steps of gathers;
+//   * the fp32 sum is a left fold over contributors in registers: no LDS;
+//   * the destination of the reduce and the source of the placement are
+//     only guaranteed 4-byte (fp32) or 2-byte (bf16) aligned: dword-aligned
+//     16-byte accesses are native on CDNA, and a bf16 run that starts
+//     mid-dword is realigned in registers with a 16-bit funnel shift;
+//   * vectors that straddle two ranks' pieces, and the ragged ends of
+//     parameters and tiles, go element by element.
+// The work list is a table of tiles (TileRec) built on the host; a kernel
+// walks tiles [tile_lo, tile_hi) with a grid-stride loop, so the same kernel
+// serves a full grid (one tile per workgroup) and a small fixed budget of
+// workgroups.
+#include "tide_internal.hpp"
+
+namespace tide {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+// Pointers read from the per-call table are generic pointers to the compiler;
+// naming their address space lets it emit global_ (not flat_) memory ops,
+// which count only against vmcnt.
+#define TIDE_GLOBAL __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ const TIDE_GLOBAL T* gbl(const void* p) {
+    return (const TIDE_GLOBAL T*)(p);
+}
+template <class T>
+__device__ __forceinline__ TIDE_GLOBAL T* gbl_mut(void* p) {
+    return (TIDE_GLOBAL T*)(p);
+}
+
+// Exact bf16 -> fp32 widening of the low / high half of a dword.
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float widen(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Rank r and offset j inside rank r's piece of flat index f of tile t, for
+// idx0 <= f < idx0 + tile. Since j0 < s, j < s + tile: one subtraction does
+// when s >= tile, and a 32-bit division otherwise.
+template <int64_t kTile>
+__device__ __forceinline__ void locate(const TileRec& t, int64_t s, int64_t f, int64_t& r,
+                                       int64_t& j) {
+    j = t.j0 + (f - t.idx0);
+    r = t.r0;
+    if (j >= s) {
+        if (s >= kTile) {
+            j -= s;
+            r += 1;
+        } else {
+            const uint32_t q = (uint32_t)j / (uint32_t)s;
+            r += q;
+            j -= (int64_t)q * s;
+        }
+    }
+}
+
+// Advance (r, j) by one element.
+__device__ __forceinline__ void step(int64_t s, int64_t& r, int64_t& j) {
+    if (++j == s) {
+        j = 0;
+        ++r;
+    }
+}
+
+// Write 8 fp32 results for flat indices f..f+7 (all inside the tile's range).
+__device__ __forceinline__ void store8(const TileRec& t, const ParamDev& pd, int64_t f,
+                                       const float (&a)[kVec], float* __restrict__ out,
+                                       int64_t stride) {
+    int64_t r, j;
+    locate<kRsTile>(t, pd.s, f, r, j);
+    if (j + kVec <= pd.s) {
+        float* dst = out + r * stride + pd.o + j;
+        const f32x4_a4 x0 = {a[0], a[1], a[2], a[3]};
+        const f32x4_a4 x1 = {a[4], a[5], a[6], a[7]};
+        __builtin_nontemporal_store(x0, reinterpret_cast<f32x4_a4*>(dst));
+        __builtin_nontemporal_store(x1, reinterpret_cast<f32x4_a4*>(dst + 4));
+    } else {
+        // The 8 elements straddle two or more ranks' pieces.
+#pragma unroll 1
+        for (int e = 0; e < kVec; ++e) {
+            out[r * stride + pd.o + j] = a[e];
+            step(pd.s, r, j);
+        }
+    }
+}
+
+// Reduce: out[rank piece] = fold_c widen(g[c][f]) for f < valid, +0 past it.
+// LT > 0: L known at compile time (fully unrolled); LT == 0: runtime L.
+template <int LT>
+__global__ __launch_bounds__(kThreads) void reduce_kernel(
+    const TileRec* __restrict__ tiles, int64_t tile_lo, int64_t tile_hi,
+    const ParamDev* __restrict__ params, const uint16_t* const* __restrict__ ptrs,
+    const uint32_t* __restrict__ flags, int Lrt, float* __restrict__ out, int64_t out_stride) {
+    const int L = LT > 0 ? LT : Lrt;
+    for (int64_t t = tile_lo + blockIdx.x; t < tile_hi; t += gridDim.x) {
+        const TileRec tr = tiles[t];
+        const ParamDev pd = params[tr.p];
+        const uint16_t* const* g = ptrs + (int64_t)tr.p * L;
+        const bool vec = (flags[tr.p] & kFlagVector) != 0;
+        const int64_t end = min(tr.idx0 + kRsTile, tr.hi);
+        for (int64_t g0 = tr.idx0; g0 < end; g0 += kRsUnroll * kStep) {
+            const int64_t g1 = g0 + kRsUnroll * kStep;
+            const bool interior = vec && g0 >= tr.lo && g1 <= end;
+            const int64_t f0 = g0 + (int64_t)threadIdx.x * kVec;
+            if (interior && g1 <= pd.valid) {
+                // All L * kRsUnroll loads are independent of the adds, so they
+                // are all issued before the first add waits.
+                float a[kRsUnroll][kVec];
+#pragma unroll
+                for (int c = 0; c < L; ++c) {
+                    const TIDE_GLOBAL u32x4* gc = gbl<u32x4>(g[c] + f0);
+                    u32x4 v[kRsUnroll];
+#pragma unroll
+                    for (int u = 0; u < kRsUnroll; ++u)
+                        v[u] = __builtin_nontemporal_load(gc + u * (kStep / kVec));
+#pragma unroll
+                    for (int u = 0; u < kRsUnroll; ++u) {
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) {
+                            if (c == 0) {
+                                a[u][2 * m] = lo_bf16(v[u][m]);
+                                a[u][2 * m + 1] = hi_bf16(v[u][m]);
+                            } else {
+                                a[u][2 * m] = a[u][2 * m] + lo_bf16(v[u][m]);
+                                a[u][2 * m + 1] = a[u][2 * m + 1] + hi_bf16(v[u][m]);
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kRsUnroll; ++u)
+                    store8(tr, pd, f0 + (int64_t)u * kStep, a[u], out, out_stride);
+            } else if (interior && g0 >= pd.valid) {
+                float z[kVec];
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) z[e] = 0.0f;
+#pragma unroll
+                for (int u = 0; u < kRsUnroll; ++u)
+                    store8(tr, pd, f0 + (int64_t)u * kStep, z, out, out_stride);
+            } else {
+                // Ragged edge: element by element, exact bounds.
+#pragma unroll 1
+                for (int u = 0; u < kRsUnroll; ++u) {
+                    const int64_t fu = f0 + (int64_t)u * kStep;
+                    int64_t r, j;
+                    locate<kRsTile>(tr, pd.s, fu, r, j);
+#pragma unroll 1
+                    for (int e = 0; e < kVec; ++e, step(pd.s, r, j)) {
+                        const int64_t f = fu + e;
+                        if (f < tr.lo || f >= end) continue;
+                        float v = 0.0f;
+                        if (f < pd.valid) {
+                            v = widen(gbl<uint16_t>(g[0])[f]);
+#pragma unroll 1
+                            for (int c = 1; c < L; ++c) v = v + widen(gbl<uint16_t>(g[c])[f]);
+                        }
+                        out[r * out_stride + pd.o + j] = v;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// 8 bf16 of the rank-major shards for flat parameter indices f..f+7.
+__device__ __forceinline__ u32x4 gather8(const TileRec& t, const ParamDev& pd, int64_t f,
+                                         const uint16_t* __restrict__ shards, int64_t stride,
+                                         int64_t shard_elems) {
+    int64_t r, j;
+    locate<kAgTile>(t, pd.s, f, r, j);
+    if (j + kVec <= pd.s) {
+        const int64_t e = r * stride + pd.o + j;
+        const uint16_t* src = shards + e;
+        if ((reinterpret_cast<uintptr_t>(src) & 3) == 0)
+            return __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4*>(src));
+        if (e >= 1 && e + 9 <= shard_elems) {
+            // src is 2 mod 4: load the 5 dwords covering elements e-1 .. e+8
+            // (all inside the shard buffer) and shift them down 16 bits.
+            const uint32_t* d = reinterpret_cast<const uint32_t*>(src - 1);
+            const u32x4_a4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4*>(d));
+            const uint32_t y = __builtin_nontemporal_load(d + 4);
+            u32x4 w;
+            w[0] = __builtin_amdgcn_alignbit(x[1], x[0], 16);
+            w[1] = __builtin_amdgcn_alignbit(x[2], x[1], 16);
+            w[2] = __builtin_amdgcn_alignbit(x[3], x[2], 16);
+            w[3] = __builtin_amdgcn_alignbit(y, x[3], 16);
+            return w;
+        }
+    }
+    // Straddles two ranks' pieces, or sits at the very ends of the buffer.
+    uint32_t h[kVec];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+        h[e] = shards[r * stride + pd.o + j];
+        step(pd.s, r, j);
+    }
+    u32x4 w;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) w[m] = h[2 * m] | (h[2 * m + 1] << 16);
+    return w;
+}
+
+// Placement: param[f] = shards[rank(f) * stride + o_p + offset(f)] for true f.
+__global__ __launch_bounds__(kThreads) void place_kernel(
+    const TileRec* __restrict__ tiles, int64_t tile_lo, int64_t tile_hi,
+    const ParamDev* __restrict__ params, uint16_t* const* __restrict__ ptrs,
+    const uint32_t* __restrict__ flags, const uint16_t* __restrict__ shards, int64_t stride,
+    int64_t shard_elems) {
+    for (int64_t t = tile_lo + blockIdx.x; t < tile_hi; t += gridDim.x) {
+        const TileRec tr = tiles[t];
+        const ParamDev pd = params[tr.p];
+        uint16_t* dst = ptrs[tr.p];
+        const bool vec = (flags[tr.p] & kFlagVector) != 0;
+        const int64_t end = min(tr.idx0 + kAgTile, tr.hi);
+        for (int64_t g0 = tr.idx0; g0 < end; g0 += kAgUnroll * kStep) {
+            const int64_t g1 = g0 + kAgUnroll * kStep;
+            const int64_t f0 = g0 + (int64_t)threadIdx.x * kVec;
+            if (vec && g0 >= tr.lo && g1 <= end) {
+                u32x4 w[kAgUnroll];
+#pragma unroll
+                for (int u = 0; u < kAgUnroll; ++u)
+                    w[u] = gather8(tr, pd, f0 + (int64_t)u * kStep, shards, stride, shard_elems);
+                TIDE_GLOBAL u32x4* d4 = gbl_mut<u32x4>(dst + f0);
+#pragma unroll
+                for (int u = 0; u < kAgUnroll; ++u)
+                    __builtin_nontemporal_store(w[u], d4 + u * (kStep / kVec));
+            } else {
+                TIDE_GLOBAL uint16_t* d = gbl_mut<uint16_t>(dst);
+#pragma unroll 1
+                for (int u = 0; u < kAgUnroll; ++u) {
+                    const int64_t fu = f0 + (int64_t)u * kStep;
+                    int64_t r, j;
+                    locate<kAgTile>(tr, pd.s, fu, r, j);
+#pragma unroll 1
+                    for (int e = 0; e < kVec; ++e, step(pd.s, r, j)) {
+                        const int64_t f = fu + e;
+                        if (f < tr.lo || f >= end) continue;
+                        d[f] = shards[r * stride + pd.o + j];
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int LT>
+hipError_t launch_reduce_t(int L, int grid, hipStream_t stream, const TileRec* tiles,
+                           int64_t tile_lo, int64_t tile_hi, const ParamDev* params,
+                           const uint16_t* const* ptrs, const uint32_t* flags, float* out,
+                           int64_t out_stride) {
+    void* args[] = {&tiles, &tile_lo, &tile_hi, &params, &ptrs, &flags, &L, &out, &out_stride};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&reduce_kernel<LT>), dim3(grid),
+                           dim3(kThreads), args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_reduce(int L, int grid, hipStream_t stream, const TileRec* tiles,
+                         int64_t tile_lo, int64_t tile_hi, const ParamDev* params,
+                         const uint16_t* const* ptrs, const uint32_t* flags, float* out,
+                         int64_t out_stride) {
+#define TIDE_REDUCE_CASE(n)                                                                   \
+    case n:                                                                                   \
+        return launch_reduce_t<n>(L, grid, stream, tiles, tile_lo, tile_hi, params, ptrs,    \
+                                  flags, out, out_stride);
+    switch (L) {
+        TIDE_REDUCE_CASE(1)
+        TIDE_REDUCE_CASE(2)
+        TIDE_REDUCE_CASE(3)
+        TIDE_REDUCE_CASE(4)
+        TIDE_REDUCE_CASE(5)
+        TIDE_REDUCE_CASE(6)
+        TIDE_REDUCE_CASE(7)
+        TIDE_REDUCE_CASE(8)
+        default:
+            return launch_reduce_t<0>(L, grid, stream, tiles, tile_lo, tile_hi, params, ptrs,
+                                      flags, out, out_stride);
+    }
+#undef TIDE_REDUCE_CASE
+}
+
+hipError_t launch_place(int grid, hipStream_t stream, const TileRec* tiles, int64_t tile_lo,
+                        int64_t tile_hi, const ParamDev* params, uint16_t* const* ptrs,
+                        const uint32_t* flags, const uint16_t* shards, int64_t shard_stride,
+                        int64_t shard_elems) {
+    void* args[] = {&tiles, &tile_lo, &tile_hi, &params, &ptrs, &flags, &shards, &shard_stride,
+                    &shard_elems};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&place_kernel), dim3(grid),
+                           dim3(kThreads), args, 0, stream);
+}
+
+}  // namespace tide

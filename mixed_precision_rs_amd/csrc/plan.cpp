@@ -1,0 +1,654 @@
+// Host side of the C ABI declared in include/tide.h: the layout planner
+// (page 3 Table 2 notation), argument validation, per-device tables, the
+// per-call pointer-table ring, and the launch policies (full grid,
+// CU-budgeted, SDMA placement).
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <new>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "tide.h"
+#include "tide_internal.hpp"
+
+using namespace tide;
+
+namespace {
+
+thread_local std::string g_detail;
+
+tide_status fail(tide_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_detail = buf;
+    return st;
+}
+
+tide_status hip_fail(hipError_t e, const char* what) {
+    return fail(TIDE_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+#define TIDE_HIP_TRY(expr)                                      \
+    do {                                                        \
+        hipError_t e_ = (expr);                                 \
+        if (e_ != hipSuccess) return hip_fail(e_, #expr);       \
+    } while (0)
+
+// Defaults of the CU-budgeted mode: 16 summing + 4 landing blocks living
+// 0.2-0.4 ms each (page 1 "Why does a communication kernel slow a matrix
+// multiply by 69%?"; page 3 Table 4 "TIDE, training 16+4").
+constexpr int kDefaultReduceBlocks = 16;
+constexpr int kDefaultPlaceBlocks = 4;
+constexpr int kDefaultMaxLaunchUs = 300;
+// Bytes one workgroup streams per microsecond when it has a CU to itself;
+// sizes the budgeted launches so a workgroup lives about max_launch_us.
+constexpr int64_t kWgBytesPerUs = 60000;
+constexpr int kFullGridCap = 1 << 30;
+constexpr int kRingSlots = 8;
+
+struct TileTable {
+    TileRec* dev = nullptr;
+    int64_t count = 0;
+};
+
+struct Slot {
+    void* dev = nullptr;
+    void* host = nullptr;
+    size_t used = 0;
+    bool loaded = false;
+    hipStream_t upload_stream = nullptr;
+    hipEvent_t upload_done = nullptr;      // recorded after the upload copy
+    std::vector<hipEvent_t> readers;       // recorded after each call that read the slot
+};
+
+struct DevState {
+    int device = -1;
+    ParamDev* params = nullptr;
+    std::map<std::tuple<int, int, int>, TileTable> tiles;   // (op, rank_begin, rank_end)
+    size_t slot_cap = 0;
+    char* ring_dev = nullptr;
+    char* ring_host = nullptr;
+    Slot slots[kRingSlots];
+    int next_slot = 0;
+    int last_slot = -1;
+    std::vector<hipEvent_t> event_pool;
+
+    ~DevState() {
+        int prev = -1;
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        (void)hipSetDevice(device);
+        for (auto& kv : tiles) (void)hipFree(kv.second.dev);
+        (void)hipFree(params);
+        (void)hipFree(ring_dev);
+        if (ring_host) (void)hipHostFree(ring_host);
+        for (auto& s : slots) {
+            for (hipEvent_t e : s.readers) {
+                (void)hipEventSynchronize(e);
+                (void)hipEventDestroy(e);
+            }
+            if (s.upload_done) (void)hipEventDestroy(s.upload_done);
+        }
+        for (hipEvent_t e : event_pool) (void)hipEventDestroy(e);
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+struct ParamInfo {
+    int64_t T, K, R, s, o, valid;
+};
+
+}  // namespace
+
+struct tide_plan {
+    int32_t P = 0, N = 0, L = 0;
+    int64_t S = 0;
+    std::vector<ParamInfo> prm;
+    mutable std::mutex mu;
+    mutable std::vector<std::unique_ptr<DevState>> devs;
+};
+
+namespace {
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+bool add_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_add_overflow(a, b, out); }
+
+tide_status resolve_launch(const tide_plan* plan, const tide_launch* in, tide_launch* out) {
+    tide_launch l{};
+    if (in) l = *in;
+    if (l.mode != TIDE_LAUNCH_FULL && l.mode != TIDE_LAUNCH_BUDGETED)
+        return fail(TIDE_ERR_INVALID_ARG, "launch.mode %d is not FULL (0) or BUDGETED (1)", l.mode);
+    if (l.reduce_blocks < 0 || l.place_blocks < 0 || l.max_launch_us < 0)
+        return fail(TIDE_ERR_INVALID_ARG, "negative launch budget");
+    if (l.reserved != 0 || (l.flags & ~TIDE_FLAG_SCALAR_PATH) != 0)
+        return fail(TIDE_ERR_INVALID_ARG, "unknown launch flags 0x%x", l.flags);
+    if (l.reduce_blocks == 0) l.reduce_blocks = kDefaultReduceBlocks;
+    if (l.place_blocks == 0) l.place_blocks = kDefaultPlaceBlocks;
+    if (l.max_launch_us == 0) l.max_launch_us = kDefaultMaxLaunchUs;
+    if (l.rank_end == 0) l.rank_end = plan->N;
+    if (l.rank_begin < 0 || l.rank_end > plan->N || l.rank_begin > l.rank_end)
+        return fail(TIDE_ERR_INVALID_ARG, "rank range [%d, %d) outside [0, %d)", l.rank_begin,
+                    l.rank_end, plan->N);
+    *out = l;
+    return TIDE_OK;
+}
+
+// Tiles of one op over ranks [rb, re). op 0: reduce over each parameter's
+// padded index space restricted to [rb * s_p, re * s_p); op 1: placement over
+// its true elements restricted the same way.
+std::vector<TileRec> build_tiles(const tide_plan* plan, int op, int rb, int re) {
+    std::vector<TileRec> out;
+    const int64_t tile = op == 0 ? kRsTile : kAgTile;
+    for (int32_t p = 0; p < plan->P; ++p) {
+        const ParamInfo& q = plan->prm[p];
+        if (q.s == 0) continue;
+        const int64_t lo = (int64_t)rb * q.s;
+        int64_t hi = (int64_t)re * q.s;
+        if (op == 1) hi = std::min(hi, q.valid);
+        if (hi <= lo) continue;
+        for (int64_t a = lo - lo % kVec; a < hi; a += tile) {
+            TileRec t{};
+            t.idx0 = a;
+            t.r0 = (int32_t)(a / q.s);
+            t.j0 = a - (int64_t)t.r0 * q.s;
+            t.lo = lo;
+            t.hi = hi;
+            t.p = p;
+            out.push_back(t);
+        }
+    }
+    return out;
+}
+
+int64_t tile_bytes(const tide_plan* plan, int op) {
+    return op == 0 ? kRsTile * (2 * (int64_t)plan->L + 4) : kAgTile * 4;
+}
+
+// Tiles one budgeted workgroup handles per launch.
+int64_t budget_tiles_per_block(const tide_plan* plan, int op, const tide_launch& l) {
+    const int64_t per = ((int64_t)l.max_launch_us * kWgBytesPerUs) / tile_bytes(plan, op);
+    return std::max<int64_t>(1, per);
+}
+
+int64_t count_launches(const tide_plan* plan, int op, const tide_launch& l, int64_t ntiles) {
+    if (ntiles == 0) return 0;
+    if (l.mode == TIDE_LAUNCH_FULL) return (ntiles + kFullGridCap - 1) / kFullGridCap;
+    const int64_t blocks = op == 0 ? l.reduce_blocks : l.place_blocks;
+    const int64_t per_launch = blocks * budget_tiles_per_block(plan, op, l);
+    return (ntiles + per_launch - 1) / per_launch;
+}
+
+tide_status stream_device(hipStream_t stream, int* dev) {
+    if (stream) {
+        hipError_t e = hipStreamGetDevice(stream, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+        return TIDE_OK;
+    }
+    hipError_t e = hipGetDevice(dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    return TIDE_OK;
+}
+
+// Device state of `plan` on `dev` (created on first use). Caller holds plan->mu.
+tide_status get_dev_state(const tide_plan* plan, int dev, DevState** out) {
+    for (auto& d : plan->devs) {
+        if (d->device == dev) {
+            *out = d.get();
+            return TIDE_OK;
+        }
+    }
+    std::unique_ptr<DevState> ds(new DevState());
+    ds->device = dev;
+    std::vector<ParamDev> pd(std::max<int32_t>(plan->P, 1));
+    for (int32_t p = 0; p < plan->P; ++p) {
+        pd[p].s = plan->prm[p].s;
+        pd[p].o = plan->prm[p].o;
+        pd[p].valid = plan->prm[p].valid;
+        pd[p].pad = 0;
+    }
+    TIDE_HIP_TRY(hipMalloc(&ds->params, pd.size() * sizeof(ParamDev)));
+    TIDE_HIP_TRY(hipMemcpy(ds->params, pd.data(), pd.size() * sizeof(ParamDev),
+                           hipMemcpyHostToDevice));
+    const size_t P = (size_t)std::max<int32_t>(plan->P, 1);
+    size_t cap = std::max(P * (size_t)plan->L * sizeof(void*), P * sizeof(void*)) +
+                 P * sizeof(uint32_t);
+    cap = (cap + 255) / 256 * 256;
+    ds->slot_cap = cap;
+    TIDE_HIP_TRY(hipMalloc(&ds->ring_dev, cap * kRingSlots));
+    TIDE_HIP_TRY(hipHostMalloc(&ds->ring_host, cap * kRingSlots, hipHostMallocDefault));
+    for (int i = 0; i < kRingSlots; ++i) {
+        ds->slots[i].dev = ds->ring_dev + cap * i;
+        ds->slots[i].host = ds->ring_host + cap * i;
+        TIDE_HIP_TRY(hipEventCreateWithFlags(&ds->slots[i].upload_done, hipEventDisableTiming));
+    }
+    *out = ds.get();
+    plan->devs.push_back(std::move(ds));
+    return TIDE_OK;
+}
+
+tide_status get_tiles(const tide_plan* plan, DevState* ds, int op, int rb, int re,
+                      TileTable** out) {
+    auto key = std::make_tuple(op, rb, re);
+    auto it = ds->tiles.find(key);
+    if (it != ds->tiles.end()) {
+        *out = &it->second;
+        return TIDE_OK;
+    }
+    std::vector<TileRec> t = build_tiles(plan, op, rb, re);
+    TileTable tt;
+    tt.count = (int64_t)t.size();
+    if (!t.empty()) {
+        TIDE_HIP_TRY(hipMalloc(&tt.dev, t.size() * sizeof(TileRec)));
+        hipError_t e = hipMemcpy(tt.dev, t.data(), t.size() * sizeof(TileRec),
+                                 hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            (void)hipFree(tt.dev);
+            return hip_fail(e, "hipMemcpy(tiles)");
+        }
+    }
+    auto ins = ds->tiles.emplace(key, tt);
+    *out = &ins.first->second;
+    return TIDE_OK;
+}
+
+tide_status take_event(DevState* ds, hipEvent_t* ev) {
+    if (!ds->event_pool.empty()) {
+        *ev = ds->event_pool.back();
+        ds->event_pool.pop_back();
+        return TIDE_OK;
+    }
+    TIDE_HIP_TRY(hipEventCreateWithFlags(ev, hipEventDisableTiming));
+    return TIDE_OK;
+}
+
+// Make the per-call table `bytes` visible on the device in stream order.
+// Reuses the previous slot, with no copy, when the table is unchanged.
+tide_status stage_table(DevState* ds, const void* bytes, size_t n, hipStream_t stream,
+                        int* slot_out) {
+    if (ds->last_slot >= 0) {
+        Slot& s = ds->slots[ds->last_slot];
+        if (s.loaded && s.used == n && std::memcmp(s.host, bytes, n) == 0) {
+            if (s.upload_stream != stream)
+                TIDE_HIP_TRY(hipStreamWaitEvent(stream, s.upload_done, 0));
+            *slot_out = ds->last_slot;
+            return TIDE_OK;
+        }
+    }
+    const int k = ds->next_slot;
+    ds->next_slot = (k + 1) % kRingSlots;
+    Slot& s = ds->slots[k];
+    for (hipEvent_t e : s.readers) {          // earlier readers of this slot must be done
+        TIDE_HIP_TRY(hipEventSynchronize(e));
+        ds->event_pool.push_back(e);
+    }
+    s.readers.clear();
+    s.loaded = false;
+    std::memcpy(s.host, bytes, n);
+    TIDE_HIP_TRY(hipMemcpyAsync(s.dev, s.host, n, hipMemcpyHostToDevice, stream));
+    TIDE_HIP_TRY(hipEventRecord(s.upload_done, stream));
+    s.used = n;
+    s.loaded = true;
+    s.upload_stream = stream;
+    ds->last_slot = k;
+    *slot_out = k;
+    return TIDE_OK;
+}
+
+tide_status release_slot(DevState* ds, int slot, hipStream_t stream) {
+    hipEvent_t ev;
+    tide_status st = take_event(ds, &ev);
+    if (st != TIDE_OK) return st;
+    hipError_t e = hipEventRecord(ev, stream);
+    if (e != hipSuccess) {
+        ds->event_pool.push_back(ev);
+        return hip_fail(e, "hipEventRecord");
+    }
+    ds->slots[slot].readers.push_back(ev);
+    return TIDE_OK;
+}
+
+struct Range {
+    uintptr_t lo, hi;
+    int who;
+};
+
+bool overlaps(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// The run of tiles of each launch and the grid it uses.
+template <typename F>
+tide_status for_each_launch(const tide_plan* plan, int op, const tide_launch& l,
+                            int64_t ntiles, F&& launch) {
+    if (ntiles == 0) return TIDE_OK;
+    int64_t per_launch;
+    int grid_cap;
+    if (l.mode == TIDE_LAUNCH_FULL) {
+        per_launch = kFullGridCap;
+        grid_cap = kFullGridCap;
+    } else {
+        const int blocks = op == 0 ? l.reduce_blocks : l.place_blocks;
+        per_launch = (int64_t)blocks * budget_tiles_per_block(plan, op, l);
+        grid_cap = blocks;
+    }
+    for (int64_t lo = 0; lo < ntiles; lo += per_launch) {
+        const int64_t hi = std::min(ntiles, lo + per_launch);
+        const int grid = (int)std::min<int64_t>(grid_cap, hi - lo);
+        hipError_t e = launch(grid, lo, hi);
+        if (e != hipSuccess) return hip_fail(e, op == 0 ? "reduce launch" : "place launch");
+    }
+    return TIDE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tide_status tide_plan_create(const int64_t* rows, const int64_t* row_len, int32_t P, int32_t N,
+                             int32_t L, tide_plan** out_plan) {
+    try {
+        if (!out_plan) return fail(TIDE_ERR_INVALID_ARG, "out_plan is NULL");
+        *out_plan = nullptr;
+        if (P < 0) return fail(TIDE_ERR_INVALID_ARG, "P = %d < 0", P);
+        if (N < 1) return fail(TIDE_ERR_INVALID_ARG, "N = %d < 1", N);
+        if (L < 1 || L > 64) return fail(TIDE_ERR_INVALID_ARG, "L = %d not in [1, 64]", L);
+        if (P > 0 && (!rows || !row_len)) return fail(TIDE_ERR_INVALID_ARG, "rows/row_len NULL");
+        std::unique_ptr<tide_plan> plan(new tide_plan());
+        plan->P = P;
+        plan->N = N;
+        plan->L = L;
+        plan->prm.resize(P);
+        int64_t acc = 0;
+        for (int32_t p = 0; p < P; ++p) {
+            ParamInfo& q = plan->prm[p];
+            q.T = rows[p];
+            q.K = row_len[p];
+            if (q.T < 0) return fail(TIDE_ERR_INVALID_ARG, "rows[%d] = %lld < 0", p, (long long)q.T);
+            if (q.K < 1)
+                return fail(TIDE_ERR_INVALID_ARG, "row_len[%d] = %lld < 1", p, (long long)q.K);
+            q.R = q.T / N + (q.T % N != 0);                  // ceil(T_p / N)
+            if (!mul_ok(q.R, q.K, &q.s) || !mul_ok(q.T, q.K, &q.valid))
+                return fail(TIDE_ERR_OVERFLOW, "parameter %d size overflows int64", p);
+            q.o = acc;
+            if (!add_ok(acc, q.s, &acc)) return fail(TIDE_ERR_OVERFLOW, "S overflows int64");
+        }
+        plan->S = acc;
+        int64_t ns;
+        if (!mul_ok(acc, N, &ns)) return fail(TIDE_ERR_OVERFLOW, "N * S overflows int64");
+        // Byte offsets of the fp32 output must fit too.
+        if (!mul_ok(ns, 4, &ns)) return fail(TIDE_ERR_OVERFLOW, "4 * N * S overflows int64");
+        *out_plan = plan.release();
+        return TIDE_OK;
+    } catch (const std::bad_alloc&) {
+        return fail(TIDE_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return fail(TIDE_ERR_INVALID_ARG, "unexpected exception");
+    }
+}
+
+void tide_plan_destroy(tide_plan* plan) {
+    try {
+        delete plan;
+    } catch (...) {
+    }
+}
+
+tide_status tide_plan_dims(const tide_plan* plan, int32_t* P, int32_t* N, int32_t* L, int64_t* S) {
+    if (!plan) return fail(TIDE_ERR_INVALID_ARG, "plan is NULL");
+    if (P) *P = plan->P;
+    if (N) *N = plan->N;
+    if (L) *L = plan->L;
+    if (S) *S = plan->S;
+    return TIDE_OK;
+}
+
+tide_status tide_plan_param(const tide_plan* plan, int32_t p, int64_t* rows, int64_t* row_len,
+                            int64_t* R_p, int64_t* s_p, int64_t* o_p) {
+    if (!plan) return fail(TIDE_ERR_INVALID_ARG, "plan is NULL");
+    if (p < 0 || p >= plan->P) return fail(TIDE_ERR_INVALID_ARG, "p = %d out of range", p);
+    const ParamInfo& q = plan->prm[p];
+    if (rows) *rows = q.T;
+    if (row_len) *row_len = q.K;
+    if (R_p) *R_p = q.R;
+    if (s_p) *s_p = q.s;
+    if (o_p) *o_p = q.o;
+    return TIDE_OK;
+}
+
+tide_status tide_plan_map(const tide_plan* plan, int32_t r, int32_t p, int64_t* rank_major,
+                          int64_t* param_major, int64_t* valid) {
+    if (!plan) return fail(TIDE_ERR_INVALID_ARG, "plan is NULL");
+    if (p < 0 || p >= plan->P) return fail(TIDE_ERR_INVALID_ARG, "p = %d out of range", p);
+    if (r < 0 || r >= plan->N) return fail(TIDE_ERR_INVALID_ARG, "r = %d out of range", r);
+    const ParamInfo& q = plan->prm[p];
+    if (rank_major) *rank_major = (int64_t)r * plan->S + q.o;
+    if (param_major) *param_major = (int64_t)plan->N * q.o + (int64_t)r * q.s;
+    if (valid) *valid = std::max<int64_t>(0, std::min(q.s, q.valid - (int64_t)r * q.s));
+    return TIDE_OK;
+}
+
+tide_status tide_plan_launch_count(const tide_plan* plan, int32_t op, const tide_launch* launch,
+                                   int64_t* launches) {
+    try {
+        if (!plan || !launches) return fail(TIDE_ERR_INVALID_ARG, "NULL argument");
+        if (op != 0 && op != 1) return fail(TIDE_ERR_INVALID_ARG, "op %d not 0 or 1", op);
+        tide_launch l;
+        tide_status st = resolve_launch(plan, launch, &l);
+        if (st != TIDE_OK) return st;
+        const int64_t n = (int64_t)build_tiles(plan, op, l.rank_begin, l.rank_end).size();
+        *launches = count_launches(plan, op, l, n);
+        return TIDE_OK;
+    } catch (const std::bad_alloc&) {
+        return fail(TIDE_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return fail(TIDE_ERR_INVALID_ARG, "unexpected exception");
+    }
+}
+
+tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t* const* grads,
+                                          float* out, int64_t out_stride, void* stream_v,
+                                          const tide_launch* launch) {
+    try {
+        if (!plan) return fail(TIDE_ERR_INVALID_ARG, "plan is NULL");
+        tide_launch l;
+        tide_status st = resolve_launch(plan, launch, &l);
+        if (st != TIDE_OK) return st;
+        const int32_t P = plan->P, L = plan->L;
+        if (out_stride < plan->S)
+            return fail(TIDE_ERR_INVALID_ARG, "out_stride %lld < S %lld", (long long)out_stride,
+                        (long long)plan->S);
+        int64_t total;
+        if (!mul_ok(out_stride, plan->N, &total) || !mul_ok(total, 4, &total))
+            return fail(TIDE_ERR_OVERFLOW, "N * out_stride * 4 overflows int64");
+        const bool work = plan->S > 0 && l.rank_end > l.rank_begin;
+        if (!work) return TIDE_OK;
+        if (!out) return fail(TIDE_ERR_INVALID_ARG, "out is NULL");
+        if (reinterpret_cast<uintptr_t>(out) & 3)
+            return fail(TIDE_ERR_ALIGNMENT, "out is not 4-byte aligned");
+        if (P > 0 && !grads) return fail(TIDE_ERR_INVALID_ARG, "grads is NULL");
+        // Per-call table: P*L pointers (parameter-major) then P flag words.
+        std::vector<char> table((size_t)P * L * sizeof(void*) + (size_t)P * sizeof(uint32_t));
+        const uint16_t** tp = reinterpret_cast<const uint16_t**>(table.data());
+        uint32_t* fl = reinterpret_cast<uint32_t*>(table.data() + (size_t)P * L * sizeof(void*));
+        const Range w{reinterpret_cast<uintptr_t>(out) + (uintptr_t)l.rank_begin * out_stride * 4,
+                      reinterpret_cast<uintptr_t>(out) + (uintptr_t)(l.rank_end - 1) * out_stride * 4 +
+                          (uintptr_t)plan->S * 4,
+                      -1};
+        for (int32_t p = 0; p < P; ++p) {
+            const ParamInfo& q = plan->prm[p];
+            uint32_t f = (l.flags & TIDE_FLAG_SCALAR_PATH) ? 0u : kFlagVector;
+            for (int32_t c = 0; c < L; ++c) {
+                const uint16_t* g = grads[(size_t)c * P + p];
+                tp[(size_t)p * L + c] = g;
+                if (q.valid == 0) continue;
+                if (!g) return fail(TIDE_ERR_INVALID_ARG, "grads[%d] (c=%d, p=%d) is NULL", c * P + p, c, p);
+                const uintptr_t a = reinterpret_cast<uintptr_t>(g);
+                if (a & 1) return fail(TIDE_ERR_ALIGNMENT, "grads[%d] is not 2-byte aligned", c * P + p);
+                if (a & 15) f &= ~kFlagVector;
+                const Range in{a, a + (uintptr_t)q.valid * 2, c * P + p};
+                if (overlaps(in, w))
+                    return fail(TIDE_ERR_INVALID_ARG, "grads[%d] overlaps the output", c * P + p);
+            }
+            fl[p] = f;
+        }
+        hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+        std::lock_guard<std::mutex> lock(plan->mu);
+        int dev;
+        st = stream_device(stream, &dev);
+        if (st != TIDE_OK) return st;
+        DevState* ds;
+        st = get_dev_state(plan, dev, &ds);
+        if (st != TIDE_OK) return st;
+        TileTable* tt;
+        st = get_tiles(plan, ds, 0, l.rank_begin, l.rank_end, &tt);
+        if (st != TIDE_OK) return st;
+        if (tt->count == 0) return TIDE_OK;
+        int slot;
+        st = stage_table(ds, table.data(), table.size(), stream, &slot);
+        if (st != TIDE_OK) return st;
+        const char* base = static_cast<const char*>(ds->slots[slot].dev);
+        const uint16_t* const* dptrs = reinterpret_cast<const uint16_t* const*>(base);
+        const uint32_t* dflags =
+            reinterpret_cast<const uint32_t*>(base + (size_t)P * L * sizeof(void*));
+        st = for_each_launch(plan, 0, l, tt->count, [&](int grid, int64_t lo, int64_t hi) {
+            return launch_reduce(L, grid, stream, tt->dev, lo, hi, ds->params, dptrs, dflags, out,
+                                 out_stride);
+        });
+        tide_status st2 = release_slot(ds, slot, stream);
+        return st != TIDE_OK ? st : st2;
+    } catch (const std::bad_alloc&) {
+        return fail(TIDE_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return fail(TIDE_ERR_INVALID_ARG, "unexpected exception");
+    }
+}
+
+tide_status tide_allgather_place(const tide_plan* plan, const uint16_t* shards,
+                                 int64_t shard_stride, uint16_t* const* params, void* stream_v,
+                                 int32_t engine, const tide_launch* launch) {
+    try {
+        if (!plan) return fail(TIDE_ERR_INVALID_ARG, "plan is NULL");
+        tide_launch l;
+        tide_status st = resolve_launch(plan, launch, &l);
+        if (st != TIDE_OK) return st;
+        if (engine != TIDE_ENGINE_KERNEL && engine != TIDE_ENGINE_SDMA)
+            return fail(TIDE_ERR_INVALID_ARG, "engine %d is not KERNEL (0) or SDMA (1)", engine);
+        const int32_t P = plan->P;
+        if (shard_stride < plan->S)
+            return fail(TIDE_ERR_INVALID_ARG, "shard_stride %lld < S %lld",
+                        (long long)shard_stride, (long long)plan->S);
+        int64_t shard_elems;
+        if (!mul_ok(shard_stride, plan->N, &shard_elems) || !mul_ok(shard_elems, 2, &shard_elems))
+            return fail(TIDE_ERR_OVERFLOW, "N * shard_stride * 2 overflows int64");
+        shard_elems /= 2;
+        if (plan->S == 0 || l.rank_end == l.rank_begin) return TIDE_OK;
+        if (!shards) return fail(TIDE_ERR_INVALID_ARG, "shards is NULL");
+        if (reinterpret_cast<uintptr_t>(shards) & 1)
+            return fail(TIDE_ERR_ALIGNMENT, "shards is not 2-byte aligned");
+        if (P > 0 && !params) return fail(TIDE_ERR_INVALID_ARG, "params is NULL");
+        std::vector<char> table((size_t)P * sizeof(void*) + (size_t)P * sizeof(uint32_t));
+        uint16_t** tp = reinterpret_cast<uint16_t**>(table.data());
+        uint32_t* fl = reinterpret_cast<uint32_t*>(table.data() + (size_t)P * sizeof(void*));
+        const uintptr_t sb = reinterpret_cast<uintptr_t>(shards);
+        const Range rd{sb + (uintptr_t)l.rank_begin * shard_stride * 2,
+                       sb + (uintptr_t)(l.rank_end - 1) * shard_stride * 2 + (uintptr_t)plan->S * 2,
+                       -1};
+        std::vector<Range> wr;
+        for (int32_t p = 0; p < P; ++p) {
+            const ParamInfo& q = plan->prm[p];
+            uint16_t* d = params[p];
+            tp[p] = d;
+            fl[p] = (l.flags & TIDE_FLAG_SCALAR_PATH) ? 0u : kFlagVector;
+            if (q.valid == 0) continue;
+            if (!d) return fail(TIDE_ERR_INVALID_ARG, "params[%d] is NULL", p);
+            const uintptr_t a = reinterpret_cast<uintptr_t>(d);
+            if (a & 1) return fail(TIDE_ERR_ALIGNMENT, "params[%d] is not 2-byte aligned", p);
+            if (a & 15) fl[p] = 0;
+            const Range r{a, a + (uintptr_t)q.valid * 2, p};
+            if (overlaps(r, rd)) return fail(TIDE_ERR_INVALID_ARG, "params[%d] overlaps the shards", p);
+            wr.push_back(r);
+        }
+        std::sort(wr.begin(), wr.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+        for (size_t i = 1; i < wr.size(); ++i)
+            if (wr[i].lo < wr[i - 1].hi)
+                return fail(TIDE_ERR_INVALID_ARG, "params[%d] and params[%d] overlap", wr[i - 1].who,
+                            wr[i].who);
+        hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+        if (engine == TIDE_ENGINE_SDMA) {
+            // One 2-D copy per parameter for its full pieces (rows of s_p
+            // elements, source pitch = shard stride, destination contiguous),
+            // plus one 1-D copy for a partial last piece.
+            for (int32_t p = 0; p < P; ++p) {
+                const ParamInfo& q = plan->prm[p];
+                if (q.valid == 0) continue;
+                const int64_t full = q.valid / q.s;                   // ranks with a whole piece
+                const int64_t fb = std::min<int64_t>(l.rank_begin, full);
+                const int64_t fe = std::min<int64_t>(l.rank_end, full);
+                const uint16_t* src0 = shards + q.o;
+                if (fe > fb)
+                    TIDE_HIP_TRY(hipMemcpy2DAsync(params[p] + fb * q.s, (size_t)q.s * 2,
+                                                  src0 + fb * shard_stride,
+                                                  (size_t)shard_stride * 2, (size_t)q.s * 2,
+                                                  (size_t)(fe - fb), hipMemcpyDeviceToDevice,
+                                                  stream));
+                const int64_t rem = q.valid - full * q.s;
+                if (rem > 0 && full >= l.rank_begin && full < l.rank_end)
+                    TIDE_HIP_TRY(hipMemcpyAsync(params[p] + full * q.s, src0 + full * shard_stride,
+                                                (size_t)rem * 2, hipMemcpyDeviceToDevice, stream));
+            }
+            return TIDE_OK;
+        }
+        std::lock_guard<std::mutex> lock(plan->mu);
+        int dev;
+        st = stream_device(stream, &dev);
+        if (st != TIDE_OK) return st;
+        DevState* ds;
+        st = get_dev_state(plan, dev, &ds);
+        if (st != TIDE_OK) return st;
+        TileTable* tt;
+        st = get_tiles(plan, ds, 1, l.rank_begin, l.rank_end, &tt);
+        if (st != TIDE_OK) return st;
+        if (tt->count == 0) return TIDE_OK;
+        int slot;
+        st = stage_table(ds, table.data(), table.size(), stream, &slot);
+        if (st != TIDE_OK) return st;
+        char* base = static_cast<char*>(ds->slots[slot].dev);
+        uint16_t* const* dptrs = reinterpret_cast<uint16_t* const*>(base);
+        const uint32_t* dflags = reinterpret_cast<const uint32_t*>(base + (size_t)P * sizeof(void*));
+        st = for_each_launch(plan, 1, l, tt->count, [&](int grid, int64_t lo, int64_t hi) {
+            return launch_place(grid, stream, tt->dev, lo, hi, ds->params, dptrs, dflags, shards,
+                                shard_stride, shard_elems);
+        });
+        tide_status st2 = release_slot(ds, slot, stream);
+        return st != TIDE_OK ? st : st2;
+    } catch (const std::bad_alloc&) {
+        return fail(TIDE_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return fail(TIDE_ERR_INVALID_ARG, "unexpected exception");
+    }
+}
+
+const char* tide_status_string(tide_status s) {
+    switch (s) {
+        case TIDE_OK: return "TIDE_OK";
+        case TIDE_ERR_INVALID_ARG: return "TIDE_ERR_INVALID_ARG";
+        case TIDE_ERR_ALIGNMENT: return "TIDE_ERR_ALIGNMENT";
+        case TIDE_ERR_OVERFLOW: return "TIDE_ERR_OVERFLOW";
+        case TIDE_ERR_UNSUPPORTED: return "TIDE_ERR_UNSUPPORTED";
+        case TIDE_ERR_NO_MEMORY: return "TIDE_ERR_NO_MEMORY";
+        case TIDE_ERR_HIP: return "TIDE_ERR_HIP";
+    }
+    return "TIDE_ERR_UNKNOWN";
+}
+
+const char* tide_last_error_detail(void) { return g_detail.c_str(); }
+
+int32_t tide_version(void) { return (1 << 16) | 0; }
+
+}  // extern "C"

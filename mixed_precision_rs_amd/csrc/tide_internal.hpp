@@ -1,0 +1,57 @@
+// Internal declarations shared by the host planner (plan.cpp) and the HIP
+// kernels (kernels.hip). Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tide {
+
+constexpr int kThreads = 256;              // workgroup size: 4 wave64s
+constexpr int kVec = 8;                    // elements a thread handles per step (16 B of bf16)
+constexpr int kStep = kThreads * kVec;     // elements a workgroup handles per step
+constexpr int kRsUnroll = 2;               // steps whose loads a reduce thread keeps in flight
+constexpr int kAgUnroll = 4;               // same, placement
+constexpr int64_t kRsTile = 8 * kStep;     // elements per reduce tile (16384)
+constexpr int64_t kAgTile = 16 * kStep;    // elements per placement tile (32768)
+static_assert(kRsTile % (kRsUnroll * kStep) == 0, "tile must hold whole groups");
+static_assert(kAgTile % (kAgUnroll * kStep) == 0, "tile must hold whole groups");
+
+// One unit of work: a run of up to one tile of flat element indices inside one
+// parameter. For the reduce, the flat index runs over the parameter's padded
+// storage [0, N * s_p) (index f is rank f / s_p, offset f % s_p of its piece);
+// for the placement, over its true elements [0, T_p * K_p).
+struct TileRec {
+    int64_t idx0;   // first index of the tile, a multiple of kVec
+    int64_t j0;     // idx0 - r0 * s_p
+    int64_t lo;     // the tile only touches indices in [lo, hi)
+    int64_t hi;
+    int32_t p;      // parameter
+    int32_t r0;     // rank that holds idx0
+    int32_t pad0, pad1;
+};
+static_assert(sizeof(TileRec) == 48, "TileRec layout");
+
+struct ParamDev {
+    int64_t s;      // s_p, elements per rank piece
+    int64_t o;      // o_p, offset of the piece in a rank's shard
+    int64_t valid;  // T_p * K_p, true elements
+    int64_t pad;
+};
+static_assert(sizeof(ParamDev) == 32, "ParamDev layout");
+
+// Per-parameter flag bits of the per-call table.
+constexpr uint32_t kFlagVector = 1u;  // every pointer of this parameter allows 16-byte vector access
+
+// Launch wrappers (kernels.hip). Return the launch's hipError_t.
+hipError_t launch_reduce(int L, int grid, hipStream_t stream, const TileRec* tiles,
+                         int64_t tile_lo, int64_t tile_hi, const ParamDev* params,
+                         const uint16_t* const* ptrs, const uint32_t* flags, float* out,
+                         int64_t out_stride);
+
+hipError_t launch_place(int grid, hipStream_t stream, const TileRec* tiles, int64_t tile_lo,
+                        int64_t tile_hi, const ParamDev* params, uint16_t* const* ptrs,
+                        const uint32_t* flags, const uint16_t* shards, int64_t shard_stride,
+                        int64_t shard_elems);
+
+}  // namespace tide

@@ -1,0 +1,163 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every symbol that
+include/tide.h declares, plans layouts identical to the oracle's, and rejects
+bad arguments before touching the GPU. No compute call is made here."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def tide():
+    import mixed_precision_rs_amd as t
+    return t
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "tide.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tide_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(tide):
+    declared = header_functions()
+    assert set(declared) == set(tide.EXPORTS), declared
+    lib = ctypes.CDLL(tide.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(tide):
+    lib = tide.lib()
+    for code, name in tide._lib.STATUS_NAMES.items():
+        assert lib.tide_status_string(code).decode() == name
+    assert lib.tide_status_string(99).decode() == "TIDE_ERR_UNKNOWN"
+    assert tide.version() >> 16 == 1
+
+
+def test_layout_equals_oracle(tide, orc):
+    from workloads.configs import CONFIGS, padding_stress_shapes
+    groups = [(c.shapes, c.N) for c in CONFIGS.values()]
+    groups += [(padding_stress_shapes(s, count=30, max_rows=40, ks=(1, 2, 3, 7)), n)
+               for s, n in [(1, 5), (2, 16), (3, 1)]]
+    for shapes, N in groups:
+        plan = tide.plan_create(shapes, N, 8)
+        lay = orc.layout(shapes, N)
+        assert plan.S == lay["S"]
+        for p, (t, k) in enumerate(shapes):
+            T, K, R, s, o = plan.param(p)
+            assert (T, K, R, s, o) == (t, k, lay["R"][p], lay["s"][p], lay["o"][p])
+        for r in sorted({0, min(1, N - 1), N // 2, N - 1}):
+            for p in range(0, len(shapes), max(1, len(shapes) // 7)):
+                rm, pm, valid = plan.map(r, p)
+                orm, _, opmg = orc.piece_start(shapes, N, r, p)
+                assert (rm, pm) == (orm, opmg)
+                _, nrows = orc.piece_rows(shapes, N, r, p)
+                assert valid == nrows * shapes[p][1]
+
+
+def test_worked_example_map(tide):
+    with open(os.path.join(ROOT, "tests", "golden", "worked_example.json")) as f:
+        g = json.load(f)
+    N = g["N"]
+    plan = tide.plan_create([(N * n, 1) for n in g["pieces_per_rank"]], N, 4)
+    rm, pm, valid = plan.map(g["rank"], g["param"])
+    assert (rm, pm) == (g["rank_major_start"], g["param_major_start"])
+    assert plan.S == g["per_rank_total"]
+
+
+def _status(fn):
+    try:
+        fn()
+    except Exception as e:  # noqa: BLE001
+        return getattr(e, "status_name", type(e).__name__)
+    return "TIDE_OK"
+
+
+def test_plan_create_rejects(tide):
+    assert _status(lambda: tide.plan_create([(4, 1)], 0, 1)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: tide.plan_create([(4, 1)], 2, 0)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: tide.plan_create([(4, 1)], 2, 65)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: tide.plan_create([(-1, 1)], 2, 1)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: tide.plan_create([(4, 0)], 2, 1)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: tide.plan_create([(1 << 40, 1 << 30)], 2, 1)) == "TIDE_ERR_OVERFLOW"
+    assert _status(lambda: tide.plan_create([(1 << 31, 1 << 31)], 1, 1)) == "TIDE_ERR_OVERFLOW"
+    assert _status(lambda: tide.plan_create([(1 << 31, 1 << 30)] * 3, 1, 1)) == "TIDE_ERR_OVERFLOW"
+    lib = tide.lib()
+    assert lib.tide_plan_create(None, None, 1, 2, 1, ctypes.byref(ctypes.c_void_p())) == 1
+    assert lib.tide_plan_create(None, None, 0, 2, 1, None) == 1
+    # An empty group and zero-row parameters are valid.
+    assert tide.plan_create([], 4, 2).S == 0
+    p = tide.plan_create([(0, 7), (5, 2)], 4, 2)
+    assert p.param(0)[2:] == (0, 0, 0) and p.S == 4
+    assert _status(lambda: p.param(2)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: p.map(4, 0)) == "TIDE_ERR_INVALID_ARG"
+    tide.lib().tide_plan_destroy(None)          # NULL-safe
+
+
+def test_launch_count(tide):
+    from workloads.configs import CONFIGS
+    cfg = CONFIGS["wan22_dit_block"]
+    plan = tide.plan_create(cfg.shapes, cfg.N, cfg.L)
+    assert plan.launch_count(0) == 1 and plan.launch_count(1) == 1
+    b = plan.launch_count(0, tide.budgeted())
+    assert b > 4
+    assert plan.launch_count(0, tide.budgeted(max_launch_us=3000)) < b
+    assert plan.launch_count(0, tide.Launch(rank_begin=3, rank_end=3)) == 0
+    assert _status(lambda: plan.launch_count(2)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: plan.launch_count(0, tide.Launch(mode=7))) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: plan.launch_count(0, tide.Launch(rank_begin=5, rank_end=2))) == \
+        "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: plan.launch_count(0, tide.Launch(flags=0x10))) == "TIDE_ERR_INVALID_ARG"
+
+
+FAKE = 0x7f0000000000    # addresses are never dereferenced: validation fails first
+
+
+def test_compute_calls_validate_before_enqueue(tide):
+    shapes = [(8, 4), (4, 4), (12, 4)]
+    plan = tide.plan_create(shapes, 4, 2)
+    S = plan.S
+    grads = [[FAKE + 0x100000 * (c * 3 + p) for p in range(3)] for c in range(2)]
+    out = FAKE + 0x10000000
+    rs = tide.reduce_scatter_bf16_fp32
+    assert _status(lambda: rs(plan, grads, out, out_stride=S - 1, stream=0)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: rs(plan, grads, out + 2, stream=0)) == "TIDE_ERR_ALIGNMENT"
+    assert _status(lambda: rs(plan, grads, 0, stream=0)) == "TIDE_ERR_INVALID_ARG"
+    bad = [list(g) for g in grads]
+    bad[1][2] = 0
+    assert _status(lambda: rs(plan, bad, out, stream=0)) == "TIDE_ERR_INVALID_ARG"
+    bad[1][2] = FAKE + 1
+    assert _status(lambda: rs(plan, bad, out, stream=0)) == "TIDE_ERR_ALIGNMENT"
+    bad[1][2] = out + 8                      # reads overlap the written output
+    assert _status(lambda: rs(plan, bad, out, stream=0)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: rs(plan, grads, out, stream=0, launch=tide.Launch(mode=3))) == \
+        "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: rs(plan, grads, out, stream=0, launch=tide.Launch(rank_begin=-1))) == \
+        "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: rs(plan, grads, out, out_stride=1 << 62, stream=0)) == "TIDE_ERR_OVERFLOW"
+    # An empty rank range enqueues nothing and succeeds without a GPU.
+    assert _status(lambda: rs(plan, grads, out, stream=0,
+                              launch=tide.Launch(rank_begin=2, rank_end=2))) == "TIDE_OK"
+
+    ag = tide.allgather_place
+    shards = FAKE + 0x20000000
+    params = [FAKE + 0x30000000 + 0x100000 * p for p in range(3)]
+    assert _status(lambda: ag(plan, shards, params, shard_stride=S - 1, stream=0)) == \
+        "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: ag(plan, shards + 1, params, stream=0)) == "TIDE_ERR_ALIGNMENT"
+    assert _status(lambda: ag(plan, shards, params, stream=0, engine=5)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: ag(plan, shards, [params[0], params[0], params[2]], stream=0)) == \
+        "TIDE_ERR_INVALID_ARG"                # two parameters overlap
+    assert _status(lambda: ag(plan, shards, [shards + 4, params[1], params[2]], stream=0)) == \
+        "TIDE_ERR_INVALID_ARG"                # a parameter overlaps the shards
+    assert _status(lambda: ag(plan, shards, [params[0], 0, params[2]], stream=0)) == \
+        "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: ag(plan, shards, [params[0], params[1] + 1, params[2]], stream=0)) == \
+        "TIDE_ERR_ALIGNMENT"

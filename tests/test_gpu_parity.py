@@ -1,0 +1,195 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Inputs are seeded host draws copied to the device; the oracle sees the same
+bits. Every output element is compared bit for bit (fp32 NaN as a class), and
+every element outside what a call may write must keep its sentinel.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import (SENTINEL_BF16, SENTINEL_F32, bits_of, dev, same_f32, same_u16, say,
+                      to_dev_bf16)
+from workloads import host_grads, host_rank_major_bits, host_special_grads
+from workloads.configs import CONFIGS, padding_stress_shapes
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tide():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mixed_precision_rs_amd as t
+    return t
+
+
+def run_case(tide, orc, shapes, N, L, grads, *, stride_extra=0, out_off=0, grad_offs=None,
+             launch=None, rank_range=None, shard_off=0, param_offs=None, engines=("kernel",),
+             seed=0, check_ag=True):
+    """Run RS (and AG) on the GPU and compare with the oracle."""
+    P = len(shapes)
+    plan = tide.plan_create(shapes, N, L)
+    S = plan.S
+    stride = S + stride_extra
+    rb, re = (0, N) if rank_range is None else rank_range
+    if launch is None:
+        launch = tide.Launch()
+    launch.rank_begin, launch.rank_end = rb, re
+    if re == 0:
+        launch.rank_begin, launch.rank_end = N, N      # empty range
+    g_dev = [[to_dev_bf16(grads[c][p], (t, k),
+                          0 if grad_offs is None else grad_offs[c][p])
+              for p, (t, k) in enumerate(shapes)] for c in range(L)]
+    out_buf = torch.full((N * stride + out_off + 4,), float(SENTINEL_F32), dtype=torch.float32,
+                         device=dev())
+    out = out_buf[out_off:out_off + N * stride]
+    tide.reduce_scatter_bf16_fp32(plan, g_dev, out, out_stride=stride, launch=launch)
+    torch.cuda.synchronize()
+    want = np.full(N * stride, SENTINEL_F32, dtype=np.float32)
+    if re > rb:
+        orc.reduce_scatter(shapes, N, L, grads, out_stride=stride, rank_range=(rb, re), out=want)
+    same_f32(bits_of(out), want, "reduce-scatter")
+    tail = bits_of(out_buf)
+    assert np.all(tail[:out_off] == SENTINEL_F32) and np.all(tail[out_off + N * stride:] == SENTINEL_F32)
+    if not check_ag:
+        return
+    shards_bits = host_rank_major_bits(N * stride, seed=seed + 17)
+    sh = to_dev_bf16(shards_bits, (N * stride,), shard_off)
+    want_p = [np.full(t * k, SENTINEL_BF16, np.uint16) for t, k in shapes]
+    if re > rb:
+        orc.allgather_place(shapes, N, shards_bits, shard_stride=stride, rank_range=(rb, re),
+                            params=want_p)
+    for eng in engines:
+        params = [to_dev_bf16(np.full(t * k, SENTINEL_BF16, np.uint16), (t, k),
+                              0 if param_offs is None else param_offs[p])
+                  for p, (t, k) in enumerate(shapes)]
+        tide.allgather_place(plan, sh, params, shard_stride=stride, engine=eng, launch=launch)
+        torch.cuda.synchronize()
+        for p in range(P):
+            same_u16(bits_of(params[p]), want_p[p], "placement[%s] param %d" % (eng, p))
+
+
+def test_worked_example_group(tide, orc):
+    cfg = CONFIGS["worked_example"]
+    grads = host_grads(cfg.shapes, cfg.L, seed=0, sigma=cfg.sigma)
+    say("worked example: full grid, kernel + sdma")
+    run_case(tide, orc, list(cfg.shapes), cfg.N, cfg.L, grads, engines=("kernel", "sdma"))
+    say("worked example: budgeted")
+    run_case(tide, orc, list(cfg.shapes), cfg.N, cfg.L, grads, launch=tide.budgeted())
+
+
+def test_special_values(tide, orc):
+    """Subnormals, signed zeros, infinities, huge values (NaN from inf - inf)."""
+    shapes, N, L = [(37, 3), (5, 16), (64, 8), (3, 1)], 8, 8
+    grads = host_special_grads(shapes, L, seed=11)
+    run_case(tide, orc, shapes, N, L, grads)
+    run_case(tide, orc, shapes, N, L, grads, launch=tide.Launch(flags=tide.FLAG_SCALAR_PATH))
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_fuzz(tide, orc, case):
+    rng = np.random.default_rng(1000 + case)
+    P = int(rng.integers(1, 9))
+    N = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 16, 48, 64]))
+    L = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 8, 8, 11, 16]))
+    shapes = []
+    for _ in range(P):
+        k = int(rng.choice([1, 2, 3, 5, 8, 16, 24, 64, 100, 1000, 4096]))
+        t = int(rng.integers(0, max(2, min(4 * N + 9, 200000 // k))))
+        shapes.append((t, k))
+    if case % 5 == 0:
+        grads = host_special_grads(shapes, L, seed=case)
+    else:
+        grads = host_grads(shapes, L, seed=case, sigma=float(rng.choice([1e-3, 1.0, 300.0])))
+    stride_extra = int(rng.choice([0, 0, 1, 3, 8]))
+    out_off = int(rng.choice([0, 0, 1, 2, 3]))
+    grad_offs = [[int(rng.choice([0, 0, 0, 1, 3, 4, 8])) for _ in shapes] for _ in range(L)]
+    param_offs = [int(rng.choice([0, 0, 1, 8])) for _ in shapes]
+    shard_off = int(rng.choice([0, 1, 2, 3]))
+    mode = int(rng.integers(0, 3))
+    launch = [tide.Launch(), tide.budgeted(reduce_blocks=int(rng.integers(1, 17)),
+                                           place_blocks=int(rng.integers(1, 5)), max_launch_us=1),
+              tide.Launch(flags=tide.FLAG_SCALAR_PATH)][mode]
+    rr = None
+    if N > 1 and rng.random() < 0.4:
+        a = int(rng.integers(0, N))
+        b = int(rng.integers(a, N + 1))
+        rr = (a, b) if b > a else (0, 0)
+    say("fuzz %d: P=%d N=%d L=%d shapes=%s stride+%d out+%d shard+%d mode=%d ranks=%s" % (
+        case, P, N, L, shapes, stride_extra, out_off, shard_off, mode, rr))
+    run_case(tide, orc, shapes, N, L, grads, stride_extra=stride_extra, out_off=out_off,
+             grad_offs=grad_offs, launch=launch, rank_range=rr, shard_off=shard_off,
+             param_offs=param_offs, engines=("kernel", "sdma"), seed=case)
+
+
+def test_multi_tile_ragged_group(tide, orc):
+    """A padding-stress-shaped group small enough for the oracle to check in
+    full: many tiles per parameter, ragged tails, K = 1 straddles, misaligned
+    prefix offsets, outliers."""
+    shapes = padding_stress_shapes(3, count=30, max_rows=500, ks=(1, 64, 4096))
+    N, L = 48, 8
+    grads = host_grads(shapes, L, seed=3, sigma=1.0, outlier_frac=0.01)
+    say("multi-tile group: %d params, %d elements" % (len(shapes), sum(t * k for t, k in shapes)))
+    run_case(tide, orc, shapes, N, L, grads, engines=("kernel", "sdma"))
+    say("multi-tile group: budgeted, rank subset")
+    run_case(tide, orc, shapes, N, L, grads, launch=tide.budgeted(max_launch_us=20),
+             rank_range=(5, 29))
+
+
+def test_runtime_contributor_count(tide, orc):
+    """L above 8 takes the runtime-L kernel."""
+    shapes = [(300, 64), (17, 1), (1000, 40)]
+    for L in (9, 16):
+        grads = host_grads(shapes, L, seed=L)
+        run_case(tide, orc, shapes, 6, L, grads, check_ag=False)
+
+
+def test_empty_and_degenerate(tide, orc):
+    # zero-row parameters, T < N, a single rank, one element
+    for shapes, N, L in [([(0, 5), (3, 2), (0, 1)], 4, 2), ([(1, 1)], 1, 1),
+                         ([(2, 3)], 64, 8), ([(5, 8192)], 1, 3)]:
+        grads = host_grads(shapes, L, seed=N)
+        run_case(tide, orc, shapes, N, L, grads, engines=("kernel", "sdma"))
+    plan = tide.plan_create([], 4, 2)
+    tide.reduce_scatter_bf16_fp32(plan, [[], []], None)
+    tide.allgather_place(plan, None, [])
+
+
+def test_streams_and_repeat(tide, orc):
+    """Calls on a side stream, and repeated calls with changing and unchanged
+    pointers (the per-call table cache), all give the oracle's result."""
+    shapes, N, L = [(129, 33), (64, 1), (7, 500)], 4, 3
+    plan = tide.plan_create(shapes, N, L)
+    side = torch.cuda.Stream()
+    for it in range(12):
+        grads = host_grads(shapes, L, seed=it % 3)
+        g_dev = [[to_dev_bf16(grads[c][p], (t, k)) for p, (t, k) in enumerate(shapes)]
+                 for c in range(L)]
+        out = torch.empty(N * plan.S, dtype=torch.float32, device=dev())
+        s = side if it % 2 else torch.cuda.current_stream()
+        s.wait_stream(torch.cuda.current_stream())      # inputs were copied on the current stream
+        for _ in range(3):
+            tide.reduce_scatter_bf16_fp32(plan, g_dev, out, stream=s)
+        torch.cuda.synchronize()
+        same_f32(bits_of(out), orc.reduce_scatter(shapes, N, L, grads).reshape(-1), "iter %d" % it)
+
+
+def test_no_device_allocation_on_repeat(tide):
+    """After the first call (which builds the plan's small device tables) a
+    call allocates no device memory: gradients are read in place, with no
+    packed or upcast copy."""
+    cfg = CONFIGS["wan22_dit_block"]
+    shapes = [(t // 8 or 1, k) for t, k in cfg.shapes]
+    plan = tide.plan_create(shapes, cfg.N, cfg.L)
+    g = [[torch.zeros((t, k), dtype=torch.bfloat16, device=dev()) for t, k in shapes]
+         for _ in range(cfg.L)]
+    out = torch.empty(cfg.N * plan.S, dtype=torch.float32, device=dev())
+    tide.reduce_scatter_bf16_fp32(plan, g, out)
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    for _ in range(5):
+        tide.reduce_scatter_bf16_fp32(plan, g, out)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 == free0
