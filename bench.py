@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Benchmark of the one-GPU hot path of TIDE's layout-aware FSDP2 collectives
+on MI355X: the level-1 bf16 -> fp32 reduce-scatter into padded rank-major
+shards, then the all-gather placement into parameter storage.
+
+One step = one reduce-scatter + one placement (HIP kernel engine) of one
+parameter group, back to back on one stream, inputs already in HBM.
+value = algorithmic bytes per step / time per step:
+    reduce-scatter: 2 * L * valid (bf16 reads) + 4 * N * S (fp32 writes,
+                    padding included), placement: 2 * valid + 2 * valid.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--parts] [--victim] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "effective HBM GB/s (and % of 8 TB/s) for bf16->fp32 layout RS + AG placement"
+KERNEL_SOURCES = [os.path.join(ROOT, "mixed_precision_rs_amd", "csrc", f)
+                  for f in ("kernels.hip", "tide_internal.hpp")]
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per reduce launch measured with rocprofv3 counters, if a
+    summary for this workload exists and was taken on the current kernels."""
+    path = os.path.join(PROFILES, "reduce_kernel_%s_counters.md" % workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return int(m_bytes.group(1))
+
+
+def group_bytes(cfg, S):
+    valid = sum(t * k for t, k in cfg.shapes)
+    rs = 2 * cfg.L * valid + 4 * cfg.N * S
+    ag = 4 * valid
+    return rs, ag, valid
+
+
+def cpu_baseline(orc, cfg, plan, grads, shards, out, ranks):
+    """Time the CPU oracle (one thread) on ranks [0, ranks) of the same group,
+    with the same bits copied from the GPU; check the GPU's shards there."""
+    import numpy as np
+    import torch
+    N, L, S = cfg.N, cfg.L, plan.S
+    lay = orc.layout(cfg.shapes, N)
+    h_grads, valid = [], 0
+    for c in range(L):
+        row = []
+        for p, (t, k) in enumerate(cfg.shapes):
+            nrows = min(t, ranks * int(lay["R"][p]))
+            row.append(grads[c][p][:nrows].reshape(-1).view(torch.int16).cpu().numpy()
+                       .view(np.uint16))
+            if c == 0:
+                valid += nrows * k
+        h_grads.append(row)
+    h_out = np.empty(N * S, np.float32)
+    orc.reduce_scatter(cfg.shapes, N, L, h_grads, rank_range=(0, ranks), out=h_out)
+    t_rs = orc.last_call_s
+    gpu_part = out[: ranks * S].cpu().numpy()
+    exact = bool(np.array_equal(gpu_part.view(np.uint32), h_out[: ranks * S].view(np.uint32)))
+    h_sh = np.zeros(N * S, np.uint16)
+    h_sh[: ranks * S] = shards[: ranks * S].view(torch.int16).cpu().numpy().view(np.uint16)
+    h_params = [np.zeros(min(t, ranks * int(lay["R"][p])) * k, np.uint16)
+                for p, (t, k) in enumerate(cfg.shapes)]
+    orc.allgather_place(cfg.shapes, N, h_sh, rank_range=(0, ranks), params=h_params)
+    t_ag = orc.last_call_s
+    nbytes = 2 * L * valid + 4 * ranks * S + 4 * valid
+    return {
+        "value": round(nbytes / (t_rs + t_ag) / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "ranks 0-%d of %d of the same group (all %d params), reduce-scatter + "
+                  "placement, same bits copied from the GPU; %.1f s reduce + %.1f s placement "
+                  "on one core" % (ranks - 1, N, len(cfg.shapes), t_rs, t_ag),
+        "gpu_shards_bit_exact_on_sample": exact,
+    }
+
+
+def copy_ceiling_gbps(torch, nbytes=4 << 30, iters=10):
+    """Read+write GB/s of a plain device-to-device copy (practical ceiling)."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    del a, b
+    return 2 * nbytes / (ms / 1e3) / 1e9
+
+
+def victim_slowdown(torch, tide, plan, grads, out, shards, params, launch, reps=3, nb=4):
+    """Slowdown of a 256x8192x8192 bf16 GEMM while the reduce-scatter +
+    placement run on another stream (median GEMM time, concurrent vs alone).
+
+    The GEMMs cycle through `nb` different B matrices (nb * 128 MiB, more than
+    the 256 MB Infinity Cache), so neither measurement finds B cached from the
+    previous GEMM: both read it from HBM, as a training step's GEMMs do."""
+    A = torch.randn(256, 8192, device="cuda", dtype=torch.bfloat16)
+    Bs = [torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16) for _ in range(nb)]
+    C = torch.empty(256, 8192, device="cuda", dtype=torch.bfloat16)
+    gs = torch.cuda.Stream()
+    cs = torch.cuda.Stream()
+    for i in range(20):
+        torch.matmul(A, Bs[i % nb], out=C)
+    torch.cuda.synchronize()
+
+    def gemm_times(n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        with torch.cuda.stream(gs):
+            for i, (a, b) in enumerate(evs):
+                a.record(gs)
+                torch.matmul(A, Bs[i % nb], out=C)
+                b.record(gs)
+        return evs
+
+    alone = gemm_times(200)
+    torch.cuda.synchronize()
+    t_alone = statistics.median(a.elapsed_time(b) for a, b in alone)
+    # Concurrent: the collective on cs, GEMMs back to back on gs. Count the
+    # GEMMs that run entirely inside the collective's window; if none does
+    # (a full-grid collective is shorter than its queueing delay), count those
+    # that overlap the window at all.
+    res = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cs.wait_stream(torch.cuda.current_stream())
+        c0.record(cs)
+        tide.reduce_scatter_bf16_fp32(plan, grads, out, stream=cs, launch=launch)
+        tide.allgather_place(plan, shards, params, stream=cs, launch=launch)
+        c1.record(cs)
+        evs = gemm_times(400)
+        torch.cuda.synchronize()
+        win = c0.elapsed_time(c1)
+        spans = [(c0.elapsed_time(a_), c0.elapsed_time(b_)) for a_, b_ in evs]
+        inside = [e - s for s, e in spans if s >= 0 and e <= win]
+        kind = "inside"
+        if not inside:
+            inside = [e - s for s, e in spans if s < win and e > 0]
+            kind = "overlapping"
+        if inside:
+            res.append((statistics.median(inside), win, len(inside), kind))
+    del A, Bs, C
+    if not res:
+        return {"gemm_ms_alone": round(t_alone, 4), "note": "no GEMM overlapped the collective"}
+    conc = statistics.median(r[0] for r in res)
+    return {"gemm_ms_alone": round(t_alone, 4), "gemm_ms_concurrent": round(conc, 4),
+            "slowdown_pct": round(100.0 * (conc / t_alone - 1.0), 2),
+            "collective_ms": round(statistics.median(r[1] for r in res), 3),
+            "gemms_counted": int(statistics.median(r[2] for r in res)),
+            "gemms_counted_are": res[0][3] + " the collective window"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama70b_layer",
+                    choices=["llama70b_layer", "qwen3_moe_layer", "padding_stress", "wan22_dit_block"])
+    ap.add_argument("--mode", default="full", choices=["full", "budgeted"])
+    ap.add_argument("--parts", action="store_true",
+                    help="also time the SDMA placement engine and a plain copy")
+    ap.add_argument("--victim", action="store_true",
+                    help="GEMM-victim slowdown, budgeted and full grid")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-ranks", type=int, default=24)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (the path is one GPU's share of "
+              "the collective); --gpus %d is not supported." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mixed_precision_rs_amd as tide
+    from workloads import device_grads, device_rank_major_bits
+    from workloads.configs import CONFIGS
+
+    cfg = CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    log("bench: %s, generating inputs" % cfg.name)
+    plan = tide.plan_create(cfg.shapes, cfg.N, cfg.L)
+    S = plan.S
+    grads = device_grads(cfg.shapes, cfg.L, seed=cfg.seed, sigma=cfg.sigma,
+                         outlier_frac=cfg.outlier_frac)
+    out = torch.empty(cfg.N * S, dtype=torch.float32, device="cuda")
+    shards = device_rank_major_bits(cfg.N * S, seed=1)
+    params = [torch.empty((t, k), dtype=torch.bfloat16, device="cuda") for t, k in cfg.shapes]
+    rs_bytes, ag_bytes, valid = group_bytes(cfg, S)
+    launch = tide.Launch() if args.mode == "full" else tide.budgeted()
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(ev):
+        ev[0].record(stream)
+        tide.reduce_scatter_bf16_fp32(plan, grads, out, stream=stream, launch=launch)
+        ev[1].record(stream)
+        tide.allgather_place(plan, shards, params, stream=stream, launch=launch)
+        ev[2].record(stream)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(args.warmup + args.steps)]
+    log("bench: %d warmup steps" % args.warmup)
+    for i in range(args.warmup):
+        step(evs[i])
+    torch.cuda.synchronize()
+    log("bench: %d timed steps" % args.steps)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[args.warmup + i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    timed = evs[args.warmup:]
+    rs_ms = [a.elapsed_time(b) for a, b, _ in timed]
+    ag_ms = [b.elapsed_time(c) for _, b, c in timed]
+    rs_avg, ag_avg = statistics.mean(rs_ms), statistics.mean(ag_ms)
+    value = (rs_bytes + ag_bytes) / (ms_per_step / 1e3) / 1e9
+    achieved = rs_bytes / (rs_avg / 1e3) / 1e9
+    log("bench: %.3f ms/step, %.1f GB/s; reduce %.3f ms (%.1f GB/s), placement %.3f ms (%.1f GB/s)"
+        % (ms_per_step, value, rs_avg, achieved, ag_avg, ag_bytes / (ag_avg / 1e3) / 1e9))
+
+    parts = {
+        "reduce_ms_mean": round(rs_avg, 4), "reduce_ms_median": round(statistics.median(rs_ms), 4),
+        "reduce_ms_min": round(min(rs_ms), 4),
+        "placement_ms_mean": round(ag_avg, 4),
+        "placement_ms_median": round(statistics.median(ag_ms), 4),
+        "reduce_GBps": round(achieved, 1),
+        "placement_GBps": round(ag_bytes / (ag_avg / 1e3) / 1e9, 1),
+        "reduce_bytes": rs_bytes, "placement_bytes": ag_bytes,
+        "pct_of_8TBps": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "reduce_launches_per_call": plan.launch_count(0, launch),
+        "placement_launches_per_call": plan.launch_count(1, launch),
+    }
+    if args.parts:
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        tide.allgather_place(plan, shards, params, engine="sdma")
+        torch.cuda.synchronize()
+        e[0].record()
+        for _ in range(5):
+            tide.allgather_place(plan, shards, params, engine="sdma")
+        e[1].record()
+        torch.cuda.synchronize()
+        sd = e[0].elapsed_time(e[1]) / 5
+        parts["placement_sdma_ms"] = round(sd, 4)
+        parts["placement_sdma_GBps"] = round(ag_bytes / (sd / 1e3) / 1e9, 1)
+        parts["plain_copy_GBps"] = round(copy_ceiling_gbps(torch), 1)
+        log("bench: sdma placement %.3f ms, plain copy %.1f GB/s" % (sd, parts["plain_copy_GBps"]))
+
+    victim = None
+    if args.victim:
+        log("bench: GEMM victim, budgeted")
+        victim = {"budgeted_16_4": victim_slowdown(torch, tide, plan, grads, out, shards, params,
+                                                   tide.budgeted()),
+                  "full_grid": victim_slowdown(torch, tide, plan, grads, out, shards, params,
+                                               tide.Launch())}
+        log("bench: victim %s" % json.dumps(victim))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("bench: CPU oracle baseline on ranks 0-%d" % (args.cpu_ranks - 1))
+        cpu = cpu_baseline(oracle.load(), cfg, plan, grads, shards, out, args.cpu_ranks)
+        log("bench: cpu %s" % json.dumps(cpu))
+
+    traffic = counter_traffic(cfg.name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "params": len(cfg.shapes), "N": cfg.N, "L": cfg.L,
+                   "S": S, "valid_elements": valid, "bytes_per_step": rs_bytes + ag_bytes,
+                   "launch": args.mode, "placement_engine": "kernel",
+                   "inputs": "bf16 grads %s, seeded on device" % (
+                       "N(0,%g)" % cfg.sigma + (" + %g outliers" % cfg.outlier_frac
+                                                if cfg.outlier_frac else ""))},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": "reduce_kernel<%d>" % cfg.L},
+        "cpu_baseline": cpu,
+        "parts": parts,
+    }
+    if victim is not None:
+        line["victim_gemm_256x8192x8192"] = victim
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,7 +9,8 @@ import os
 from typing import List, Optional, Sequence, Tuple, Union
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libtide.so")
+# TIDE_LIBRARY may name another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("TIDE_LIBRARY") or os.path.join(HERE, "libtide.so")
 
 TIDE_OK = 0
 STATUS_NAMES = {0: "TIDE_OK", 1: "TIDE_ERR_INVALID_ARG", 2: "TIDE_ERR_ALIGNMENT",

@@ -41,6 +41,24 @@ __device__ __forceinline__ TIDE_GLOBAL T* gbl_mut(void* p) {
     return (TIDE_GLOBAL T*)(p);
 }
 
+// Streaming (non-temporal) loads and stores: every byte is touched once.
+#ifndef TIDE_NT_LOAD
+#define TIDE_NT_LOAD 1
+#endif
+#ifndef TIDE_NT_STORE
+#define TIDE_NT_STORE 1
+#endif
+#if TIDE_NT_LOAD
+#define TIDE_LD(p) __builtin_nontemporal_load(p)
+#else
+#define TIDE_LD(p) (*(p))
+#endif
+#if TIDE_NT_STORE
+#define TIDE_ST(v, p) __builtin_nontemporal_store((v), (p))
+#else
+#define TIDE_ST(v, p) (*(p) = (v))
+#endif
+
 // Exact bf16 -> fp32 widening of the low / high half of a dword.
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -84,8 +102,8 @@ __device__ __forceinline__ void store8(const TileRec& t, const ParamDev& pd, int
         float* dst = out + r * stride + pd.o + j;
         const f32x4_a4 x0 = {a[0], a[1], a[2], a[3]};
         const f32x4_a4 x1 = {a[4], a[5], a[6], a[7]};
-        __builtin_nontemporal_store(x0, reinterpret_cast<f32x4_a4*>(dst));
-        __builtin_nontemporal_store(x1, reinterpret_cast<f32x4_a4*>(dst + 4));
+        TIDE_ST(x0, reinterpret_cast<f32x4_a4*>(dst));
+        TIDE_ST(x1, reinterpret_cast<f32x4_a4*>(dst + 4));
     } else {
         // The 8 elements straddle two or more ranks' pieces.
 #pragma unroll 1
@@ -98,8 +116,8 @@ __device__ __forceinline__ void store8(const TileRec& t, const ParamDev& pd, int
 
 // Reduce: out[rank piece] = fold_c widen(g[c][f]) for f < valid, +0 past it.
 // LT > 0: L known at compile time (fully unrolled); LT == 0: runtime L.
-template <int LT>
-__global__ __launch_bounds__(kThreads) void reduce_kernel(
+template <int LT, int NT>
+__global__ __launch_bounds__(NT) void reduce_kernel(
     const TileRec* __restrict__ tiles, int64_t tile_lo, int64_t tile_hi,
     const ParamDev* __restrict__ params, const uint16_t* const* __restrict__ ptrs,
     const uint32_t* __restrict__ flags, int Lrt, float* __restrict__ out, int64_t out_stride) {
@@ -110,21 +128,22 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(
         const uint16_t* const* g = ptrs + (int64_t)tr.p * L;
         const bool vec = (flags[tr.p] & kFlagVector) != 0;
         const int64_t end = min(tr.idx0 + kRsTile, tr.hi);
-        for (int64_t g0 = tr.idx0; g0 < end; g0 += kRsUnroll * kStep) {
-            const int64_t g1 = g0 + kRsUnroll * kStep;
+        for (int64_t g0 = tr.idx0; g0 < end; g0 += kRsUnroll * (NT * kVec)) {
+            const int64_t g1 = g0 + kRsUnroll * (NT * kVec);
             const bool interior = vec && g0 >= tr.lo && g1 <= end;
             const int64_t f0 = g0 + (int64_t)threadIdx.x * kVec;
             if (interior && g1 <= pd.valid) {
                 // All L * kRsUnroll loads are independent of the adds, so they
                 // are all issued before the first add waits.
                 float a[kRsUnroll][kVec];
-#pragma unroll
+                constexpr int kCUnroll = LT > 0 ? LT : 1;
+#pragma unroll kCUnroll
                 for (int c = 0; c < L; ++c) {
                     const TIDE_GLOBAL u32x4* gc = gbl<u32x4>(g[c] + f0);
                     u32x4 v[kRsUnroll];
 #pragma unroll
                     for (int u = 0; u < kRsUnroll; ++u)
-                        v[u] = __builtin_nontemporal_load(gc + u * (kStep / kVec));
+                        v[u] = TIDE_LD(gc + u * ((NT * kVec) / kVec));
 #pragma unroll
                     for (int u = 0; u < kRsUnroll; ++u) {
 #pragma unroll
@@ -141,19 +160,19 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(
                 }
 #pragma unroll
                 for (int u = 0; u < kRsUnroll; ++u)
-                    store8(tr, pd, f0 + (int64_t)u * kStep, a[u], out, out_stride);
+                    store8(tr, pd, f0 + (int64_t)u * (NT * kVec), a[u], out, out_stride);
             } else if (interior && g0 >= pd.valid) {
                 float z[kVec];
 #pragma unroll
                 for (int e = 0; e < kVec; ++e) z[e] = 0.0f;
 #pragma unroll
                 for (int u = 0; u < kRsUnroll; ++u)
-                    store8(tr, pd, f0 + (int64_t)u * kStep, z, out, out_stride);
+                    store8(tr, pd, f0 + (int64_t)u * (NT * kVec), z, out, out_stride);
             } else {
                 // Ragged edge: element by element, exact bounds.
 #pragma unroll 1
                 for (int u = 0; u < kRsUnroll; ++u) {
-                    const int64_t fu = f0 + (int64_t)u * kStep;
+                    const int64_t fu = f0 + (int64_t)u * (NT * kVec);
                     int64_t r, j;
                     locate<kRsTile>(tr, pd.s, fu, r, j);
 #pragma unroll 1
@@ -184,13 +203,13 @@ __device__ __forceinline__ u32x4 gather8(const TileRec& t, const ParamDev& pd, i
         const int64_t e = r * stride + pd.o + j;
         const uint16_t* src = shards + e;
         if ((reinterpret_cast<uintptr_t>(src) & 3) == 0)
-            return __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4*>(src));
+            return TIDE_LD(reinterpret_cast<const u32x4_a4*>(src));
         if (e >= 1 && e + 9 <= shard_elems) {
             // src is 2 mod 4: load the 5 dwords covering elements e-1 .. e+8
             // (all inside the shard buffer) and shift them down 16 bits.
             const uint32_t* d = reinterpret_cast<const uint32_t*>(src - 1);
-            const u32x4_a4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4*>(d));
-            const uint32_t y = __builtin_nontemporal_load(d + 4);
+            const u32x4_a4 x = TIDE_LD(reinterpret_cast<const u32x4_a4*>(d));
+            const uint32_t y = TIDE_LD(d + 4);
             u32x4 w;
             w[0] = __builtin_amdgcn_alignbit(x[1], x[0], 16);
             w[1] = __builtin_amdgcn_alignbit(x[2], x[1], 16);
@@ -213,7 +232,8 @@ __device__ __forceinline__ u32x4 gather8(const TileRec& t, const ParamDev& pd, i
 }
 
 // Placement: param[f] = shards[rank(f) * stride + o_p + offset(f)] for true f.
-__global__ __launch_bounds__(kThreads) void place_kernel(
+template <int NT>
+__global__ __launch_bounds__(NT) void place_kernel(
     const TileRec* __restrict__ tiles, int64_t tile_lo, int64_t tile_hi,
     const ParamDev* __restrict__ params, uint16_t* const* __restrict__ ptrs,
     const uint32_t* __restrict__ flags, const uint16_t* __restrict__ shards, int64_t stride,
@@ -224,23 +244,23 @@ __global__ __launch_bounds__(kThreads) void place_kernel(
         uint16_t* dst = ptrs[tr.p];
         const bool vec = (flags[tr.p] & kFlagVector) != 0;
         const int64_t end = min(tr.idx0 + kAgTile, tr.hi);
-        for (int64_t g0 = tr.idx0; g0 < end; g0 += kAgUnroll * kStep) {
-            const int64_t g1 = g0 + kAgUnroll * kStep;
+        for (int64_t g0 = tr.idx0; g0 < end; g0 += kAgUnroll * (NT * kVec)) {
+            const int64_t g1 = g0 + kAgUnroll * (NT * kVec);
             const int64_t f0 = g0 + (int64_t)threadIdx.x * kVec;
             if (vec && g0 >= tr.lo && g1 <= end) {
                 u32x4 w[kAgUnroll];
 #pragma unroll
                 for (int u = 0; u < kAgUnroll; ++u)
-                    w[u] = gather8(tr, pd, f0 + (int64_t)u * kStep, shards, stride, shard_elems);
+                    w[u] = gather8(tr, pd, f0 + (int64_t)u * (NT * kVec), shards, stride, shard_elems);
                 TIDE_GLOBAL u32x4* d4 = gbl_mut<u32x4>(dst + f0);
 #pragma unroll
                 for (int u = 0; u < kAgUnroll; ++u)
-                    __builtin_nontemporal_store(w[u], d4 + u * (kStep / kVec));
+                    TIDE_ST(w[u], d4 + u * ((NT * kVec) / kVec));
             } else {
                 TIDE_GLOBAL uint16_t* d = gbl_mut<uint16_t>(dst);
 #pragma unroll 1
                 for (int u = 0; u < kAgUnroll; ++u) {
-                    const int64_t fu = f0 + (int64_t)u * kStep;
+                    const int64_t fu = f0 + (int64_t)u * (NT * kVec);
                     int64_t r, j;
                     locate<kAgTile>(tr, pd.s, fu, r, j);
 #pragma unroll 1
@@ -256,25 +276,27 @@ __global__ __launch_bounds__(kThreads) void place_kernel(
 }
 
 template <int LT>
-hipError_t launch_reduce_t(int L, int grid, hipStream_t stream, const TileRec* tiles,
-                           int64_t tile_lo, int64_t tile_hi, const ParamDev* params,
-                           const uint16_t* const* ptrs, const uint32_t* flags, float* out,
-                           int64_t out_stride) {
+hipError_t launch_reduce_t(int L, int grid, int threads, size_t lds, hipStream_t stream,
+                           const TileRec* tiles, int64_t tile_lo, int64_t tile_hi,
+                           const ParamDev* params, const uint16_t* const* ptrs,
+                           const uint32_t* flags, float* out, int64_t out_stride) {
     void* args[] = {&tiles, &tile_lo, &tile_hi, &params, &ptrs, &flags, &L, &out, &out_stride};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&reduce_kernel<LT>), dim3(grid),
-                           dim3(kThreads), args, 0, stream);
+    const void* fn = threads == kFatThreads
+                         ? reinterpret_cast<const void*>(&reduce_kernel<LT, kFatThreads>)
+                         : reinterpret_cast<const void*>(&reduce_kernel<LT, kThreads>);
+    return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, lds, stream);
 }
 
 }  // namespace
 
-hipError_t launch_reduce(int L, int grid, hipStream_t stream, const TileRec* tiles,
-                         int64_t tile_lo, int64_t tile_hi, const ParamDev* params,
-                         const uint16_t* const* ptrs, const uint32_t* flags, float* out,
-                         int64_t out_stride) {
+hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t stream,
+                         const TileRec* tiles, int64_t tile_lo, int64_t tile_hi,
+                         const ParamDev* params, const uint16_t* const* ptrs,
+                         const uint32_t* flags, float* out, int64_t out_stride) {
 #define TIDE_REDUCE_CASE(n)                                                                   \
     case n:                                                                                   \
-        return launch_reduce_t<n>(L, grid, stream, tiles, tile_lo, tile_hi, params, ptrs,    \
-                                  flags, out, out_stride);
+        return launch_reduce_t<n>(L, grid, threads, lds, stream, tiles, tile_lo, tile_hi,    \
+                                  params, ptrs, flags, out, out_stride);
     switch (L) {
         TIDE_REDUCE_CASE(1)
         TIDE_REDUCE_CASE(2)
@@ -285,20 +307,54 @@ hipError_t launch_reduce(int L, int grid, hipStream_t stream, const TileRec* til
         TIDE_REDUCE_CASE(7)
         TIDE_REDUCE_CASE(8)
         default:
-            return launch_reduce_t<0>(L, grid, stream, tiles, tile_lo, tile_hi, params, ptrs,
-                                      flags, out, out_stride);
+            return launch_reduce_t<0>(L, grid, threads, lds, stream, tiles, tile_lo, tile_hi,
+                                      params, ptrs, flags, out, out_stride);
     }
 #undef TIDE_REDUCE_CASE
 }
 
-hipError_t launch_place(int grid, hipStream_t stream, const TileRec* tiles, int64_t tile_lo,
-                        int64_t tile_hi, const ParamDev* params, uint16_t* const* ptrs,
-                        const uint32_t* flags, const uint16_t* shards, int64_t shard_stride,
-                        int64_t shard_elems) {
+hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
+                        const TileRec* tiles, int64_t tile_lo, int64_t tile_hi,
+                        const ParamDev* params, uint16_t* const* ptrs, const uint32_t* flags,
+                        const uint16_t* shards, int64_t shard_stride, int64_t shard_elems) {
     void* args[] = {&tiles, &tile_lo, &tile_hi, &params, &ptrs, &flags, &shards, &shard_stride,
                     &shard_elems};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&place_kernel), dim3(grid),
-                           dim3(kThreads), args, 0, stream);
+    const void* fn = threads == kFatThreads
+                         ? reinterpret_cast<const void*>(&place_kernel<kFatThreads>)
+                         : reinterpret_cast<const void*>(&place_kernel<kThreads>);
+    return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, lds, stream);
+}
+
+hipError_t allow_dynamic_lds(int L, size_t lds) {
+    // Dynamic LDS beyond the default per-workgroup limit needs opting in per kernel.
+    const void* fns[] = {reinterpret_cast<const void*>(&place_kernel<kFatThreads>),
+                         reinterpret_cast<const void*>(&place_kernel<kThreads>)};
+    for (const void* f : fns) {
+        hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+#define TIDE_LDS_CASE(n)                                                                      \
+    case n: {                                                                                 \
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&reduce_kernel<n, kFatThreads>), \
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+        if (e != hipSuccess) return e;                                                        \
+        return hipFuncSetAttribute(reinterpret_cast<const void*>(&reduce_kernel<n, kThreads>), \
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);     \
+    }
+    switch (L) {
+        TIDE_LDS_CASE(1)
+        TIDE_LDS_CASE(2)
+        TIDE_LDS_CASE(3)
+        TIDE_LDS_CASE(4)
+        TIDE_LDS_CASE(5)
+        TIDE_LDS_CASE(6)
+        TIDE_LDS_CASE(7)
+        TIDE_LDS_CASE(8)
+        TIDE_LDS_CASE(0)
+        default:
+            return allow_dynamic_lds(0, lds);
+    }
+#undef TIDE_LDS_CASE
 }
 
 }  // namespace tide

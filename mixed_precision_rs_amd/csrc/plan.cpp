@@ -49,10 +49,29 @@ tide_status hip_fail(hipError_t e, const char* what) {
 constexpr int kDefaultReduceBlocks = 16;
 constexpr int kDefaultPlaceBlocks = 4;
 constexpr int kDefaultMaxLaunchUs = 300;
-// Bytes one workgroup streams per microsecond when it has a CU to itself;
+// Budgeted launches use fat workgroups (kFatThreads) that reserve most of
+// their CU's LDS, so no other kernel's workgroup (a GEMM's, typically) shares
+// the CU with them: the concurrent kernel's workgroups are placed on the many
+// idle CUs instead of running beside a streaming workgroup.
+#ifndef TIDE_BUDGET_THREADS
+#define TIDE_BUDGET_THREADS kFatThreads
+#endif
+#ifndef TIDE_BUDGET_LDS
+#define TIDE_BUDGET_LDS (128 * 1024)
+#endif
+// Bytes one budgeted workgroup streams per microsecond with a CU to itself;
 // sizes the budgeted launches so a workgroup lives about max_launch_us.
-constexpr int64_t kWgBytesPerUs = 60000;
-constexpr int kFullGridCap = 1 << 30;
+#ifndef TIDE_WG_BYTES_PER_US
+#define TIDE_WG_BYTES_PER_US 100000
+#endif
+constexpr int kBudgetThreads = TIDE_BUDGET_THREADS;
+constexpr size_t kBudgetLds = TIDE_BUDGET_LDS;
+constexpr int64_t kWgBytesPerUs = TIDE_WG_BYTES_PER_US;
+// Full mode: at most this many workgroups per launch (they loop over tiles).
+#ifndef TIDE_FULL_GRID_CAP
+#define TIDE_FULL_GRID_CAP (1 << 30)
+#endif
+constexpr int kFullGridCap = TIDE_FULL_GRID_CAP;
 constexpr int kRingSlots = 8;
 
 struct TileTable {
@@ -79,8 +98,9 @@ struct DevState {
     char* ring_host = nullptr;
     Slot slots[kRingSlots];
     int next_slot = 0;
-    int last_slot = -1;
+    int last_slot = 0;
     std::vector<hipEvent_t> event_pool;
+    bool lds_allowed[65] = {};             // allow_dynamic_lds done for this L
 
     ~DevState() {
         int prev = -1;
@@ -180,7 +200,7 @@ int64_t budget_tiles_per_block(const tide_plan* plan, int op, const tide_launch&
 
 int64_t count_launches(const tide_plan* plan, int op, const tide_launch& l, int64_t ntiles) {
     if (ntiles == 0) return 0;
-    if (l.mode == TIDE_LAUNCH_FULL) return (ntiles + kFullGridCap - 1) / kFullGridCap;
+    if (l.mode == TIDE_LAUNCH_FULL) return 1;
     const int64_t blocks = op == 0 ? l.reduce_blocks : l.place_blocks;
     const int64_t per_launch = blocks * budget_tiles_per_block(plan, op, l);
     return (ntiles + per_launch - 1) / per_launch;
@@ -273,12 +293,15 @@ tide_status take_event(DevState* ds, hipEvent_t* ev) {
 // Reuses the previous slot, with no copy, when the table is unchanged.
 tide_status stage_table(DevState* ds, const void* bytes, size_t n, hipStream_t stream,
                         int* slot_out) {
-    if (ds->last_slot >= 0) {
-        Slot& s = ds->slots[ds->last_slot];
+    for (int i = 0; i < kRingSlots; ++i) {
+        // Most recent first: callers typically alternate a few fixed tables.
+        const int k = (ds->last_slot - i + 2 * kRingSlots) % kRingSlots;
+        Slot& s = ds->slots[k];
         if (s.loaded && s.used == n && std::memcmp(s.host, bytes, n) == 0) {
             if (s.upload_stream != stream)
                 TIDE_HIP_TRY(hipStreamWaitEvent(stream, s.upload_done, 0));
-            *slot_out = ds->last_slot;
+            ds->last_slot = k;
+            *slot_out = k;
             return TIDE_OK;
         }
     }
@@ -315,6 +338,16 @@ tide_status release_slot(DevState* ds, int slot, hipStream_t stream) {
     return TIDE_OK;
 }
 
+// Budgeted launches reserve dynamic LDS; opt the kernels in once per device.
+tide_status prepare_budget(DevState* ds, int L, const tide_launch& l) {
+    if (l.mode != TIDE_LAUNCH_BUDGETED || kBudgetLds == 0) return TIDE_OK;
+    const int key = L <= 8 ? L : 0;
+    if (ds->lds_allowed[key]) return TIDE_OK;
+    TIDE_HIP_TRY(allow_dynamic_lds(key, kBudgetLds));
+    ds->lds_allowed[key] = true;
+    return TIDE_OK;
+}
+
 struct Range {
     uintptr_t lo, hi;
     int who;
@@ -330,17 +363,19 @@ tide_status for_each_launch(const tide_plan* plan, int op, const tide_launch& l,
     int64_t per_launch;
     int grid_cap;
     if (l.mode == TIDE_LAUNCH_FULL) {
-        per_launch = kFullGridCap;
+        per_launch = ntiles;                  // one launch; workgroups loop over tiles
         grid_cap = kFullGridCap;
     } else {
         const int blocks = op == 0 ? l.reduce_blocks : l.place_blocks;
         per_launch = (int64_t)blocks * budget_tiles_per_block(plan, op, l);
         grid_cap = blocks;
     }
+    const int threads = l.mode == TIDE_LAUNCH_FULL ? kThreads : kBudgetThreads;
+    const size_t lds = l.mode == TIDE_LAUNCH_FULL ? 0 : kBudgetLds;
     for (int64_t lo = 0; lo < ntiles; lo += per_launch) {
         const int64_t hi = std::min(ntiles, lo + per_launch);
         const int grid = (int)std::min<int64_t>(grid_cap, hi - lo);
-        hipError_t e = launch(grid, lo, hi);
+        hipError_t e = launch(grid, threads, lds, lo, hi);
         if (e != hipSuccess) return hip_fail(e, op == 0 ? "reduce launch" : "place launch");
     }
     return TIDE_OK;
@@ -516,9 +551,12 @@ tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t*
         const uint16_t* const* dptrs = reinterpret_cast<const uint16_t* const*>(base);
         const uint32_t* dflags =
             reinterpret_cast<const uint32_t*>(base + (size_t)P * L * sizeof(void*));
-        st = for_each_launch(plan, 0, l, tt->count, [&](int grid, int64_t lo, int64_t hi) {
-            return launch_reduce(L, grid, stream, tt->dev, lo, hi, ds->params, dptrs, dflags, out,
-                                 out_stride);
+        st = prepare_budget(ds, L, l);
+        if (st != TIDE_OK) return st;
+        st = for_each_launch(plan, 0, l, tt->count,
+                             [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi) {
+            return launch_reduce(L, grid, threads, lds, stream, tt->dev, lo, hi, ds->params,
+                                 dptrs, dflags, out, out_stride);
         });
         tide_status st2 = release_slot(ds, slot, stream);
         return st != TIDE_OK ? st : st2;
@@ -621,9 +659,12 @@ tide_status tide_allgather_place(const tide_plan* plan, const uint16_t* shards,
         char* base = static_cast<char*>(ds->slots[slot].dev);
         uint16_t* const* dptrs = reinterpret_cast<uint16_t* const*>(base);
         const uint32_t* dflags = reinterpret_cast<const uint32_t*>(base + (size_t)P * sizeof(void*));
-        st = for_each_launch(plan, 1, l, tt->count, [&](int grid, int64_t lo, int64_t hi) {
-            return launch_place(grid, stream, tt->dev, lo, hi, ds->params, dptrs, dflags, shards,
-                                shard_stride, shard_elems);
+        st = prepare_budget(ds, plan->L, l);
+        if (st != TIDE_OK) return st;
+        st = for_each_launch(plan, 1, l, tt->count,
+                             [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi) {
+            return launch_place(grid, threads, lds, stream, tt->dev, lo, hi, ds->params, dptrs,
+                                dflags, shards, shard_stride, shard_elems);
         });
         tide_status st2 = release_slot(ds, slot, stream);
         return st != TIDE_OK ? st : st2;

@@ -7,15 +7,30 @@
 
 namespace tide {
 
-constexpr int kThreads = 256;              // workgroup size: 4 wave64s
+// Tuning knobs (overridable at build time for measurement sweeps).
+#ifndef TIDE_RS_UNROLL
+#define TIDE_RS_UNROLL 2
+#endif
+#ifndef TIDE_AG_UNROLL
+#define TIDE_AG_UNROLL 4
+#endif
+#ifndef TIDE_RS_TILE_STEPS
+#define TIDE_RS_TILE_STEPS 8
+#endif
+#ifndef TIDE_AG_TILE_STEPS
+#define TIDE_AG_TILE_STEPS 16
+#endif
+
+constexpr int kThreads = 256;              // workgroup size of the full grid: 4 wave64s
+constexpr int kFatThreads = 1024;          // workgroup size of budgeted launches: 16 wave64s
 constexpr int kVec = 8;                    // elements a thread handles per step (16 B of bf16)
 constexpr int kStep = kThreads * kVec;     // elements a workgroup handles per step
-constexpr int kRsUnroll = 2;               // steps whose loads a reduce thread keeps in flight
-constexpr int kAgUnroll = 4;               // same, placement
-constexpr int64_t kRsTile = 8 * kStep;     // elements per reduce tile (16384)
-constexpr int64_t kAgTile = 16 * kStep;    // elements per placement tile (32768)
-static_assert(kRsTile % (kRsUnroll * kStep) == 0, "tile must hold whole groups");
-static_assert(kAgTile % (kAgUnroll * kStep) == 0, "tile must hold whole groups");
+constexpr int kRsUnroll = TIDE_RS_UNROLL;  // steps whose loads a reduce thread keeps in flight
+constexpr int kAgUnroll = TIDE_AG_UNROLL;  // same, placement
+constexpr int64_t kRsTile = (int64_t)TIDE_RS_TILE_STEPS * kStep;   // elements per reduce tile
+constexpr int64_t kAgTile = (int64_t)TIDE_AG_TILE_STEPS * kStep;   // elements per placement tile
+static_assert(kRsTile % (kRsUnroll * kFatThreads * kVec) == 0, "tile must hold whole groups");
+static_assert(kAgTile % (kAgUnroll * kFatThreads * kVec) == 0, "tile must hold whole groups");
 
 // One unit of work: a run of up to one tile of flat element indices inside one
 // parameter. For the reduce, the flat index runs over the parameter's padded
@@ -43,15 +58,20 @@ static_assert(sizeof(ParamDev) == 32, "ParamDev layout");
 // Per-parameter flag bits of the per-call table.
 constexpr uint32_t kFlagVector = 1u;  // every pointer of this parameter allows 16-byte vector access
 
-// Launch wrappers (kernels.hip). Return the launch's hipError_t.
-hipError_t launch_reduce(int L, int grid, hipStream_t stream, const TileRec* tiles,
-                         int64_t tile_lo, int64_t tile_hi, const ParamDev* params,
-                         const uint16_t* const* ptrs, const uint32_t* flags, float* out,
-                         int64_t out_stride);
+// Launch wrappers (kernels.hip). threads is kThreads or kFatThreads; lds is
+// dynamic LDS reserved per workgroup (unused by the kernels: it only keeps
+// other kernels' workgroups off the CU). Return the launch's hipError_t.
+hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t stream,
+                         const TileRec* tiles, int64_t tile_lo, int64_t tile_hi,
+                         const ParamDev* params, const uint16_t* const* ptrs,
+                         const uint32_t* flags, float* out, int64_t out_stride);
 
-hipError_t launch_place(int grid, hipStream_t stream, const TileRec* tiles, int64_t tile_lo,
-                        int64_t tile_hi, const ParamDev* params, uint16_t* const* ptrs,
-                        const uint32_t* flags, const uint16_t* shards, int64_t shard_stride,
-                        int64_t shard_elems);
+hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
+                        const TileRec* tiles, int64_t tile_lo, int64_t tile_hi,
+                        const ParamDev* params, uint16_t* const* ptrs, const uint32_t* flags,
+                        const uint16_t* shards, int64_t shard_stride, int64_t shard_elems);
+
+// Allow `lds` bytes of dynamic LDS on every kernel variant for L contributors.
+hipError_t allow_dynamic_lds(int L, size_t lds);
 
 }  // namespace tide

@@ -8,6 +8,7 @@ shapes and re-derives the layout in C.
 """
 import ctypes
 import os
+import time
 from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -48,6 +49,7 @@ class Oracle:
             getattr(lib, f).restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
+        self.last_call_s = 0.0     # wall time of the last C compute call alone
 
     # -- helpers -------------------------------------------------------------
     @staticmethod
@@ -115,10 +117,12 @@ class Oracle:
                 for c in range(L) for p in range(P)]
         ptrs = (_U16P * max(len(arrs), 1))(*[self._p(a, _U16P) for a in arrs])
         counts = np.zeros(N * stride, np.uint32) if count_writes else None
+        t0 = time.perf_counter()
         rc = self.lib.oracle_reduce_scatter(
             P, self._p(rows, _I64P), self._p(rlen, _I64P), N, L, ptrs,
             self._p(out, _F32P), stride, rb, re,
             self._p(counts, _U32P) if counts is not None else None)
+        self.last_call_s = time.perf_counter() - t0
         if rc != 0:
             raise ValueError("oracle_reduce_scatter rejected its arguments")
         out2 = out.reshape(N, stride) if stride > 0 else out.reshape(N, 0)
@@ -156,9 +160,11 @@ class Oracle:
         pp = (_U16P * max(P, 1))(*[self._p(a, _U16P) for a in params])
         counts = [np.zeros(t * k, np.uint32) for t, k in shapes] if count_writes else None
         cp = (_U32P * max(P, 1))(*[self._p(a, _U32P) for a in counts]) if counts else None
+        t0 = time.perf_counter()
         rc = self.lib.oracle_allgather_place(
             P, self._p(rows, _I64P), self._p(rlen, _I64P), N, self._p(shards, _U16P),
             stride, pp, rb, re, cp)
+        self.last_call_s = time.perf_counter() - t0
         if rc != 0:
             raise ValueError("oracle_allgather_place rejected its arguments")
         if count_writes:
