@@ -64,11 +64,18 @@ __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float widen(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// A tile as the kernels use it: its first index, that index's rank and
+// in-piece offset, and the index bounds [lo, hi) of the launch's rank range.
+struct Span {
+    int64_t idx0, j0, lo, hi;
+    int64_t r0;
+};
+
 // Rank r and offset j inside rank r's piece of flat index f of tile t, for
 // idx0 <= f < idx0 + tile. Since j0 < s, j < s + tile: one subtraction does
 // when s >= tile, and a 32-bit division otherwise.
 template <int64_t kTile>
-__device__ __forceinline__ void locate(const TileRec& t, int64_t s, int64_t f, int64_t& r,
+__device__ __forceinline__ void locate(const Span& t, int64_t s, int64_t f, int64_t& r,
                                        int64_t& j) {
     j = t.j0 + (f - t.idx0);
     r = t.r0;
@@ -93,7 +100,7 @@ __device__ __forceinline__ void step(int64_t s, int64_t& r, int64_t& j) {
 }
 
 // Write 8 fp32 results for flat indices f..f+7 (all inside the tile's range).
-__device__ __forceinline__ void store8(const TileRec& t, const ParamDev& pd, int64_t f,
+__device__ __forceinline__ void store8(const Span& t, const ParamDev& pd, int64_t f,
                                        const float (&a)[kVec], float* __restrict__ out,
                                        int64_t stride) {
     int64_t r, j;
@@ -116,22 +123,30 @@ __device__ __forceinline__ void store8(const TileRec& t, const ParamDev& pd, int
 
 // Reduce: out[rank piece] = fold_c widen(g[c][f]) for f < valid, +0 past it.
 // LT > 0: L known at compile time (fully unrolled); LT == 0: runtime L.
+// A workgroup of NT threads is NT / kThreads independent quarters of kThreads
+// threads; each quarter walks its own tiles (no barrier between quarters).
 template <int LT, int NT>
 __global__ __launch_bounds__(NT) void reduce_kernel(
-    const TileRec* __restrict__ tiles, int64_t tile_lo, int64_t tile_hi,
+    const TileRec* __restrict__ tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb, int32_t re,
     const ParamDev* __restrict__ params, const uint16_t* const* __restrict__ ptrs,
     const uint32_t* __restrict__ flags, int Lrt, float* __restrict__ out, int64_t out_stride) {
+    constexpr int kSubs = NT / kThreads;
     const int L = LT > 0 ? LT : Lrt;
-    for (int64_t t = tile_lo + blockIdx.x; t < tile_hi; t += gridDim.x) {
-        const TileRec tr = tiles[t];
-        const ParamDev pd = params[tr.p];
-        const uint16_t* const* g = ptrs + (int64_t)tr.p * L;
-        const bool vec = (flags[tr.p] & kFlagVector) != 0;
+    const int sub = (int)threadIdx.x / kThreads;          // wave-uniform
+    const int tid = (int)threadIdx.x % kThreads;
+    for (int64_t t = tile_lo + (int64_t)blockIdx.x * kSubs + sub; t < tile_hi;
+         t += (int64_t)gridDim.x * kSubs) {
+        const TileRec rec = tiles[t];
+        const ParamDev pd = params[rec.p];
+        const uint16_t* const* g = ptrs + (int64_t)rec.p * L;
+        const bool vec = (flags[rec.p] & kFlagVector) != 0;
+        const Span tr{rec.idx0, rec.idx0 - (int64_t)rec.r0 * pd.s, (int64_t)rb * pd.s,
+                      (int64_t)re * pd.s, rec.r0};
         const int64_t end = min(tr.idx0 + kRsTile, tr.hi);
-        for (int64_t g0 = tr.idx0; g0 < end; g0 += kRsUnroll * (NT * kVec)) {
-            const int64_t g1 = g0 + kRsUnroll * (NT * kVec);
+        for (int64_t g0 = tr.idx0; g0 < end; g0 += kRsUnroll * kStep) {
+            const int64_t g1 = g0 + kRsUnroll * kStep;
             const bool interior = vec && g0 >= tr.lo && g1 <= end;
-            const int64_t f0 = g0 + (int64_t)threadIdx.x * kVec;
+            const int64_t f0 = g0 + (int64_t)tid * kVec;
             if (interior && g1 <= pd.valid) {
                 // All L * kRsUnroll loads are independent of the adds, so they
                 // are all issued before the first add waits.
@@ -143,7 +158,7 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
                     u32x4 v[kRsUnroll];
 #pragma unroll
                     for (int u = 0; u < kRsUnroll; ++u)
-                        v[u] = TIDE_LD(gc + u * ((NT * kVec) / kVec));
+                        v[u] = TIDE_LD(gc + u * (kStep / kVec));
 #pragma unroll
                     for (int u = 0; u < kRsUnroll; ++u) {
 #pragma unroll
@@ -160,19 +175,19 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
                 }
 #pragma unroll
                 for (int u = 0; u < kRsUnroll; ++u)
-                    store8(tr, pd, f0 + (int64_t)u * (NT * kVec), a[u], out, out_stride);
+                    store8(tr, pd, f0 + (int64_t)u * kStep, a[u], out, out_stride);
             } else if (interior && g0 >= pd.valid) {
                 float z[kVec];
 #pragma unroll
                 for (int e = 0; e < kVec; ++e) z[e] = 0.0f;
 #pragma unroll
                 for (int u = 0; u < kRsUnroll; ++u)
-                    store8(tr, pd, f0 + (int64_t)u * (NT * kVec), z, out, out_stride);
+                    store8(tr, pd, f0 + (int64_t)u * kStep, z, out, out_stride);
             } else {
                 // Ragged edge: element by element, exact bounds.
 #pragma unroll 1
                 for (int u = 0; u < kRsUnroll; ++u) {
-                    const int64_t fu = f0 + (int64_t)u * (NT * kVec);
+                    const int64_t fu = f0 + (int64_t)u * kStep;
                     int64_t r, j;
                     locate<kRsTile>(tr, pd.s, fu, r, j);
 #pragma unroll 1
@@ -194,7 +209,7 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
 }
 
 // 8 bf16 of the rank-major shards for flat parameter indices f..f+7.
-__device__ __forceinline__ u32x4 gather8(const TileRec& t, const ParamDev& pd, int64_t f,
+__device__ __forceinline__ u32x4 gather8(const Span& t, const ParamDev& pd, int64_t f,
                                          const uint16_t* __restrict__ shards, int64_t stride,
                                          int64_t shard_elems) {
     int64_t r, j;
@@ -234,33 +249,39 @@ __device__ __forceinline__ u32x4 gather8(const TileRec& t, const ParamDev& pd, i
 // Placement: param[f] = shards[rank(f) * stride + o_p + offset(f)] for true f.
 template <int NT>
 __global__ __launch_bounds__(NT) void place_kernel(
-    const TileRec* __restrict__ tiles, int64_t tile_lo, int64_t tile_hi,
+    const TileRec* __restrict__ tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb, int32_t re,
     const ParamDev* __restrict__ params, uint16_t* const* __restrict__ ptrs,
     const uint32_t* __restrict__ flags, const uint16_t* __restrict__ shards, int64_t stride,
     int64_t shard_elems) {
-    for (int64_t t = tile_lo + blockIdx.x; t < tile_hi; t += gridDim.x) {
-        const TileRec tr = tiles[t];
-        const ParamDev pd = params[tr.p];
-        uint16_t* dst = ptrs[tr.p];
-        const bool vec = (flags[tr.p] & kFlagVector) != 0;
+    constexpr int kSubs = NT / kThreads;
+    const int sub = (int)threadIdx.x / kThreads;
+    const int tid = (int)threadIdx.x % kThreads;
+    for (int64_t t = tile_lo + (int64_t)blockIdx.x * kSubs + sub; t < tile_hi;
+         t += (int64_t)gridDim.x * kSubs) {
+        const TileRec rec = tiles[t];
+        const ParamDev pd = params[rec.p];
+        uint16_t* dst = ptrs[rec.p];
+        const bool vec = (flags[rec.p] & kFlagVector) != 0;
+        const Span tr{rec.idx0, rec.idx0 - (int64_t)rec.r0 * pd.s, (int64_t)rb * pd.s,
+                      min((int64_t)re * pd.s, pd.valid), rec.r0};
         const int64_t end = min(tr.idx0 + kAgTile, tr.hi);
-        for (int64_t g0 = tr.idx0; g0 < end; g0 += kAgUnroll * (NT * kVec)) {
-            const int64_t g1 = g0 + kAgUnroll * (NT * kVec);
-            const int64_t f0 = g0 + (int64_t)threadIdx.x * kVec;
+        for (int64_t g0 = tr.idx0; g0 < end; g0 += kAgUnroll * kStep) {
+            const int64_t g1 = g0 + kAgUnroll * kStep;
+            const int64_t f0 = g0 + (int64_t)tid * kVec;
             if (vec && g0 >= tr.lo && g1 <= end) {
                 u32x4 w[kAgUnroll];
 #pragma unroll
                 for (int u = 0; u < kAgUnroll; ++u)
-                    w[u] = gather8(tr, pd, f0 + (int64_t)u * (NT * kVec), shards, stride, shard_elems);
+                    w[u] = gather8(tr, pd, f0 + (int64_t)u * kStep, shards, stride, shard_elems);
                 TIDE_GLOBAL u32x4* d4 = gbl_mut<u32x4>(dst + f0);
 #pragma unroll
                 for (int u = 0; u < kAgUnroll; ++u)
-                    TIDE_ST(w[u], d4 + u * ((NT * kVec) / kVec));
+                    TIDE_ST(w[u], d4 + u * (kStep / kVec));
             } else {
                 TIDE_GLOBAL uint16_t* d = gbl_mut<uint16_t>(dst);
 #pragma unroll 1
                 for (int u = 0; u < kAgUnroll; ++u) {
-                    const int64_t fu = f0 + (int64_t)u * (NT * kVec);
+                    const int64_t fu = f0 + (int64_t)u * kStep;
                     int64_t r, j;
                     locate<kAgTile>(tr, pd.s, fu, r, j);
 #pragma unroll 1
@@ -277,10 +298,11 @@ __global__ __launch_bounds__(NT) void place_kernel(
 
 template <int LT>
 hipError_t launch_reduce_t(int L, int grid, int threads, size_t lds, hipStream_t stream,
-                           const TileRec* tiles, int64_t tile_lo, int64_t tile_hi,
-                           const ParamDev* params, const uint16_t* const* ptrs,
+                           const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
+                           int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
                            const uint32_t* flags, float* out, int64_t out_stride) {
-    void* args[] = {&tiles, &tile_lo, &tile_hi, &params, &ptrs, &flags, &L, &out, &out_stride};
+    void* args[] = {&tiles, &tile_lo, &tile_hi, &rb, &re, &params, &ptrs, &flags, &L, &out,
+                    &out_stride};
     const void* fn = threads == kFatThreads
                          ? reinterpret_cast<const void*>(&reduce_kernel<LT, kFatThreads>)
                          : reinterpret_cast<const void*>(&reduce_kernel<LT, kThreads>);
@@ -290,13 +312,13 @@ hipError_t launch_reduce_t(int L, int grid, int threads, size_t lds, hipStream_t
 }  // namespace
 
 hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t stream,
-                         const TileRec* tiles, int64_t tile_lo, int64_t tile_hi,
-                         const ParamDev* params, const uint16_t* const* ptrs,
+                         const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
+                         int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
                          const uint32_t* flags, float* out, int64_t out_stride) {
 #define TIDE_REDUCE_CASE(n)                                                                   \
     case n:                                                                                   \
-        return launch_reduce_t<n>(L, grid, threads, lds, stream, tiles, tile_lo, tile_hi,    \
-                                  params, ptrs, flags, out, out_stride);
+        return launch_reduce_t<n>(L, grid, threads, lds, stream, tiles, tile_lo, tile_hi, rb, \
+                                  re, params, ptrs, flags, out, out_stride);
     switch (L) {
         TIDE_REDUCE_CASE(1)
         TIDE_REDUCE_CASE(2)
@@ -307,18 +329,19 @@ hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t s
         TIDE_REDUCE_CASE(7)
         TIDE_REDUCE_CASE(8)
         default:
-            return launch_reduce_t<0>(L, grid, threads, lds, stream, tiles, tile_lo, tile_hi,
-                                      params, ptrs, flags, out, out_stride);
+            return launch_reduce_t<0>(L, grid, threads, lds, stream, tiles, tile_lo, tile_hi, rb,
+                                      re, params, ptrs, flags, out, out_stride);
     }
 #undef TIDE_REDUCE_CASE
 }
 
 hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
-                        const TileRec* tiles, int64_t tile_lo, int64_t tile_hi,
-                        const ParamDev* params, uint16_t* const* ptrs, const uint32_t* flags,
-                        const uint16_t* shards, int64_t shard_stride, int64_t shard_elems) {
-    void* args[] = {&tiles, &tile_lo, &tile_hi, &params, &ptrs, &flags, &shards, &shard_stride,
-                    &shard_elems};
+                        const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
+                        int32_t re, const ParamDev* params, uint16_t* const* ptrs,
+                        const uint32_t* flags, const uint16_t* shards, int64_t shard_stride,
+                        int64_t shard_elems) {
+    void* args[] = {&tiles, &tile_lo, &tile_hi, &rb, &re, &params, &ptrs, &flags, &shards,
+                    &shard_stride, &shard_elems};
     const void* fn = threads == kFatThreads
                          ? reinterpret_cast<const void*>(&place_kernel<kFatThreads>)
                          : reinterpret_cast<const void*>(&place_kernel<kThreads>);

@@ -72,6 +72,9 @@ constexpr int64_t kWgBytesPerUs = TIDE_WG_BYTES_PER_US;
 #define TIDE_FULL_GRID_CAP (1 << 30)
 #endif
 constexpr int kFullGridCap = TIDE_FULL_GRID_CAP;
+#ifndef TIDE_TILE_ORDER_RANK_MAJOR
+#define TIDE_TILE_ORDER_RANK_MAJOR 0
+#endif
 constexpr int kRingSlots = 8;
 
 struct TileTable {
@@ -177,14 +180,17 @@ std::vector<TileRec> build_tiles(const tide_plan* plan, int op, int rb, int re) 
         for (int64_t a = lo - lo % kVec; a < hi; a += tile) {
             TileRec t{};
             t.idx0 = a;
-            t.r0 = (int32_t)(a / q.s);
-            t.j0 = a - (int64_t)t.r0 * q.s;
-            t.lo = lo;
-            t.hi = hi;
             t.p = p;
+            t.r0 = (int32_t)(a / q.s);
             out.push_back(t);
         }
     }
+#if TIDE_TILE_ORDER_RANK_MAJOR
+    // The same tiles (a partition of the index space) walked rank by rank.
+    std::stable_sort(out.begin(), out.end(), [](const TileRec& a, const TileRec& b) {
+        return a.r0 != b.r0 ? a.r0 < b.r0 : a.p < b.p;
+    });
+#endif
     return out;
 }
 
@@ -555,8 +561,8 @@ tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t*
         if (st != TIDE_OK) return st;
         st = for_each_launch(plan, 0, l, tt->count,
                              [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi) {
-            return launch_reduce(L, grid, threads, lds, stream, tt->dev, lo, hi, ds->params,
-                                 dptrs, dflags, out, out_stride);
+            return launch_reduce(L, grid, threads, lds, stream, tt->dev, lo, hi, l.rank_begin,
+                                 l.rank_end, ds->params, dptrs, dflags, out, out_stride);
         });
         tide_status st2 = release_slot(ds, slot, stream);
         return st != TIDE_OK ? st : st2;
@@ -663,8 +669,9 @@ tide_status tide_allgather_place(const tide_plan* plan, const uint16_t* shards,
         if (st != TIDE_OK) return st;
         st = for_each_launch(plan, 1, l, tt->count,
                              [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi) {
-            return launch_place(grid, threads, lds, stream, tt->dev, lo, hi, ds->params, dptrs,
-                                dflags, shards, shard_stride, shard_elems);
+            return launch_place(grid, threads, lds, stream, tt->dev, lo, hi, l.rank_begin,
+                                l.rank_end, ds->params, dptrs, dflags, shards, shard_stride,
+                                shard_elems);
         });
         tide_status st2 = release_slot(ds, slot, stream);
         return st != TIDE_OK ? st : st2;

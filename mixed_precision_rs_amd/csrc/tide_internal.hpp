@@ -7,45 +7,51 @@
 
 namespace tide {
 
-// Tuning knobs (overridable at build time for measurement sweeps).
+// Tuning knobs (overridable at build time for measurement sweeps). Defaults
+// were picked by interleaved in-process timing on MI355X over the four large
+// workloads: many small, short workgroups stream best (a workgroup covers
+// 1024 elements of the reduce, 2048 of the placement).
+#ifndef TIDE_THREADS
+#define TIDE_THREADS 128
+#endif
 #ifndef TIDE_RS_UNROLL
-#define TIDE_RS_UNROLL 2
+#define TIDE_RS_UNROLL 1
 #endif
 #ifndef TIDE_AG_UNROLL
-#define TIDE_AG_UNROLL 4
+#define TIDE_AG_UNROLL 2
 #endif
 #ifndef TIDE_RS_TILE_STEPS
-#define TIDE_RS_TILE_STEPS 8
+#define TIDE_RS_TILE_STEPS 1
 #endif
 #ifndef TIDE_AG_TILE_STEPS
-#define TIDE_AG_TILE_STEPS 16
+#define TIDE_AG_TILE_STEPS 2
 #endif
 
-constexpr int kThreads = 256;              // workgroup size of the full grid: 4 wave64s
-constexpr int kFatThreads = 1024;          // workgroup size of budgeted launches: 16 wave64s
+constexpr int kThreads = TIDE_THREADS;     // workgroup size of the full grid (wave64s x 64)
+constexpr int kFatThreads = 1024;          // workgroup size of budgeted launches: 16 wave64s,
+                                           // 4 independent quarters of kThreads
 constexpr int kVec = 8;                    // elements a thread handles per step (16 B of bf16)
 constexpr int kStep = kThreads * kVec;     // elements a workgroup handles per step
 constexpr int kRsUnroll = TIDE_RS_UNROLL;  // steps whose loads a reduce thread keeps in flight
 constexpr int kAgUnroll = TIDE_AG_UNROLL;  // same, placement
 constexpr int64_t kRsTile = (int64_t)TIDE_RS_TILE_STEPS * kStep;   // elements per reduce tile
 constexpr int64_t kAgTile = (int64_t)TIDE_AG_TILE_STEPS * kStep;   // elements per placement tile
-static_assert(kRsTile % (kRsUnroll * kFatThreads * kVec) == 0, "tile must hold whole groups");
-static_assert(kAgTile % (kAgUnroll * kFatThreads * kVec) == 0, "tile must hold whole groups");
+static_assert(kRsTile % (kRsUnroll * kStep) == 0, "tile must hold whole groups");
+static_assert(kAgTile % (kAgUnroll * kStep) == 0, "tile must hold whole groups");
+static_assert(kFatThreads % kThreads == 0, "a fat workgroup is whole quarters");
 
 // One unit of work: a run of up to one tile of flat element indices inside one
 // parameter. For the reduce, the flat index runs over the parameter's padded
 // storage [0, N * s_p) (index f is rank f / s_p, offset f % s_p of its piece);
-// for the placement, over its true elements [0, T_p * K_p).
+// for the placement, over its true elements [0, T_p * K_p). A launch over
+// ranks [rb, re) only touches indices in [rb * s_p, re * s_p) (placement: also
+// below T_p * K_p); the kernel derives those bounds from the parameter.
 struct TileRec {
     int64_t idx0;   // first index of the tile, a multiple of kVec
-    int64_t j0;     // idx0 - r0 * s_p
-    int64_t lo;     // the tile only touches indices in [lo, hi)
-    int64_t hi;
     int32_t p;      // parameter
-    int32_t r0;     // rank that holds idx0
-    int32_t pad0, pad1;
+    int32_t r0;     // rank that holds idx0 (idx0 / s_p)
 };
-static_assert(sizeof(TileRec) == 48, "TileRec layout");
+static_assert(sizeof(TileRec) == 16, "TileRec layout");
 
 struct ParamDev {
     int64_t s;      // s_p, elements per rank piece
@@ -62,14 +68,15 @@ constexpr uint32_t kFlagVector = 1u;  // every pointer of this parameter allows 
 // dynamic LDS reserved per workgroup (unused by the kernels: it only keeps
 // other kernels' workgroups off the CU). Return the launch's hipError_t.
 hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t stream,
-                         const TileRec* tiles, int64_t tile_lo, int64_t tile_hi,
-                         const ParamDev* params, const uint16_t* const* ptrs,
+                         const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
+                         int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
                          const uint32_t* flags, float* out, int64_t out_stride);
 
 hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
-                        const TileRec* tiles, int64_t tile_lo, int64_t tile_hi,
-                        const ParamDev* params, uint16_t* const* ptrs, const uint32_t* flags,
-                        const uint16_t* shards, int64_t shard_stride, int64_t shard_elems);
+                        const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
+                        int32_t re, const ParamDev* params, uint16_t* const* ptrs,
+                        const uint32_t* flags, const uint16_t* shards, int64_t shard_stride,
+                        int64_t shard_elems);
 
 // Allow `lds` bytes of dynamic LDS on every kernel variant for L contributors.
 hipError_t allow_dynamic_lds(int L, size_t lds);
