@@ -67,9 +67,10 @@ def group_bytes(cfg, S):
     return rs, ag, valid
 
 
-def cpu_baseline(orc, cfg, plan, grads, shards, out, ranks):
+def cpu_baseline(orc, cfg, plan, grads, shards, out, ranks, reps=3):
     """Time the CPU oracle (one thread) on ranks [0, ranks) of the same group,
-    with the same bits copied from the GPU; check the GPU's shards there."""
+    with the same bits copied from the GPU (median of `reps` runs of each leg);
+    check the GPU's shards there."""
     import numpy as np
     import torch
     N, L, S = cfg.N, cfg.L, plan.S
@@ -85,16 +86,22 @@ def cpu_baseline(orc, cfg, plan, grads, shards, out, ranks):
                 valid += nrows * k
         h_grads.append(row)
     h_out = np.empty(N * S, np.float32)
-    orc.reduce_scatter(cfg.shapes, N, L, h_grads, rank_range=(0, ranks), out=h_out)
-    t_rs = orc.last_call_s
+    t = []
+    for _ in range(reps):
+        orc.reduce_scatter(cfg.shapes, N, L, h_grads, rank_range=(0, ranks), out=h_out)
+        t.append(orc.last_call_s)
+    t_rs = statistics.median(t)
     gpu_part = out[: ranks * S].cpu().numpy()
     exact = bool(np.array_equal(gpu_part.view(np.uint32), h_out[: ranks * S].view(np.uint32)))
     h_sh = np.zeros(N * S, np.uint16)
     h_sh[: ranks * S] = shards[: ranks * S].view(torch.int16).cpu().numpy().view(np.uint16)
     h_params = [np.zeros(min(t, ranks * int(lay["R"][p])) * k, np.uint16)
                 for p, (t, k) in enumerate(cfg.shapes)]
-    orc.allgather_place(cfg.shapes, N, h_sh, rank_range=(0, ranks), params=h_params)
-    t_ag = orc.last_call_s
+    t = []
+    for _ in range(reps):
+        orc.allgather_place(cfg.shapes, N, h_sh, rank_range=(0, ranks), params=h_params)
+        t.append(orc.last_call_s)
+    t_ag = statistics.median(t)
     nbytes = 2 * L * valid + 4 * ranks * S + 4 * valid
     return {
         "value": round(nbytes / (t_rs + t_ag) / 1e9, 4),
@@ -102,8 +109,8 @@ def cpu_baseline(orc, cfg, plan, grads, shards, out, ranks):
         "cores": 1,
         "kind": "oracle",
         "sample": "ranks 0-%d of %d of the same group (all %d params), reduce-scatter + "
-                  "placement, same bits copied from the GPU; %.1f s reduce + %.1f s placement "
-                  "on one core" % (ranks - 1, N, len(cfg.shapes), t_rs, t_ag),
+                  "placement, same bits copied from the GPU; median of %d runs: %.2f s reduce + "
+                  "%.2f s placement on one core" % (ranks - 1, N, len(cfg.shapes), reps, t_rs, t_ag),
         "gpu_shards_bit_exact_on_sample": exact,
     }
 
@@ -202,7 +209,7 @@ def main():
     ap.add_argument("--victim", action="store_true",
                     help="GEMM-victim slowdown, budgeted and full grid")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-ranks", type=int, default=24)
+    ap.add_argument("--cpu-ranks", type=int, default=0, help="ranks in the CPU sample (0: all)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -299,8 +306,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        log("bench: CPU oracle baseline on ranks 0-%d" % (args.cpu_ranks - 1))
-        cpu = cpu_baseline(oracle.load(), cfg, plan, grads, shards, out, args.cpu_ranks)
+        ranks = args.cpu_ranks if args.cpu_ranks > 0 else cfg.N
+        log("bench: CPU oracle baseline on ranks 0-%d" % (ranks - 1))
+        cpu = cpu_baseline(oracle.load(), cfg, plan, grads, shards, out, ranks)
         log("bench: cpu %s" % json.dumps(cpu))
 
     traffic = counter_traffic(cfg.name)

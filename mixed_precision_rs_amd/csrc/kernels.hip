@@ -25,6 +25,7 @@ namespace tide {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
@@ -99,6 +100,18 @@ __device__ __forceinline__ void step(int64_t s, int64_t& r, int64_t& j) {
     }
 }
 
+// Lane layout of a reduce step. With TIDE_RS_SPLIT_STORE, a wave's 512
+// elements are two runs of 256: lane l owns elements 4l..4l+3 of each run, so
+// each wave-wide 16-byte store writes 1 KiB of fp32 with no gaps (whole cache
+// lines) and each 8-byte load reads 512 contiguous bf16 bytes. Without it,
+// lane l owns elements 8l..8l+7 (16-byte loads, two gapped stores).
+#ifndef TIDE_RS_SPLIT_STORE
+#define TIDE_RS_SPLIT_STORE 1
+#endif
+constexpr int kWave = 64;
+constexpr int kHalf = kWave * 4;           // elements of one run
+
+#if !TIDE_RS_SPLIT_STORE
 // Write 8 fp32 results for flat indices f..f+7 (all inside the tile's range).
 __device__ __forceinline__ void store8(const Span& t, const ParamDev& pd, int64_t f,
                                        const float (&a)[kVec], float* __restrict__ out,
@@ -115,6 +128,25 @@ __device__ __forceinline__ void store8(const Span& t, const ParamDev& pd, int64_
         // The 8 elements straddle two or more ranks' pieces.
 #pragma unroll 1
         for (int e = 0; e < kVec; ++e) {
+            out[r * stride + pd.o + j] = a[e];
+            step(pd.s, r, j);
+        }
+    }
+}
+#endif
+
+// Write 4 fp32 results for flat indices f..f+3 (all inside the tile's range).
+__device__ __forceinline__ void store4(const Span& t, const ParamDev& pd, int64_t f,
+                                       const float (&a)[4], float* __restrict__ out,
+                                       int64_t stride) {
+    int64_t r, j;
+    locate<kRsTile>(t, pd.s, f, r, j);
+    if (j + 4 <= pd.s) {
+        const f32x4_a4 x = {a[0], a[1], a[2], a[3]};
+        TIDE_ST(x, reinterpret_cast<f32x4_a4*>(out + r * stride + pd.o + j));
+    } else {
+#pragma unroll 1
+        for (int e = 0; e < 4; ++e) {
             out[r * stride + pd.o + j] = a[e];
             step(pd.s, r, j);
         }
@@ -147,6 +179,54 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
             const int64_t g1 = g0 + kRsUnroll * kStep;
             const bool interior = vec && g0 >= tr.lo && g1 <= end;
             const int64_t f0 = g0 + (int64_t)tid * kVec;
+#if TIDE_RS_SPLIT_STORE
+            const int64_t fh = g0 + (int64_t)(tid / kWave) * (2 * kHalf) + (tid % kWave) * 4;
+            if (interior && g1 <= pd.valid) {
+                // All loads are independent of the adds: they are all issued
+                // before the first add waits.
+                float a[kRsUnroll][2][4];
+                constexpr int kCUnroll = LT > 0 ? LT : 1;
+#pragma unroll kCUnroll
+                for (int c = 0; c < L; ++c) {
+                    const TIDE_GLOBAL u32x2* gc = gbl<u32x2>(g[c] + fh);
+                    u32x2 v[kRsUnroll][2];
+#pragma unroll
+                    for (int u = 0; u < kRsUnroll; ++u)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+                            v[u][h] = TIDE_LD(gc + (u * kStep + h * kHalf) / 4);
+#pragma unroll
+                    for (int u = 0; u < kRsUnroll; ++u) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                            for (int m = 0; m < 2; ++m) {
+                                if (c == 0) {
+                                    a[u][h][2 * m] = lo_bf16(v[u][h][m]);
+                                    a[u][h][2 * m + 1] = hi_bf16(v[u][h][m]);
+                                } else {
+                                    a[u][h][2 * m] = a[u][h][2 * m] + lo_bf16(v[u][h][m]);
+                                    a[u][h][2 * m + 1] = a[u][h][2 * m + 1] + hi_bf16(v[u][h][m]);
+                                }
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kRsUnroll; ++u)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        store4(tr, pd, fh + (int64_t)u * kStep + h * kHalf, a[u][h], out,
+                               out_stride);
+            } else if (interior && g0 >= pd.valid) {
+                const float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int u = 0; u < kRsUnroll; ++u)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+                        store4(tr, pd, fh + (int64_t)u * kStep + h * kHalf, z, out, out_stride);
+            } else
+#else
             if (interior && g1 <= pd.valid) {
                 // All L * kRsUnroll loads are independent of the adds, so they
                 // are all issued before the first add waits.
@@ -183,7 +263,9 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
 #pragma unroll
                 for (int u = 0; u < kRsUnroll; ++u)
                     store8(tr, pd, f0 + (int64_t)u * kStep, z, out, out_stride);
-            } else {
+            } else
+#endif
+            {
                 // Ragged edge: element by element, exact bounds.
 #pragma unroll 1
                 for (int u = 0; u < kRsUnroll; ++u) {
