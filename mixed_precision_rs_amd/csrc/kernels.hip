@@ -153,6 +153,51 @@ __device__ __forceinline__ void store4(const Span& t, const ParamDev& pd, int64_
     }
 }
 
+// XCD-aware tile order for the full grid. The dispatcher sends workgroup i
+// to XCD i mod kXcds, and each XCD has its own L2. With a chunk C > 0,
+// workgroup i takes tile (chunk * kXcds + xcd) * C + within, so every XCD
+// walks runs of C consecutive tiles and a cache line shared by two
+// neighbouring tiles goes through one L2 rather than two. The mapping is a
+// bijection on the first multiple of kXcds * C tiles and the identity on the
+// rest. Measured on MI355X: +2% for the placement (whose bf16 source runs
+// start at arbitrary 2-byte offsets), -2% for the reduce, so only the
+// placement uses it.
+#ifndef TIDE_XCD_CHUNK_RS
+#define TIDE_XCD_CHUNK_RS 0
+#endif
+#ifndef TIDE_XCD_CHUNK_AG
+#define TIDE_XCD_CHUNK_AG 64
+#endif
+constexpr int64_t kXcds = 8;
+template <int64_t C>
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t n) {
+    if (C <= 0) return b;
+    const int64_t full = n / (kXcds * C) * (kXcds * C);
+    if (b >= full) return b;
+    const int64_t xcd = b % kXcds, j = b / kXcds;
+    return ((j / C) * kXcds + xcd) * C + j % C;
+}
+
+// Write one wave's run of kHalf fp32 results: lane l holds a[0..3] for flat
+// indices f_run + 4l .. f_run + 4l + 3. A run inside one rank's piece has a
+// contiguous destination (one wave-wide 16-byte store, 1 KiB); a run that
+// crosses into the next rank's piece goes lane by lane. Runs that start
+// mid-line (prefix offsets that are not multiples of 4 elements) cost about
+// 3.5% of bandwidth; neither realigning them across lanes nor plain
+// write-back stores recovered it on MI355X.
+__device__ __forceinline__ void store_run(const Span& t, const ParamDev& pd, int64_t f_run,
+                                          int lane, const float (&a)[4],
+                                          float* __restrict__ out, int64_t stride) {
+    int64_t r, j;
+    locate<kRsTile>(t, pd.s, f_run, r, j);
+    if (j + kHalf > pd.s) {                   // the run crosses into the next rank's piece
+        store4(t, pd, f_run + 4 * lane, a, out, stride);
+        return;
+    }
+    const f32x4_a4 x = {a[0], a[1], a[2], a[3]};
+    TIDE_ST(x, reinterpret_cast<f32x4_a4*>(out + r * stride + pd.o + j + 4 * lane));
+}
+
 // Reduce: out[rank piece] = fold_c widen(g[c][f]) for f < valid, +0 past it.
 // LT > 0: L known at compile time (fully unrolled); LT == 0: runtime L.
 // A workgroup of NT threads is NT / kThreads independent quarters of kThreads
@@ -166,9 +211,13 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
     const int L = LT > 0 ? LT : Lrt;
     const int sub = (int)threadIdx.x / kThreads;          // wave-uniform
     const int tid = (int)threadIdx.x % kThreads;
+    // One tile per workgroup (the full grid): XCD-aware order.
+    const bool one_each = kSubs == 1 && (int64_t)gridDim.x == tile_hi - tile_lo;
     for (int64_t t = tile_lo + (int64_t)blockIdx.x * kSubs + sub; t < tile_hi;
          t += (int64_t)gridDim.x * kSubs) {
-        const TileRec rec = tiles[t];
+        const TileRec rec =
+            tiles[one_each ? tile_lo + xcd_tile<TIDE_XCD_CHUNK_RS>(t - tile_lo, tile_hi - tile_lo)
+                           : t];
         const ParamDev pd = params[rec.p];
         const uint16_t* const* g = ptrs + (int64_t)rec.p * L;
         const bool vec = (flags[rec.p] & kFlagVector) != 0;
@@ -180,7 +229,9 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
             const bool interior = vec && g0 >= tr.lo && g1 <= end;
             const int64_t f0 = g0 + (int64_t)tid * kVec;
 #if TIDE_RS_SPLIT_STORE
-            const int64_t fh = g0 + (int64_t)(tid / kWave) * (2 * kHalf) + (tid % kWave) * 4;
+            const int lane = tid % kWave;
+            const int64_t fw = g0 + (int64_t)(tid / kWave) * (2 * kHalf);   // wave's first index
+            const int64_t fh = fw + lane * 4;
             if (interior && g1 <= pd.valid) {
                 // All loads are independent of the adds: they are all issued
                 // before the first add waits.
@@ -216,15 +267,16 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
                 for (int u = 0; u < kRsUnroll; ++u)
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
-                        store4(tr, pd, fh + (int64_t)u * kStep + h * kHalf, a[u][h], out,
-                               out_stride);
+                        store_run(tr, pd, fw + (int64_t)u * kStep + h * kHalf, lane, a[u][h],
+                                  out, out_stride);
             } else if (interior && g0 >= pd.valid) {
                 const float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int u = 0; u < kRsUnroll; ++u)
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
-                        store4(tr, pd, fh + (int64_t)u * kStep + h * kHalf, z, out, out_stride);
+                        store_run(tr, pd, fw + (int64_t)u * kStep + h * kHalf, lane, z, out,
+                                  out_stride);
             } else
 #else
             if (interior && g1 <= pd.valid) {
@@ -338,9 +390,12 @@ __global__ __launch_bounds__(NT) void place_kernel(
     constexpr int kSubs = NT / kThreads;
     const int sub = (int)threadIdx.x / kThreads;
     const int tid = (int)threadIdx.x % kThreads;
+    const bool one_each = kSubs == 1 && (int64_t)gridDim.x == tile_hi - tile_lo;
     for (int64_t t = tile_lo + (int64_t)blockIdx.x * kSubs + sub; t < tile_hi;
          t += (int64_t)gridDim.x * kSubs) {
-        const TileRec rec = tiles[t];
+        const TileRec rec =
+            tiles[one_each ? tile_lo + xcd_tile<TIDE_XCD_CHUNK_AG>(t - tile_lo, tile_hi - tile_lo)
+                           : t];
         const ParamDev pd = params[rec.p];
         uint16_t* dst = ptrs[rec.p];
         const bool vec = (flags[rec.p] & kFlagVector) != 0;

@@ -75,6 +75,12 @@ constexpr int kFullGridCap = TIDE_FULL_GRID_CAP;
 #ifndef TIDE_TILE_ORDER_RANK_MAJOR
 #define TIDE_TILE_ORDER_RANK_MAJOR 0
 #endif
+#ifndef TIDE_TILE_INTERLEAVE
+#define TIDE_TILE_INTERLEAVE 1
+#endif
+#ifndef TIDE_RS_GROUP_ELEMS
+#define TIDE_RS_GROUP_ELEMS (1 << 20)
+#endif
 constexpr int kRingSlots = 8;
 
 struct TileTable {
@@ -185,11 +191,55 @@ std::vector<TileRec> build_tiles(const tide_plan* plan, int op, int rb, int re) 
             out.push_back(t);
         }
     }
+#if TIDE_RS_GROUP_ELEMS > 0
+    // Reduce: consecutive parameters are grouped until their pieces hold at
+    // least TIDE_RS_GROUP_ELEMS elements, and each group is walked rank by
+    // rank. Many small pieces of one rank are adjacent in its shard, so this
+    // turns their short scattered writes into long runs; a large parameter is
+    // a group of its own and keeps its order.
+    if (op == 0 && plan->P > 1) {
+        std::vector<int32_t> group(plan->P, 0);
+        int32_t gid = 0;
+        int64_t acc = 0;
+        for (int32_t p = 0; p < plan->P; ++p) {
+            group[p] = gid;
+            acc += plan->prm[p].s;
+            if (acc >= TIDE_RS_GROUP_ELEMS) {
+                ++gid;
+                acc = 0;
+            }
+        }
+        std::stable_sort(out.begin(), out.end(), [&](const TileRec& a, const TileRec& b) {
+            if (group[a.p] != group[b.p]) return group[a.p] < group[b.p];
+            return a.r0 != b.r0 ? a.r0 < b.r0 : a.p < b.p;
+        });
+    }
+#endif
 #if TIDE_TILE_ORDER_RANK_MAJOR
     // The same tiles (a partition of the index space) walked rank by rank.
     std::stable_sort(out.begin(), out.end(), [](const TileRec& a, const TileRec& b) {
         return a.r0 != b.r0 ? a.r0 < b.r0 : a.p < b.p;
     });
+#endif
+#if TIDE_TILE_INTERLEAVE > 1
+    // Within each group of TIDE_TILE_INTERLEAVE consecutive parameters, walk
+    // the parameters' tiles round robin.
+    {
+        std::vector<int64_t> first(plan->P + 1, 0);
+        for (const TileRec& t : out) first[t.p + 1]++;
+        for (int32_t p = 0; p < plan->P; ++p) first[p + 1] += first[p];
+        std::vector<std::pair<std::pair<int64_t, int64_t>, size_t>> key(out.size());
+        for (size_t i = 0; i < out.size(); ++i) {
+            const int32_t p = out[i].p;
+            key[i] = {{p / TIDE_TILE_INTERLEAVE, (int64_t)i - first[p]}, i};
+        }
+        std::stable_sort(key.begin(), key.end(), [](const auto& a, const auto& b) {
+            return a.first < b.first;
+        });
+        std::vector<TileRec> re(out.size());
+        for (size_t i = 0; i < key.size(); ++i) re[i] = out[key[i].second];
+        out.swap(re);
+    }
 #endif
     return out;
 }

@@ -137,6 +137,20 @@ def test_multi_tile_ragged_group(tide, orc):
              rank_range=(5, 29))
 
 
+@pytest.mark.parametrize("out_off", [0, 1, 2, 3])
+def test_misaligned_destinations(tide, orc, out_off):
+    """Every fp32 misalignment of the shards (base offset x stride), with pieces
+    long enough that whole 256-element runs are realigned in registers, plus
+    runs that cross into the next rank's piece."""
+    shapes = [(512, 1024), (300, 520), (70, 1), (1000, 3), (9, 4096)]
+    N, L = 8, 8
+    grads = host_grads(shapes, L, seed=50 + out_off)
+    for stride_extra in range(4):
+        say("misaligned: out+%d stride+%d" % (out_off, stride_extra))
+        run_case(tide, orc, shapes, N, L, grads, stride_extra=stride_extra, out_off=out_off,
+                 check_ag=False)
+
+
 def test_runtime_contributor_count(tide, orc):
     """L above 8 takes the runtime-L kernel."""
     shapes = [(300, 64), (17, 1), (1000, 40)]
