@@ -59,10 +59,11 @@ constexpr int kDefaultMaxLaunchUs = 300;
 #ifndef TIDE_BUDGET_LDS
 #define TIDE_BUDGET_LDS (128 * 1024)
 #endif
-// Bytes one budgeted workgroup streams per microsecond with a CU to itself;
+// Bytes one budgeted workgroup streams per microsecond with a CU to itself
+// (about 35 GB/s measured on MI355X: per-CU streaming is latency-bound);
 // sizes the budgeted launches so a workgroup lives about max_launch_us.
 #ifndef TIDE_WG_BYTES_PER_US
-#define TIDE_WG_BYTES_PER_US 100000
+#define TIDE_WG_BYTES_PER_US 35000
 #endif
 constexpr int kBudgetThreads = TIDE_BUDGET_THREADS;
 constexpr size_t kBudgetLds = TIDE_BUDGET_LDS;
