@@ -294,6 +294,17 @@ def main():
         e[1].record()
         torch.cuda.synchronize()
         sd = e[0].elapsed_time(e[1]) / 5
+        # Placement from a recursive-doubling stage buffer (rotated by half the ranks).
+        e2 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        tide.allgather_place_stage(plan, shards, cfg.N // 2, p_tab)
+        torch.cuda.synchronize()
+        e2[0].record()
+        for _ in range(5):
+            tide.allgather_place_stage(plan, shards, cfg.N // 2, p_tab)
+        e2[1].record()
+        torch.cuda.synchronize()
+        st = e2[0].elapsed_time(e2[1]) / 5
+        parts["placement_stage_rotated_GBps"] = round(ag_bytes / (st / 1e3) / 1e9, 1)
         parts["placement_sdma_ms"] = round(sd, 4)
         parts["placement_sdma_GBps"] = round(ag_bytes / (sd / 1e3) / 1e9, 1)
         parts["plain_copy_GBps"] = round(copy_ceiling_gbps(torch), 1)

@@ -163,6 +163,48 @@ tide_status tide_allgather_place(const tide_plan* plan, const uint16_t* shards,
                                  int64_t shard_stride, uint16_t* const* params, void* stream,
                                  int32_t engine, const tide_launch* launch);
 
+/*
+ * All-gather placement from a stage buffer in arrival order. After the
+ * recursive-doubling exchange (page 1 "All-gather: parameters land at their
+ * final address"; page 3 Figure 5), node n holds the shards of nodes n,
+ * n+1, ... (mod M) in its stage slots 0, 1, ...; with L ranks per node the
+ * shard of rank r sits at stage position (r - first_rank) mod N with
+ * first_rank = n * L. Same contract as tide_allgather_place, whose call is this
+ * one with first_rank = 0 (first_rank must lie in [0, N)).
+ */
+tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* stage,
+                                       int64_t shard_stride, int32_t first_rank,
+                                       uint16_t* const* params, void* stream, int32_t engine,
+                                       const tide_launch* launch);
+
+/* One round of node n's recursive-doubling all-gather schedule. */
+typedef struct tide_rd_step {
+    int32_t round;        /* d = 0, 1, ... */
+    int32_t send_to;      /* node (n - 2^d) mod M */
+    int32_t recv_from;    /* node (n + 2^d) mod M */
+    int32_t count;        /* pieces sent and received: min(2^d, M - 2^d) */
+    int32_t send_slot;    /* first stage slot sent (slots send_slot .. send_slot + count - 1) */
+    int32_t recv_slot;    /* first stage slot the received pieces fill */
+    int64_t head_bytes;   /* head of this round's send: min(count * piece_bytes, head limit) */
+    int64_t tail_bytes;   /* the rest of the send */
+} tide_rd_step;
+
+/*
+ * Node `node`'s recursive-doubling all-gather schedule over M nodes (page 1
+ * "All-gather: parameters land at their final address"; page 3 Figure 5(a)).
+ * In round d the node sends the first min(2^d, M - 2^d) pieces it holds to
+ * node n - 2^d and receives as many from node n + 2^d (mod M); there are
+ * ceil(log2 M) rounds, and no piece arrives twice. Stage slot k ends up
+ * holding node (n + k) mod M's piece. Each round's send is split into a head
+ * of at most head_bytes (0 -> 8 MiB) and a tail, for pacing.
+ *   steps: caller array of `capacity` entries (capacity >= ceil(log2 M));
+ *   *nsteps receives the round count. Host-only.
+ * Errors: INVALID_ARG (M < 1, node outside [0, M), piece_bytes < 0,
+ * head_bytes < 0, capacity too small, NULL pointers).
+ */
+tide_status tide_rd_schedule(int32_t M, int32_t node, int64_t piece_bytes, int64_t head_bytes,
+                             tide_rd_step* steps, int32_t capacity, int32_t* nsteps);
+
 /* Kernel launches a call with these options makes (op 0 = reduce-scatter,
  * 1 = placement with the kernel engine). Host-only. */
 tide_status tide_plan_launch_count(const tide_plan* plan, int32_t op, const tide_launch* launch,

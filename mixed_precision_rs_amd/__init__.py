@@ -16,11 +16,13 @@ from ._lib import (  # noqa: F401
     PointerTable,
     TideError,
     allgather_place,
+    allgather_place_stage,
     budgeted,
     grads_table,
     lib,
     params_table,
     plan_create,
+    rd_schedule,
     reduce_scatter_bf16_fp32,
     version,
 )

@@ -26,7 +26,7 @@ FLAG_SCALAR_PATH = 0x1
 EXPORTS = ["tide_plan_create", "tide_plan_destroy", "tide_plan_dims", "tide_plan_param",
            "tide_plan_map", "tide_reduce_scatter_bf16_fp32", "tide_allgather_place",
            "tide_plan_launch_count", "tide_status_string", "tide_last_error_detail",
-           "tide_version"]
+           "tide_version", "tide_allgather_place_stage", "tide_rd_schedule"]
 
 
 class TideError(RuntimeError):
@@ -35,6 +35,14 @@ class TideError(RuntimeError):
         self.status_name = STATUS_NAMES.get(status, "TIDE_ERR_%d" % status)
         self.detail = detail
         super().__init__("%s failed: %s: %s" % (call, self.status_name, detail))
+
+
+class RdStep(ctypes.Structure):
+    """tide_rd_step."""
+    _fields_ = [("round", ctypes.c_int32), ("send_to", ctypes.c_int32),
+                ("recv_from", ctypes.c_int32), ("count", ctypes.c_int32),
+                ("send_slot", ctypes.c_int32), ("recv_slot", ctypes.c_int32),
+                ("head_bytes", ctypes.c_int64), ("tail_bytes", ctypes.c_int64)]
 
 
 class Launch(ctypes.Structure):
@@ -83,6 +91,12 @@ def _load():
                                          ctypes.POINTER(Launch)]
     lib.tide_plan_launch_count.argtypes = [ctypes.c_void_p, ctypes.c_int32,
                                            ctypes.POINTER(Launch), _I64P]
+    lib.tide_allgather_place_stage.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                               ctypes.c_int32, _VPP, ctypes.c_void_p,
+                                               ctypes.c_int32, ctypes.POINTER(Launch)]
+    lib.tide_rd_schedule.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                     ctypes.c_int64, ctypes.POINTER(RdStep), ctypes.c_int32,
+                                     _I32P]
     lib.tide_status_string.argtypes = [ctypes.c_int]
     lib.tide_status_string.restype = ctypes.c_char_p
     lib.tide_last_error_detail.argtypes = []
@@ -90,7 +104,8 @@ def _load():
     lib.tide_version.argtypes = []
     lib.tide_version.restype = ctypes.c_int32
     for f in ("tide_plan_create", "tide_plan_dims", "tide_plan_param", "tide_plan_map",
-              "tide_reduce_scatter_bf16_fp32", "tide_allgather_place", "tide_plan_launch_count"):
+              "tide_reduce_scatter_bf16_fp32", "tide_allgather_place", "tide_plan_launch_count",
+              "tide_allgather_place_stage", "tide_rd_schedule"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -258,6 +273,36 @@ def allgather_place(plan: Plan, shards, params: Sequence[object],
                                       ctypes.byref(launch) if launch is not None else None)
     _check(st, "tide_allgather_place")
     _record(tab.refs + [shards], sobj)
+
+
+def allgather_place_stage(plan: Plan, stage, first_rank: int, params: Sequence[object],
+                          shard_stride: Optional[int] = None, stream=None,
+                          engine: Union[int, str] = ENGINE_KERNEL,
+                          launch: Optional[Launch] = None) -> None:
+    """Placement from a stage buffer whose position k holds rank
+    (first_rank + k) mod N (recursive-doubling arrival order)."""
+    tab = params if isinstance(params, PointerTable) else params_table(plan, params)
+    if tab.n != plan.P:
+        raise ValueError("pointer table holds %d entries, expected P=%d" % (tab.n, plan.P))
+    if isinstance(engine, str):
+        engine = {"kernel": ENGINE_KERNEL, "sdma": ENGINE_SDMA}[engine]
+    stride = plan.S if shard_stride is None else int(shard_stride)
+    sh, sobj = _stream_handle(stream)
+    st = _load().tide_allgather_place_stage(plan.handle, _ptr(stage), stride, int(first_rank),
+                                            tab.arr, sh, int(engine),
+                                            ctypes.byref(launch) if launch is not None else None)
+    _check(st, "tide_allgather_place_stage")
+    _record(tab.refs + [stage], sobj)
+
+
+def rd_schedule(M: int, node: int, piece_bytes: int = 0, head_bytes: int = 0):
+    """Node's recursive-doubling rounds as a list of dicts (tide_rd_schedule)."""
+    cap = 64
+    steps = (RdStep * cap)()
+    n = ctypes.c_int32()
+    _check(_load().tide_rd_schedule(M, node, piece_bytes, head_bytes, steps, cap,
+                                    ctypes.byref(n)), "tide_rd_schedule")
+    return [{f: getattr(steps[i], f) for f, _ in RdStep._fields_} for i in range(n.value)]
 
 
 def version() -> int:

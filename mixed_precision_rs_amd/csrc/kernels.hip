@@ -342,14 +342,20 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
     }
 }
 
+// Position of rank r's shard in a stage buffer that starts with rank first.
+__device__ __forceinline__ int64_t stage_pos(int64_t r, int32_t first, int32_t n) {
+    const int64_t q = r - first;
+    return q < 0 ? q + n : q;
+}
+
 // 8 bf16 of the rank-major shards for flat parameter indices f..f+7.
 __device__ __forceinline__ u32x4 gather8(const Span& t, const ParamDev& pd, int64_t f,
                                          const uint16_t* __restrict__ shards, int64_t stride,
-                                         int64_t shard_elems) {
+                                         int64_t shard_elems, int32_t first, int32_t n) {
     int64_t r, j;
     locate<kAgTile>(t, pd.s, f, r, j);
     if (j + kVec <= pd.s) {
-        const int64_t e = r * stride + pd.o + j;
+        const int64_t e = stage_pos(r, first, n) * stride + pd.o + j;
         const uint16_t* src = shards + e;
         if ((reinterpret_cast<uintptr_t>(src) & 3) == 0)
             return TIDE_LD(reinterpret_cast<const u32x4_a4*>(src));
@@ -371,7 +377,7 @@ __device__ __forceinline__ u32x4 gather8(const Span& t, const ParamDev& pd, int6
     uint32_t h[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) {
-        h[e] = shards[r * stride + pd.o + j];
+        h[e] = shards[stage_pos(r, first, n) * stride + pd.o + j];
         step(pd.s, r, j);
     }
     u32x4 w;
@@ -386,7 +392,7 @@ __global__ __launch_bounds__(NT) void place_kernel(
     const TileRec* __restrict__ tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb, int32_t re,
     const ParamDev* __restrict__ params, uint16_t* const* __restrict__ ptrs,
     const uint32_t* __restrict__ flags, const uint16_t* __restrict__ shards, int64_t stride,
-    int64_t shard_elems) {
+    int64_t shard_elems, int32_t first, int32_t nranks) {
     constexpr int kSubs = NT / kThreads;
     const int sub = (int)threadIdx.x / kThreads;
     const int tid = (int)threadIdx.x % kThreads;
@@ -409,7 +415,8 @@ __global__ __launch_bounds__(NT) void place_kernel(
                 u32x4 w[kAgUnroll];
 #pragma unroll
                 for (int u = 0; u < kAgUnroll; ++u)
-                    w[u] = gather8(tr, pd, f0 + (int64_t)u * kStep, shards, stride, shard_elems);
+                    w[u] = gather8(tr, pd, f0 + (int64_t)u * kStep, shards, stride, shard_elems,
+                                   first, nranks);
                 TIDE_GLOBAL u32x4* d4 = gbl_mut<u32x4>(dst + f0);
 #pragma unroll
                 for (int u = 0; u < kAgUnroll; ++u)
@@ -425,7 +432,7 @@ __global__ __launch_bounds__(NT) void place_kernel(
                     for (int e = 0; e < kVec; ++e, step(pd.s, r, j)) {
                         const int64_t f = fu + e;
                         if (f < tr.lo || f >= end) continue;
-                        d[f] = shards[r * stride + pd.o + j];
+                        d[f] = shards[stage_pos(r, first, nranks) * stride + pd.o + j];
                     }
                 }
             }
@@ -476,9 +483,9 @@ hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
                         const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                         int32_t re, const ParamDev* params, uint16_t* const* ptrs,
                         const uint32_t* flags, const uint16_t* shards, int64_t shard_stride,
-                        int64_t shard_elems) {
+                        int64_t shard_elems, int32_t first_rank, int32_t nranks) {
     void* args[] = {&tiles, &tile_lo, &tile_hi, &rb, &re, &params, &ptrs, &flags, &shards,
-                    &shard_stride, &shard_elems};
+                    &shard_stride, &shard_elems, &first_rank, &nranks};
     const void* fn = threads == kFatThreads
                          ? reinterpret_cast<const void*>(&place_kernel<kFatThreads>)
                          : reinterpret_cast<const void*>(&place_kernel<kThreads>);

@@ -627,8 +627,18 @@ tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t*
 tide_status tide_allgather_place(const tide_plan* plan, const uint16_t* shards,
                                  int64_t shard_stride, uint16_t* const* params, void* stream_v,
                                  int32_t engine, const tide_launch* launch) {
+    return tide_allgather_place_stage(plan, shards, shard_stride, 0, params, stream_v, engine,
+                                      launch);
+}
+
+tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* shards,
+                                       int64_t shard_stride, int32_t first_rank,
+                                       uint16_t* const* params, void* stream_v, int32_t engine,
+                                       const tide_launch* launch) {
     try {
         if (!plan) return fail(TIDE_ERR_INVALID_ARG, "plan is NULL");
+        if (first_rank < 0 || first_rank >= plan->N)
+            return fail(TIDE_ERR_INVALID_ARG, "first_rank %d outside [0, %d)", first_rank, plan->N);
         tide_launch l;
         tide_status st = resolve_launch(plan, launch, &l);
         if (st != TIDE_OK) return st;
@@ -651,9 +661,12 @@ tide_status tide_allgather_place(const tide_plan* plan, const uint16_t* shards,
         uint16_t** tp = reinterpret_cast<uint16_t**>(table.data());
         uint32_t* fl = reinterpret_cast<uint32_t*>(table.data() + (size_t)P * sizeof(void*));
         const uintptr_t sb = reinterpret_cast<uintptr_t>(shards);
-        const Range rd{sb + (uintptr_t)l.rank_begin * shard_stride * 2,
-                       sb + (uintptr_t)(l.rank_end - 1) * shard_stride * 2 + (uintptr_t)plan->S * 2,
-                       -1};
+        // Shards read: ranks [rank_begin, rank_end) in place, or the whole
+        // stage buffer when it is rotated.
+        const Range rd = first_rank == 0
+            ? Range{sb + (uintptr_t)l.rank_begin * shard_stride * 2,
+                    sb + (uintptr_t)(l.rank_end - 1) * shard_stride * 2 + (uintptr_t)plan->S * 2, -1}
+            : Range{sb, sb + (uintptr_t)(plan->N - 1) * shard_stride * 2 + (uintptr_t)plan->S * 2, -1};
         std::vector<Range> wr;
         for (int32_t p = 0; p < P; ++p) {
             const ParamInfo& q = plan->prm[p];
@@ -678,7 +691,10 @@ tide_status tide_allgather_place(const tide_plan* plan, const uint16_t* shards,
         if (engine == TIDE_ENGINE_SDMA) {
             // One 2-D copy per parameter for its full pieces (rows of s_p
             // elements, source pitch = shard stride, destination contiguous),
-            // plus one 1-D copy for a partial last piece.
+            // split in two where a rotated stage wraps, plus one 1-D copy for
+            // a partial last piece.
+            const int64_t N = plan->N;
+            auto pos = [&](int64_t r) { return (r - first_rank + N) % N; };
             for (int32_t p = 0; p < P; ++p) {
                 const ParamInfo& q = plan->prm[p];
                 if (q.valid == 0) continue;
@@ -686,16 +702,21 @@ tide_status tide_allgather_place(const tide_plan* plan, const uint16_t* shards,
                 const int64_t fb = std::min<int64_t>(l.rank_begin, full);
                 const int64_t fe = std::min<int64_t>(l.rank_end, full);
                 const uint16_t* src0 = shards + q.o;
-                if (fe > fb)
-                    TIDE_HIP_TRY(hipMemcpy2DAsync(params[p] + fb * q.s, (size_t)q.s * 2,
-                                                  src0 + fb * shard_stride,
+                const int64_t cut = std::min(std::max<int64_t>(first_rank, fb), fe);
+                const int64_t seg[2][2] = {{fb, cut}, {cut, fe}};
+                for (const auto& sg : seg) {
+                    if (sg[1] <= sg[0]) continue;
+                    TIDE_HIP_TRY(hipMemcpy2DAsync(params[p] + sg[0] * q.s, (size_t)q.s * 2,
+                                                  src0 + pos(sg[0]) * shard_stride,
                                                   (size_t)shard_stride * 2, (size_t)q.s * 2,
-                                                  (size_t)(fe - fb), hipMemcpyDeviceToDevice,
+                                                  (size_t)(sg[1] - sg[0]), hipMemcpyDeviceToDevice,
                                                   stream));
+                }
                 const int64_t rem = q.valid - full * q.s;
                 if (rem > 0 && full >= l.rank_begin && full < l.rank_end)
-                    TIDE_HIP_TRY(hipMemcpyAsync(params[p] + full * q.s, src0 + full * shard_stride,
-                                                (size_t)rem * 2, hipMemcpyDeviceToDevice, stream));
+                    TIDE_HIP_TRY(hipMemcpyAsync(params[p] + full * q.s,
+                                                src0 + pos(full) * shard_stride, (size_t)rem * 2,
+                                                hipMemcpyDeviceToDevice, stream));
             }
             return TIDE_OK;
         }
@@ -722,7 +743,7 @@ tide_status tide_allgather_place(const tide_plan* plan, const uint16_t* shards,
                              [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi) {
             return launch_place(grid, threads, lds, stream, tt->dev, lo, hi, l.rank_begin,
                                 l.rank_end, ds->params, dptrs, dflags, shards, shard_stride,
-                                shard_elems);
+                                shard_elems, first_rank, plan->N);
         });
         tide_status st2 = release_slot(ds, slot, stream);
         return st != TIDE_OK ? st : st2;
@@ -731,6 +752,38 @@ tide_status tide_allgather_place(const tide_plan* plan, const uint16_t* shards,
     } catch (...) {
         return fail(TIDE_ERR_INVALID_ARG, "unexpected exception");
     }
+}
+
+tide_status tide_rd_schedule(int32_t M, int32_t node, int64_t piece_bytes, int64_t head_bytes,
+                             tide_rd_step* steps, int32_t capacity, int32_t* nsteps) {
+    if (M < 1) return fail(TIDE_ERR_INVALID_ARG, "M = %d < 1", M);
+    if (node < 0 || node >= M) return fail(TIDE_ERR_INVALID_ARG, "node %d outside [0, %d)", node, M);
+    if (piece_bytes < 0 || head_bytes < 0) return fail(TIDE_ERR_INVALID_ARG, "negative byte count");
+    if (!nsteps) return fail(TIDE_ERR_INVALID_ARG, "nsteps is NULL");
+    if (head_bytes == 0) head_bytes = (int64_t)8 << 20;   // 8 MiB of heads (page 1)
+    int32_t rounds = 0;
+    while (((int64_t)1 << rounds) < M) ++rounds;          // ceil(log2 M)
+    if (rounds > 0 && (!steps || capacity < rounds))
+        return fail(TIDE_ERR_INVALID_ARG, "capacity %d < %d rounds", capacity, rounds);
+    int32_t held = 1;                                      // slots filled: own piece at slot 0
+    for (int32_t d = 0; d < rounds; ++d) {
+        const int32_t step = 1 << d;
+        const int32_t count = std::min(step, M - step);
+        int64_t bytes;
+        if (!mul_ok(count, piece_bytes, &bytes)) return fail(TIDE_ERR_OVERFLOW, "round bytes overflow");
+        tide_rd_step& t = steps[d];
+        t.round = d;
+        t.send_to = (int32_t)(((int64_t)node - step % M + M) % M);
+        t.recv_from = (int32_t)(((int64_t)node + step) % M);
+        t.count = count;
+        t.send_slot = 0;
+        t.recv_slot = held;
+        t.head_bytes = std::min(bytes, head_bytes);
+        t.tail_bytes = bytes - t.head_bytes;
+        held += count;
+    }
+    *nsteps = rounds;
+    return TIDE_OK;
 }
 
 const char* tide_status_string(tide_status s) {

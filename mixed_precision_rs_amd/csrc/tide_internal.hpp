@@ -76,7 +76,7 @@ hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
                         const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                         int32_t re, const ParamDev* params, uint16_t* const* ptrs,
                         const uint32_t* flags, const uint16_t* shards, int64_t shard_stride,
-                        int64_t shard_elems);
+                        int64_t shard_elems, int32_t first_rank, int32_t nranks);
 
 // Allow `lds` bytes of dynamic LDS on every kernel variant for L contributors.
 hipError_t allow_dynamic_lds(int L, size_t lds);

@@ -44,8 +44,13 @@ class Oracle:
                                                _U16P, ctypes.c_int64, ctypes.POINTER(_U16P),
                                                ctypes.c_int32, ctypes.c_int32,
                                                ctypes.POINTER(_U32P)]
+        lib.oracle_allgather_place_stage.argtypes = [ctypes.c_int32, _I64P, _I64P, ctypes.c_int32,
+                                                     _U16P, ctypes.c_int64, ctypes.c_int32,
+                                                     ctypes.POINTER(_U16P), ctypes.c_int32,
+                                                     ctypes.c_int32]
         for f in ("oracle_layout", "oracle_piece_start", "oracle_reduce_scatter",
-                  "oracle_piece_rows", "oracle_reduce_piece", "oracle_allgather_place"):
+                  "oracle_piece_rows", "oracle_reduce_piece", "oracle_allgather_place",
+                  "oracle_allgather_place_stage"):
             getattr(lib, f).restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
@@ -169,6 +174,28 @@ class Oracle:
             raise ValueError("oracle_allgather_place rejected its arguments")
         if count_writes:
             return params, counts
+        return params
+
+
+    def allgather_place_stage(self, shapes, N, stage: np.ndarray, first_rank: int,
+                              shard_stride=None, rank_range=None,
+                              params: Optional[List[np.ndarray]] = None):
+        """Placement from a stage buffer whose position k holds rank
+        (first_rank + k) mod N."""
+        rows, rlen = self._shape_arrays(shapes)
+        P = len(shapes)
+        S = self.layout(shapes, N)["S"]
+        stride = S if shard_stride is None else shard_stride
+        rb, re = (0, N) if rank_range is None else rank_range
+        stage = np.ascontiguousarray(stage, dtype=np.uint16)
+        if params is None:
+            params = [np.zeros(t * k, np.uint16) for t, k in shapes]
+        pp = (_U16P * max(P, 1))(*[self._p(a, _U16P) for a in params])
+        rc = self.lib.oracle_allgather_place_stage(
+            P, self._p(rows, _I64P), self._p(rlen, _I64P), N, self._p(stage, _U16P), stride,
+            first_rank, pp, rb, re)
+        if rc != 0:
+            raise ValueError("oracle_allgather_place_stage rejected its arguments")
         return params
 
 

@@ -1,0 +1,73 @@
+"""Recursive-doubling all-gather schedule, written from page 1 ("All-gather:
+parameters land at their final address") and page 3 Figure 5(a).
+
+TEST INFRASTRUCTURE ONLY (plain Python, small inputs): the library's own
+schedule generator is checked against this, and this against the pages'
+worked facts (M = 5 takes 3 rounds; M = 8 takes 3 where a ring takes 7).
+
+The pages' description, restated: machines are numbered 0..M-1. In round d
+(from 0) machine n sends the first min(2^d, M - 2^d) pieces it has collected
+to machine n - 2^d and receives as many from machine n + 2^d, numbers taken
+modulo M; machines begin holding only their own piece. The rounds stop once
+every machine holds all M pieces, which takes ceil(log2 M) rounds. Each
+transfer is split into a small head and the rest (the tail); the heads of a
+round total at most `head_bytes` (8 MiB by default on page 1), and the next
+round starts once the heads are confirmed.
+"""
+from typing import Dict, List
+
+
+def rd_rounds(M: int) -> int:
+    """Number of rounds: the smallest d with 2^d >= M (0 for M = 1)."""
+    d = 0
+    while (1 << d) < M:
+        d += 1
+    return d
+
+
+def rd_schedule(M: int, n: int, piece_bytes: int = 0, head_bytes: int = 8 << 20) -> List[Dict]:
+    """Node n's transfers, one dict per round:
+    round, send_to, recv_from, count (pieces), send_slots (held slots sent),
+    recv_slots (where the received pieces go), head, tail (bytes of the send).
+    Slot k of node n's stage holds the piece of node (n + k) mod M."""
+    out = []
+    held = 1
+    for d in range(rd_rounds(M)):
+        step = 1 << d
+        count = min(step, M - step)
+        nbytes = count * piece_bytes
+        head = min(nbytes, head_bytes)
+        out.append({
+            "round": d,
+            "send_to": (n - step) % M,
+            "recv_from": (n + step) % M,
+            "count": count,
+            "send_slots": list(range(0, count)),
+            "recv_slots": list(range(held, held + count)),
+            "head": head,
+            "tail": nbytes - head,
+        })
+        held += count
+    return out
+
+
+def rd_simulate(M: int) -> List[List[int]]:
+    """Run every node's schedule; return each node's stage as the list of
+    node ids held in slot order. Each sent piece is the sender's slot, read
+    before that round's receives land (all sends of a round use the holdings
+    from the end of the previous round)."""
+    stage = [[n] for n in range(M)]
+    for d in range(rd_rounds(M)):
+        before = [list(s) for s in stage]
+        for n in range(M):
+            sched = rd_schedule(M, n)[d]
+            src = sched["recv_from"]
+            for k, slot in zip(sched["send_slots"], sched["recv_slots"]):
+                # node src sends its slot k (its send_slots) to node n
+                assert slot == len(stage[n]), "receive slots must be filled in order"
+                stage[n].append(before[src][k])
+    return stage
+
+
+def ring_rounds(M: int) -> int:
+    return max(M - 1, 0)

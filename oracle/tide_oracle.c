@@ -280,3 +280,43 @@ int oracle_allgather_place(int32_t P, const int64_t *rows, const int64_t *row_le
     layout_free(&lay);
     return 0;
 }
+
+/*
+ * All-gather placement from a stage buffer in arrival order. After the
+ * recursive-doubling exchange on page 1 ("All-gather: parameters land at
+ * their final address"), node n holds the pieces of nodes n, n+1, ... (mod M)
+ * in its stage slots 0, 1, ...; with L ranks per node, rank r's shard sits at
+ * stage position (r - first_rank) mod N, first_rank = n * L. This is the
+ * placement above with shard r read from stage + ((r - first_rank) mod N) *
+ * shard_stride.
+ */
+int oracle_allgather_place_stage(int32_t P, const int64_t *rows, const int64_t *row_len,
+                                 int32_t N, const uint16_t *stage, int64_t shard_stride,
+                                 int32_t first_rank, uint16_t *const *params,
+                                 int32_t rank_begin, int32_t rank_end)
+{
+    struct layout lay;
+    int rc = layout_alloc(&lay, P, rows, row_len, N);
+    if (rc == 0 && (shard_stride < lay.S || rank_begin < 0 || rank_end > N ||
+                    rank_begin > rank_end || first_rank < 0 || first_rank >= N))
+        rc = -1;
+    if (rc != 0) {
+        layout_free(&lay);
+        return rc;
+    }
+    for (int32_t r = rank_begin; r < rank_end; ++r) {
+        const int64_t slot = ((int64_t)r - first_rank + N) % N;   /* stage position of rank r */
+        for (int32_t p = 0; p < P; ++p) {
+            const int64_t T = rows[p], K = row_len[p], Rp = lay.R[p];
+            for (int64_t i = 0; i < Rp; ++i) {
+                const int64_t t = (int64_t)r * Rp + i;
+                if (t >= T)
+                    break;
+                for (int64_t k = 0; k < K; ++k)
+                    params[p][t * K + k] = stage[slot * shard_stride + lay.o[p] + i * K + k];
+            }
+        }
+    }
+    layout_free(&lay);
+    return 0;
+}
