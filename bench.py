@@ -305,6 +305,26 @@ def main():
         torch.cuda.synchronize()
         st = e2[0].elapsed_time(e2[1]) / 5
         parts["placement_stage_rotated_GBps"] = round(ag_bytes / (st / 1e3) / 1e9, 1)
+        # Level-2 landing sum of one node (M = L source partials of this
+        # group's shard size): M * L * S * 4 bytes read, L * S * 4 written.
+        Lg = Mg = cfg.L
+        Cg = -(-S // Lg)
+        inb = [torch.empty(Lg * Lg * Cg, dtype=torch.float32, device="cuda").normal_()
+               for _ in range(Lg)]
+        shd = [torch.empty(S, dtype=torch.float32, device="cuda") for _ in range(Lg)]
+        tide.landing_sum_fp32(Lg, Mg, S, inb, shd)
+        torch.cuda.synchronize()
+        e3 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e3[0].record()
+        for _ in range(5):
+            tide.landing_sum_fp32(Lg, Mg, S, inb, shd)
+        e3[1].record()
+        torch.cuda.synchronize()
+        lt = e3[0].elapsed_time(e3[1]) / 5
+        lb = (Mg * Lg * S + Lg * S) * 4
+        parts["landing_ms"] = round(lt, 4)
+        parts["landing_GBps"] = round(lb / (lt / 1e3) / 1e9, 1)
+        del inb, shd
         parts["placement_sdma_ms"] = round(sd, 4)
         parts["placement_sdma_GBps"] = round(ag_bytes / (sd / 1e3) / 1e9, 1)
         parts["plain_copy_GBps"] = round(copy_ceiling_gbps(torch), 1)

@@ -80,7 +80,7 @@ typedef enum tide_launch_mode {
 typedef struct tide_launch {
     int32_t mode;            /* tide_launch_mode */
     int32_t reduce_blocks;   /* BUDGETED: workgroups of each reduce launch (0 -> 16) */
-    int32_t place_blocks;    /* BUDGETED: workgroups of each placement launch (0 -> 4) */
+    int32_t place_blocks;    /* BUDGETED: workgroups of each placement or landing launch (0 -> 4) */
     int32_t max_launch_us;   /* BUDGETED: work per launch sized so a workgroup lives about
                                 this long (0 -> 300). Each launch is a separate kernel; no
                                 workgroup ever waits on another. */
@@ -204,6 +204,44 @@ typedef struct tide_rd_step {
  */
 tide_status tide_rd_schedule(int32_t M, int32_t node, int64_t piece_bytes, int64_t head_bytes,
                              tide_rd_step* steps, int32_t capacity, int32_t* nsteps);
+
+/*
+ * Level 2 of the reduce-scatter on one destination node: the landing sum
+ * (page 1 "Reduce-scatter: two levels of addition, the last one done by
+ * NVSwitch"; page 3 Figure 6(b)). Plan-free; one call covers the node's L GPUs.
+ *
+ * Every GPU b of the node finally holds an fp32 shard of S elements. A source
+ * node's fp32 partial of the node's part is cut into L slices: slice s is the
+ * s-th chunk of C = ceil(S / L) elements of every local shard, one block per
+ * GPU b. A source with relative index c = (destination - source) mod M sends
+ * slice s to GPU (s - c) mod L (the Latin-square seating, tide_latin_square),
+ * so the M copies of a slice sit on M different GPUs at the same offset.
+ *   inboxes[g] (g < L): device pointer to GPU g's inbox, L slots x L blocks x C
+ *       fp32; slot s, block b starts at element (s * L + b) * C. 4-byte aligned.
+ *       Only slots that a source with c < M filled are read. Read only.
+ *   shards[b] (b < L): device pointer to GPU b's fp32 shard (S elements), 4-byte
+ *       aligned; must not overlap any inbox or another shard.
+ *   1 <= M <= L <= 64 sources (batches of at most L sources: call once per
+ *   batch with accumulate = 1 after the first).
+ * shards[b][s * C + e] = fold_{c = 0..M-1} inboxes[(s - c) mod L][(s * L + b) * C + e]
+ * as a left fold in source order (binary32 round-to-nearest-even); with
+ * accumulate = 1 the fold is then added to the shard's current value.
+ * launch: FULL or BUDGETED (place_blocks workgroups: the pages' 4 landing
+ * blocks); rank_begin / rank_end must be 0. Async on `stream`; allocates nothing.
+ */
+tide_status tide_landing_sum_fp32(int32_t L, int32_t M, int64_t S, const float* const* inboxes,
+                                  float* const* shards, int32_t accumulate, void* stream,
+                                  const tide_launch* launch);
+
+/*
+ * The Latin-square seating for one (destination, source) node pair (page 1,
+ * the 4-GPU hand calculation; page 3 Figure 6(b)): *c = (dst - src) mod M;
+ * slice_of_src_gpu[j] = (j + c) mod L, the slice source GPU j handles and sends
+ * over rail j; dst_gpu_of_slice[s] = (s - c) mod L, the destination GPU slice s
+ * lands on. Arrays of L entries (may be NULL). Host-only.
+ */
+tide_status tide_latin_square(int32_t M, int32_t L, int32_t dst_node, int32_t src_node, int32_t* c,
+                              int32_t* slice_of_src_gpu, int32_t* dst_gpu_of_slice);
 
 /* Kernel launches a call with these options makes (op 0 = reduce-scatter,
  * 1 = placement with the kernel engine). Host-only. */

@@ -19,6 +19,8 @@ from ._lib import (  # noqa: F401
     allgather_place_stage,
     budgeted,
     grads_table,
+    landing_sum_fp32,
+    latin_square,
     lib,
     params_table,
     plan_create,

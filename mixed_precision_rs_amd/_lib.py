@@ -26,7 +26,8 @@ FLAG_SCALAR_PATH = 0x1
 EXPORTS = ["tide_plan_create", "tide_plan_destroy", "tide_plan_dims", "tide_plan_param",
            "tide_plan_map", "tide_reduce_scatter_bf16_fp32", "tide_allgather_place",
            "tide_plan_launch_count", "tide_status_string", "tide_last_error_detail",
-           "tide_version", "tide_allgather_place_stage", "tide_rd_schedule"]
+           "tide_version", "tide_allgather_place_stage", "tide_rd_schedule",
+           "tide_landing_sum_fp32", "tide_latin_square"]
 
 
 class TideError(RuntimeError):
@@ -97,6 +98,11 @@ def _load():
     lib.tide_rd_schedule.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                      ctypes.c_int64, ctypes.POINTER(RdStep), ctypes.c_int32,
                                      _I32P]
+    lib.tide_landing_sum_fp32.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _VPP,
+                                          _VPP, ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.POINTER(Launch)]
+    lib.tide_latin_square.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int32, _I32P, _I32P, _I32P]
     lib.tide_status_string.argtypes = [ctypes.c_int]
     lib.tide_status_string.restype = ctypes.c_char_p
     lib.tide_last_error_detail.argtypes = []
@@ -105,7 +111,8 @@ def _load():
     lib.tide_version.restype = ctypes.c_int32
     for f in ("tide_plan_create", "tide_plan_dims", "tide_plan_param", "tide_plan_map",
               "tide_reduce_scatter_bf16_fp32", "tide_allgather_place", "tide_plan_launch_count",
-              "tide_allgather_place_stage", "tide_rd_schedule"):
+              "tide_allgather_place_stage", "tide_rd_schedule", "tide_landing_sum_fp32",
+              "tide_latin_square"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -303,6 +310,32 @@ def rd_schedule(M: int, node: int, piece_bytes: int = 0, head_bytes: int = 0):
     _check(_load().tide_rd_schedule(M, node, piece_bytes, head_bytes, steps, cap,
                                     ctypes.byref(n)), "tide_rd_schedule")
     return [{f: getattr(steps[i], f) for f, _ in RdStep._fields_} for i in range(n.value)]
+
+
+def landing_sum_fp32(L: int, M: int, S: int, inboxes: Sequence[object], shards: Sequence[object],
+                     accumulate: bool = False, stream=None,
+                     launch: Optional[Launch] = None) -> None:
+    """Level-2 landing sum of one destination node (tide_landing_sum_fp32).
+    inboxes[g]: fp32 device tensors of L*L*ceil(S/L); shards[b]: fp32 of S."""
+    if len(inboxes) != L or len(shards) != L:
+        raise ValueError("need L=%d inboxes and L shards" % L)
+    ia = (ctypes.c_void_p * L)(*[_ptr(t) for t in inboxes])
+    sa = (ctypes.c_void_p * L)(*[_ptr(t) for t in shards])
+    sh, sobj = _stream_handle(stream)
+    st = _load().tide_landing_sum_fp32(L, M, S, ia, sa, 1 if accumulate else 0, sh,
+                                       ctypes.byref(launch) if launch is not None else None)
+    _check(st, "tide_landing_sum_fp32")
+    _record(list(inboxes) + list(shards), sobj)
+
+
+def latin_square(M: int, L: int, dst_node: int, src_node: int):
+    """(c, slice handled by each source GPU, destination GPU of each slice)."""
+    c = ctypes.c_int32()
+    a = (ctypes.c_int32 * L)()
+    b = (ctypes.c_int32 * L)()
+    _check(_load().tide_latin_square(M, L, dst_node, src_node, ctypes.byref(c), a, b),
+           "tide_latin_square")
+    return int(c.value), list(a), list(b)
 
 
 def version() -> int:

@@ -440,6 +440,81 @@ __global__ __launch_bounds__(NT) void place_kernel(
     }
 }
 
+// Level-2 landing sum: shard_b[f] = fold_c inbox_{(s - c) mod L}[(s L + b) C + e]
+// with s = f / C, e = f % C. All M inboxes are read at the same offset (the
+// Latin-square seating puts a slice's copies at the same address on M
+// GPUs), 16 bytes per lane, so each wave reads M contiguous 1 KiB runs.
+template <int MT, int NT>
+__global__ __launch_bounds__(NT) void landing_kernel(LandingPtrs ptrs, int32_t L, int32_t Mrt,
+                                                     int64_t S, int64_t C, int64_t tiles_per_shard,
+                                                     int64_t tile_lo, int64_t tile_hi,
+                                                     int32_t accumulate, int32_t scalar) {
+    constexpr int kSubs = NT / kThreads;
+    const int M = MT > 0 ? MT : Mrt;
+    const int sub = (int)threadIdx.x / kThreads;
+    const int tid = (int)threadIdx.x % kThreads;
+    for (int64_t t = tile_lo + (int64_t)blockIdx.x * kSubs + sub; t < tile_hi;
+         t += (int64_t)gridDim.x * kSubs) {
+        const int64_t b = t / tiles_per_shard;
+        const int64_t f0 = (t - b * tiles_per_shard) * kLandTile;
+        const int64_t end = min(f0 + kLandTile, S);
+        float* shard = ptrs.shard[b];
+        for (int64_t fs = f0; fs < end; fs += (int64_t)kThreads * 4) {
+            const int64_t f = fs + (int64_t)tid * 4;
+            if (f >= end) continue;
+            int64_t sl = f / C;
+            int64_t e = f - sl * C;
+            if (!scalar && f + 4 <= end && e + 4 <= C) {
+                const int64_t at = (sl * L + b) * C + e;
+                const int gs = (int)(sl % L);
+                f32x4_a4 acc = TIDE_LD(gbl<f32x4_a4>(ptrs.inbox[gs] + at));
+                constexpr int kMUnroll = MT > 0 ? MT : 1;
+#pragma unroll kMUnroll
+                for (int c = 1; c < M; ++c) {
+                    const int g = gs - c < 0 ? gs - c + L : gs - c;
+                    const f32x4_a4 v = TIDE_LD(gbl<f32x4_a4>(ptrs.inbox[g] + at));
+                    acc = acc + v;
+                }
+                TIDE_GLOBAL f32x4_a4* dst = gbl_mut<f32x4_a4>(shard + f);
+                if (accumulate) acc = *dst + acc;
+                TIDE_ST(acc, dst);
+            } else {
+#pragma unroll 1
+                for (int k = 0; k < 4 && f + k < end; ++k) {
+                    const int64_t ff = f + k;
+                    sl = ff / C;
+                    e = ff - sl * C;
+                    const int64_t at = (sl * L + b) * C + e;
+                    const int gs = (int)(sl % L);
+                    float acc = gbl<float>(ptrs.inbox[gs])[at];
+#pragma unroll 1
+                    for (int c = 1; c < M; ++c) {
+                        const int g = gs - c < 0 ? gs - c + L : gs - c;
+                        acc = acc + gbl<float>(ptrs.inbox[g])[at];
+                    }
+                    TIDE_GLOBAL float* dst = gbl_mut<float>(shard + ff);
+                    *dst = accumulate ? *dst + acc : acc;
+                }
+            }
+        }
+    }
+}
+
+template <int MT>
+hipError_t launch_landing_t(int M, int grid, int threads, size_t lds, hipStream_t stream,
+                            const LandingPtrs& ptrs, int32_t L, int64_t S, int64_t C,
+                            int64_t tiles_per_shard, int64_t tile_lo, int64_t tile_hi,
+                            int32_t accumulate, int32_t scalar) {
+    LandingPtrs p = ptrs;
+    int32_t Mrt = M;
+    void* args[] = {&p, &L, &Mrt, &S, &C, &tiles_per_shard, &tile_lo, &tile_hi, &accumulate,
+                    &scalar};
+    const void* fn = threads == kFatThreads
+                         ? reinterpret_cast<const void*>(&landing_kernel<MT, kFatThreads>)
+                         : reinterpret_cast<const void*>(&landing_kernel<MT, kThreads>);
+    return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, lds, stream);
+}
+
 template <int LT>
 hipError_t launch_reduce_t(int L, int grid, int threads, size_t lds, hipStream_t stream,
                            const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
@@ -490,6 +565,56 @@ hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
                          ? reinterpret_cast<const void*>(&place_kernel<kFatThreads>)
                          : reinterpret_cast<const void*>(&place_kernel<kThreads>);
     return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, lds, stream);
+}
+
+hipError_t launch_landing(int M, int grid, int threads, size_t lds, hipStream_t stream,
+                          const LandingPtrs& ptrs, int32_t L, int64_t S, int64_t C,
+                          int64_t tiles_per_shard, int64_t tile_lo, int64_t tile_hi,
+                          int32_t accumulate, int32_t scalar) {
+#define TIDE_LANDING_CASE(n)                                                                  \
+    case n:                                                                                   \
+        return launch_landing_t<n>(M, grid, threads, lds, stream, ptrs, L, S, C,             \
+                                   tiles_per_shard, tile_lo, tile_hi, accumulate, scalar);
+    switch (M) {
+        TIDE_LANDING_CASE(1)
+        TIDE_LANDING_CASE(2)
+        TIDE_LANDING_CASE(3)
+        TIDE_LANDING_CASE(4)
+        TIDE_LANDING_CASE(5)
+        TIDE_LANDING_CASE(6)
+        TIDE_LANDING_CASE(7)
+        TIDE_LANDING_CASE(8)
+        default:
+            return launch_landing_t<0>(M, grid, threads, lds, stream, ptrs, L, S, C,
+                                       tiles_per_shard, tile_lo, tile_hi, accumulate, scalar);
+    }
+#undef TIDE_LANDING_CASE
+}
+
+hipError_t allow_dynamic_lds_landing(int M, size_t lds) {
+#define TIDE_LDS_LANDING_CASE(n)                                                              \
+    case n: {                                                                                 \
+        hipError_t e = hipFuncSetAttribute(                                                   \
+            reinterpret_cast<const void*>(&landing_kernel<n, kFatThreads>),                   \
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                            \
+        if (e != hipSuccess) return e;                                                        \
+        return hipFuncSetAttribute(reinterpret_cast<const void*>(&landing_kernel<n, kThreads>), \
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);     \
+    }
+    switch (M) {
+        TIDE_LDS_LANDING_CASE(1)
+        TIDE_LDS_LANDING_CASE(2)
+        TIDE_LDS_LANDING_CASE(3)
+        TIDE_LDS_LANDING_CASE(4)
+        TIDE_LDS_LANDING_CASE(5)
+        TIDE_LDS_LANDING_CASE(6)
+        TIDE_LDS_LANDING_CASE(7)
+        TIDE_LDS_LANDING_CASE(8)
+        TIDE_LDS_LANDING_CASE(0)
+        default:
+            return allow_dynamic_lds_landing(0, lds);
+    }
+#undef TIDE_LDS_LANDING_CASE
 }
 
 hipError_t allow_dynamic_lds(int L, size_t lds) {

@@ -410,6 +410,11 @@ struct Range {
     int who;
 };
 
+// Devices on which the landing kernels were opted in to the budgeted LDS
+// reservation (bit M, or bit 0 for the runtime-M kernel).
+std::mutex g_landing_lds_mu;
+uint64_t g_landing_lds_done[64] = {};
+
 bool overlaps(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
 
 // The run of tiles of each launch and the grid it uses.
@@ -747,6 +752,107 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* sh
         });
         tide_status st2 = release_slot(ds, slot, stream);
         return st != TIDE_OK ? st : st2;
+    } catch (const std::bad_alloc&) {
+        return fail(TIDE_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return fail(TIDE_ERR_INVALID_ARG, "unexpected exception");
+    }
+}
+
+tide_status tide_latin_square(int32_t M, int32_t L, int32_t dst_node, int32_t src_node, int32_t* c,
+                              int32_t* slice_of_src_gpu, int32_t* dst_gpu_of_slice) {
+    if (M < 1 || L < 1) return fail(TIDE_ERR_INVALID_ARG, "M = %d, L = %d must be >= 1", M, L);
+    if (dst_node < 0 || dst_node >= M || src_node < 0 || src_node >= M)
+        return fail(TIDE_ERR_INVALID_ARG, "nodes %d, %d outside [0, %d)", dst_node, src_node, M);
+    const int32_t cc = ((dst_node - src_node) % M + M) % M;   // relative index; destination is 0
+    if (c) *c = cc;
+    for (int32_t j = 0; j < L; ++j) {
+        if (slice_of_src_gpu) slice_of_src_gpu[j] = (j + cc) % L;
+        if (dst_gpu_of_slice) dst_gpu_of_slice[j] = ((j - cc) % L + L) % L;
+    }
+    return TIDE_OK;
+}
+
+tide_status tide_landing_sum_fp32(int32_t L, int32_t M, int64_t S, const float* const* inboxes,
+                                  float* const* shards, int32_t accumulate, void* stream_v,
+                                  const tide_launch* launch) {
+    try {
+        if (L < 1 || L > kMaxLanding)
+            return fail(TIDE_ERR_INVALID_ARG, "L = %d not in [1, %d]", L, kMaxLanding);
+        if (M < 1 || M > L) return fail(TIDE_ERR_INVALID_ARG, "M = %d not in [1, L = %d]", M, L);
+        if (S < 0) return fail(TIDE_ERR_INVALID_ARG, "S = %lld < 0", (long long)S);
+        if (accumulate != 0 && accumulate != 1)
+            return fail(TIDE_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+        tide_launch l{};
+        if (launch) l = *launch;
+        if (l.rank_begin != 0 || l.rank_end != 0)
+            return fail(TIDE_ERR_INVALID_ARG, "rank_begin / rank_end do not apply to the landing sum");
+        if (l.mode != TIDE_LAUNCH_FULL && l.mode != TIDE_LAUNCH_BUDGETED)
+            return fail(TIDE_ERR_INVALID_ARG, "launch.mode %d is not FULL (0) or BUDGETED (1)", l.mode);
+        if (l.reduce_blocks < 0 || l.place_blocks < 0 || l.max_launch_us < 0)
+            return fail(TIDE_ERR_INVALID_ARG, "negative launch budget");
+        if (l.reserved != 0 || (l.flags & ~TIDE_FLAG_SCALAR_PATH) != 0)
+            return fail(TIDE_ERR_INVALID_ARG, "unknown launch flags 0x%x", l.flags);
+        if (l.place_blocks == 0) l.place_blocks = kDefaultPlaceBlocks;
+        if (l.max_launch_us == 0) l.max_launch_us = kDefaultMaxLaunchUs;
+        if (S == 0) return TIDE_OK;
+        if (!inboxes || !shards) return fail(TIDE_ERR_INVALID_ARG, "inboxes / shards is NULL");
+        const int64_t C = S / L + (S % L != 0);
+        int64_t inbox_elems, bytes;
+        if (!mul_ok((int64_t)L * L, C, &inbox_elems) || !mul_ok(inbox_elems, 4, &bytes))
+            return fail(TIDE_ERR_OVERFLOW, "inbox size overflows int64");
+        LandingPtrs ptrs{};
+        std::vector<Range> rd, wr;
+        for (int32_t g = 0; g < L; ++g) {
+            const uintptr_t a = reinterpret_cast<uintptr_t>(inboxes[g]);
+            const uintptr_t w = reinterpret_cast<uintptr_t>(shards[g]);
+            if (!a || !w) return fail(TIDE_ERR_INVALID_ARG, "inboxes[%d] or shards[%d] is NULL", g, g);
+            if ((a & 3) || (w & 3)) return fail(TIDE_ERR_ALIGNMENT, "GPU %d: pointer not 4-byte aligned", g);
+            ptrs.inbox[g] = inboxes[g];
+            ptrs.shard[g] = shards[g];
+            rd.push_back(Range{a, a + (uintptr_t)bytes, g});
+            wr.push_back(Range{w, w + (uintptr_t)S * 4, g});
+        }
+        std::sort(wr.begin(), wr.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+        for (size_t i = 1; i < wr.size(); ++i)
+            if (wr[i].lo < wr[i - 1].hi)
+                return fail(TIDE_ERR_INVALID_ARG, "shards[%d] and shards[%d] overlap", wr[i - 1].who, wr[i].who);
+        for (const Range& w : wr)
+            for (const Range& r : rd)
+                if (overlaps(w, r))
+                    return fail(TIDE_ERR_INVALID_ARG, "shards[%d] overlaps inboxes[%d]", w.who, r.who);
+        hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+        const int64_t tiles_per_shard = (S + kLandTile - 1) / kLandTile;
+        const int64_t ntiles = tiles_per_shard * L;
+        const int32_t scalar = (l.flags & TIDE_FLAG_SCALAR_PATH) ? 1 : 0;
+        if (l.mode == TIDE_LAUNCH_FULL) {
+            const int grid = (int)std::min<int64_t>(ntiles, kFullGridCap);
+            TIDE_HIP_TRY(launch_landing(M, grid, kThreads, 0, stream, ptrs, L, S, C,
+                                        tiles_per_shard, 0, ntiles, accumulate, scalar));
+            return TIDE_OK;
+        }
+        if (kBudgetLds > 0) {
+            std::lock_guard<std::mutex> lock(g_landing_lds_mu);
+            int dev = 0;
+            tide_status st = stream_device(stream, &dev);
+            if (st != TIDE_OK) return st;
+            const int key = M <= 8 ? M : 0;
+            const uint64_t bit = (uint64_t)1 << key;
+            if (dev < 64 && !(g_landing_lds_done[dev] & bit)) {
+                TIDE_HIP_TRY(allow_dynamic_lds_landing(key, kBudgetLds));
+                g_landing_lds_done[dev] |= bit;
+            }
+        }
+        const int64_t tile_b = kLandTile * (4 * (int64_t)M + 4 + 4 * accumulate);
+        const int64_t per_block = std::max<int64_t>(1, (int64_t)l.max_launch_us * kWgBytesPerUs / tile_b);
+        const int64_t per_launch = (int64_t)l.place_blocks * per_block;
+        for (int64_t lo = 0; lo < ntiles; lo += per_launch) {
+            const int64_t hi = std::min(ntiles, lo + per_launch);
+            const int grid = (int)std::min<int64_t>(l.place_blocks, hi - lo);
+            TIDE_HIP_TRY(launch_landing(M, grid, kBudgetThreads, kBudgetLds, stream, ptrs, L, S, C,
+                                        tiles_per_shard, lo, hi, accumulate, scalar));
+        }
+        return TIDE_OK;
     } catch (const std::bad_alloc&) {
         return fail(TIDE_ERR_NO_MEMORY, "host allocation failed");
     } catch (...) {

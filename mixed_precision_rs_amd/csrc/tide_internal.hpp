@@ -78,6 +78,20 @@ hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
                         const uint32_t* flags, const uint16_t* shards, int64_t shard_stride,
                         int64_t shard_elems, int32_t first_rank, int32_t nranks);
 
+// Level-2 landing sum (kernels.hip). The node's inbox and shard pointers travel
+// in the kernel arguments (at most kMaxLanding GPUs per node).
+constexpr int kMaxLanding = 64;
+constexpr int64_t kLandTile = 2 * kThreads * 4;   // elements per landing tile (4 per thread per step)
+struct LandingPtrs {
+    const float* inbox[kMaxLanding];
+    float* shard[kMaxLanding];
+};
+hipError_t launch_landing(int M, int grid, int threads, size_t lds, hipStream_t stream,
+                          const LandingPtrs& ptrs, int32_t L, int64_t S, int64_t C,
+                          int64_t tiles_per_shard, int64_t tile_lo, int64_t tile_hi,
+                          int32_t accumulate, int32_t scalar);
+hipError_t allow_dynamic_lds_landing(int M, size_t lds);
+
 // Allow `lds` bytes of dynamic LDS on every kernel variant for L contributors.
 hipError_t allow_dynamic_lds(int L, size_t lds);
 

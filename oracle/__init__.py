@@ -48,9 +48,16 @@ class Oracle:
                                                      _U16P, ctypes.c_int64, ctypes.c_int32,
                                                      ctypes.POINTER(_U16P), ctypes.c_int32,
                                                      ctypes.c_int32]
+        lib.oracle_landing_sum.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                           ctypes.POINTER(_F32P), ctypes.POINTER(_F32P),
+                                           ctypes.c_int32]
+        lib.oracle_latin_square.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                            ctypes.POINTER(ctypes.c_int32),
+                                            ctypes.POINTER(ctypes.c_int32)]
         for f in ("oracle_layout", "oracle_piece_start", "oracle_reduce_scatter",
                   "oracle_piece_rows", "oracle_reduce_piece", "oracle_allgather_place",
-                  "oracle_allgather_place_stage"):
+                  "oracle_allgather_place_stage", "oracle_landing_sum", "oracle_latin_square"):
             getattr(lib, f).restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
@@ -197,6 +204,31 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_allgather_place_stage rejected its arguments")
         return params
+
+
+    def landing_sum(self, L, M, S, inboxes: List[np.ndarray], shards=None, accumulate=False):
+        """inboxes[g]: float32 arrays of L*L*ceil(S/L); returns the L shards."""
+        ib = [np.ascontiguousarray(a, dtype=np.float32) for a in inboxes]
+        if shards is None:
+            shards = [np.zeros(S, np.float32) for _ in range(L)]
+        ip = (_F32P * L)(*[self._p(a, _F32P) for a in ib])
+        sp = (_F32P * L)(*[self._p(a, _F32P) for a in shards])
+        t0 = time.perf_counter()
+        rc = self.lib.oracle_landing_sum(L, M, S, ip, sp, 1 if accumulate else 0)
+        self.last_call_s = time.perf_counter() - t0
+        if rc != 0:
+            raise ValueError("oracle_landing_sum rejected its arguments")
+        return shards
+
+    def latin_square(self, M, L, dst, src):
+        """(c, slice handled by each source GPU, destination GPU of each slice)."""
+        c = ctypes.c_int32()
+        a = (ctypes.c_int32 * L)()
+        b = (ctypes.c_int32 * L)()
+        rc = self.lib.oracle_latin_square(M, L, dst, src, ctypes.byref(c), a, b)
+        if rc != 0:
+            raise ValueError("oracle_latin_square rejected its arguments")
+        return int(c.value), list(a), list(b)
 
 
 _default: Optional[Oracle] = None

@@ -218,12 +218,17 @@ int oracle_reduce_piece(int32_t P, const int64_t *rows, const int64_t *row_len, 
                         float *dst)
 {
     int64_t first = 0, n = 0;
+    struct layout lay;
     int rc = oracle_piece_rows(P, rows, row_len, N, r, p, &first, &n);
     if (rc != 0 || L < 1)
         return -1;
+    if (layout_alloc(&lay, P, rows, row_len, N) != 0) {
+        layout_free(&lay);
+        return -1;
+    }
     {
         const int64_t K = row_len[p];
-        const int64_t Rp = rows[p] / N + (rows[p] % N != 0);
+        const int64_t Rp = lay.R[p];                       /* the layout's rows per rank */
         for (int64_t i = 0; i < Rp; ++i) {
             for (int64_t k = 0; k < K; ++k) {
                 float v;
@@ -238,6 +243,7 @@ int oracle_reduce_piece(int32_t P, const int64_t *rows, const int64_t *row_len, 
             }
         }
     }
+    layout_free(&lay);
     return 0;
 }
 
@@ -318,5 +324,70 @@ int oracle_allgather_place_stage(int32_t P, const int64_t *rows, const int64_t *
         }
     }
     layout_free(&lay);
+    return 0;
+}
+
+/*
+ * Level 2 of the reduce-scatter on one destination node: the landing sum
+ * (page 1 "Reduce-scatter: two levels of addition, the last one done by
+ * NVSwitch"; page 3 Figure 6(b)).
+ *
+ * The node's L GPUs finally hold one fp32 shard of S elements each. Every
+ * source node's fp32 partial of this node's part is cut into L slices; slice
+ * s is the s-th chunk of C = ceil(S / L) elements of every local shard, one
+ * block per destination GPU b (block b of slice s = elements s*C .. of GPU b's
+ * shard; the last chunk may be shorter or empty). A source with relative
+ * index c = (destination - source) mod M (the destination itself is 0) sends
+ * slice s to destination GPU (s - c) mod L: the Latin-square seating, so that
+ * the M copies of a slice sit on M different GPUs at the same address. Each
+ * destination GPU g has an inbox of L slots of L blocks of C elements; slot s,
+ * block b is at inbox_g[(s * L + b) * C]. M <= L sources fill the slots.
+ *
+ * GPU b's shard element s * C + e is the fp32 sum over c = 0..M-1 of
+ * inbox_{(s - c) mod L}[(s * L + b) * C + e], taken here as a left fold in
+ * the order c = 0, 1, ... (the switch's own order is not stated); with
+ * accumulate != 0 the sum is added to the shard's current value.
+ *   inboxes[g]  destination GPU g's inbox (L * L * C floats)
+ *   shards[b]   destination GPU b's shard (S floats)
+ */
+int oracle_landing_sum(int32_t L, int32_t M, int64_t S, const float *const *inboxes,
+                       float *const *shards, int32_t accumulate)
+{
+    if (L < 1 || M < 1 || M > L || S < 0)
+        return -1;
+    {
+        const int64_t C = S / L + (S % L != 0);            /* ceil(S / L) */
+        for (int32_t b = 0; b < L; ++b) {
+            for (int64_t f = 0; f < S; ++f) {
+                const int64_t s = f / C, e = f % C;
+                const int64_t at = (s * L + b) * C + e;        /* same offset in every inbox */
+                float v = inboxes[(int32_t)(s % L)][at];       /* c = 0: GPU s mod L */
+                for (int32_t c = 1; c < M; ++c) {
+                    const int32_t g = (int32_t)(((s - c) % L + L) % L);
+                    v = v + inboxes[g][at];
+                }
+                shards[b][f] = accumulate ? shards[b][f] + v : v;
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * The Latin-square seating for one (destination, source) node pair: the
+ * source's relative index c = (dst - src) mod M; source GPU j handles slice
+ * (j + c) mod L; slice s from that source lands on destination GPU
+ * (s - c) mod L (page 1, the worked 4-GPU example; page 3 Figure 6(b)).
+ */
+int oracle_latin_square(int32_t M, int32_t L, int32_t dst, int32_t src, int32_t *c,
+                        int32_t *slice_of_src_gpu, int32_t *dst_gpu_of_slice)
+{
+    if (M < 1 || L < 1 || dst < 0 || dst >= M || src < 0 || src >= M)
+        return -1;
+    *c = ((dst - src) % M + M) % M;
+    for (int32_t j = 0; j < L; ++j)
+        slice_of_src_gpu[j] = (j + *c) % L;
+    for (int32_t s = 0; s < L; ++s)
+        dst_gpu_of_slice[s] = ((s - *c) % L + L) % L;
     return 0;
 }

@@ -10,6 +10,7 @@ import os
 import pytest
 
 import pins
+import pins_landing
 from oracle import Oracle
 from oracle import build as obuild
 
@@ -17,6 +18,26 @@ RS_FOLD = (
     "v = widen_bf16(grads[0 * (int64_t)P + p][t * K + k]);\n"
     "                        for (int32_t c = 1; c < L; ++c)\n"
     "                            v = v + widen_bf16(grads[(int64_t)c * P + p][t * K + k]);")
+
+LANDING_MUTANTS = {
+    # slice from index c seated on GPU (s + c) instead of (s - c)
+    "landing_wrong_seat": ("const int32_t g = (int32_t)(((s - c) % L + L) % L);",
+                           "const int32_t g = (int32_t)(((s + c) % L + L) % L);"),
+    # the last source dropped
+    "landing_drop_source": ("for (int32_t c = 1; c < M; ++c) {\n                    const int32_t g",
+                            "for (int32_t c = 1; c < M - 1; ++c) {\n                    const int32_t g"),
+    # slot and block swapped in the inbox offset
+    "landing_block_slot_swapped": ("const int64_t at = (s * L + b) * C + e;",
+                                   "const int64_t at = (b * L + s) * C + e;"),
+    # every destination GPU reads block 0 of the slice
+    "landing_ignores_block": ("const int64_t at = (s * L + b) * C + e;",
+                              "const int64_t at = (s * L + 0 * b) * C + e;"),
+    # the accumulate flag ignored
+    "landing_accumulate_ignored": ("shards[b][f] = accumulate ? shards[b][f] + v : v;",
+                                   "shards[b][f] = v;"),
+    # Latin square with c = (src - dst) mod M
+    "latin_sign": ("*c = ((dst - src) % M + M) % M;", "*c = ((src - dst) % M + M) % M;"),
+}
 
 MUTANTS = {
     # the fold drops the last contributor
@@ -73,12 +94,12 @@ def _build_mutant(tmp_path, name, old, new):
     return Oracle(lib)
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
+@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(LANDING_MUTANTS))
 def test_pins_catch_mutant(tmp_path, name):
-    old, new = MUTANTS[name]
+    old, new = MUTANTS[name] if name in MUTANTS else LANDING_MUTANTS[name]
     orc = _build_mutant(tmp_path, name, old, new)
     caught = []
-    for pin in pins.ALL_PINS:
+    for pin in pins.ALL_PINS + pins_landing.ALL_PINS:
         try:
             pin(orc)
         except (AssertionError, ValueError, IndexError):

@@ -3,9 +3,10 @@ import numpy as np
 import pytest
 
 import pins
+import pins_landing
 
 
-@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("pin", pins.ALL_PINS + pins_landing.ALL_PINS, ids=lambda f: f.__name__)
 def test_pin(orc, pin):
     pin(orc)
 
