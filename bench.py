@@ -196,6 +196,56 @@ def victim_slowdown(torch, tide, plan, grads, out, shards, params, launch, reps=
             "gemms_counted_are": res[0][3] + " the collective window"}
 
 
+def stock_fsdp2(torch, tide, plan, cfg, grads, shards, out, p_tab, iters=3):
+    """The stock FSDP2 path on one GPU, for comparison: every contributor's
+    gradients packed with torch._chunk_cat into an fp32 rank-major buffer (the
+    pack FSDP2 runs before its reduce-scatter), the L packed buffers summed in
+    contributor order, and the all-gather's rank-major output copied out with
+    split_with_sizes_copy into padded parameter storage. Returns times, the
+    bytes that path moves, and whether its shards equal ours bit for bit."""
+    N, L, S = cfg.N, cfg.L, plan.S
+    valid = sum(t * k for t, k in cfg.shapes)
+    acc = torch.empty((N, S), dtype=torch.float32, device="cuda")
+    tmp = torch.empty((N, S), dtype=torch.float32, device="cuda")
+
+    def rs():
+        torch._chunk_cat(grads[0], dim=0, num_chunks=N, out=acc)
+        for c in range(1, L):
+            torch._chunk_cat(grads[c], dim=0, num_chunks=N, out=tmp)
+            acc.add_(tmp)
+
+    sizes = [-(-t // N) * k for t, k in cfg.shapes]
+    padded = [torch.empty((N, sz), dtype=torch.bfloat16, device="cuda") for sz in sizes]
+    src = shards.view(N, S)
+
+    def ag():
+        torch.split_with_sizes_copy(src, sizes, dim=1, out=padded)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+    rs_ms, ag_ms = timed(rs), timed(ag)
+    tide.reduce_scatter_bf16_fp32(plan, tide.grads_table(plan, grads), out)
+    torch.cuda.synchronize()
+    exact = bool(torch.equal(acc.view(-1).view(torch.int32), out.view(torch.int32)))
+    # bytes: L packs (2 V read, 4 N S written) + (L - 1) adds (8 N S read, 4 N S written)
+    rs_bytes = L * (2 * valid + 4 * N * S) + (L - 1) * 12 * N * S
+    ag_bytes = 2 * N * S * 2
+    del acc, tmp, padded
+    torch.cuda.empty_cache()
+    return {"reduce_ms": round(rs_ms, 3), "placement_ms": round(ag_ms, 3),
+            "reduce_bytes": rs_bytes, "placement_bytes": ag_bytes,
+            "shards_equal_ours_bit_for_bit": exact}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,6 +258,8 @@ def main():
                     help="also time the SDMA placement engine and a plain copy")
     ap.add_argument("--victim", action="store_true",
                     help="GEMM-victim slowdown, budgeted and full grid")
+    ap.add_argument("--stock", action="store_true",
+                    help="also time the stock FSDP2 path (chunk_cat pack + sum, split_with_sizes_copy)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-ranks", type=int, default=0, help="ranks in the CPU sample (0: all)")
     args = ap.parse_args()
@@ -330,6 +382,14 @@ def main():
         parts["plain_copy_GBps"] = round(copy_ceiling_gbps(torch), 1)
         log("bench: sdma placement %.3f ms, plain copy %.1f GB/s" % (sd, parts["plain_copy_GBps"]))
 
+    stock = None
+    if args.stock:
+        log("bench: stock FSDP2 path")
+        stock = stock_fsdp2(torch, tide, plan, cfg, grads, shards, out, p_tab)
+        stock["reduce_speedup_of_ours"] = round(stock["reduce_ms"] / rs_avg, 2)
+        stock["placement_speedup_of_ours"] = round(stock["placement_ms"] / ag_avg, 2)
+        log("bench: stock %s" % json.dumps(stock))
+
     victim = None
     if args.victim:
         log("bench: GEMM victim, budgeted")
@@ -375,6 +435,8 @@ def main():
     }
     if victim is not None:
         line["victim_gemm_256x8192x8192"] = victim
+    if stock is not None:
+        line["stock_fsdp2_same_gpu"] = stock
     print(json.dumps(line), flush=True)
 
 
