@@ -55,9 +55,14 @@ class Oracle:
                                             ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
                                             ctypes.POINTER(ctypes.c_int32),
                                             ctypes.POINTER(ctypes.c_int32)]
+        lib.oracle_stage_grads.argtypes = [ctypes.c_int32, _I64P, _I64P, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.POINTER(_U16P),
+                                           ctypes.POINTER(_U16P)]
         for f in ("oracle_layout", "oracle_piece_start", "oracle_reduce_scatter",
                   "oracle_piece_rows", "oracle_reduce_piece", "oracle_allgather_place",
-                  "oracle_allgather_place_stage", "oracle_landing_sum", "oracle_latin_square"):
+                  "oracle_allgather_place_stage", "oracle_landing_sum", "oracle_latin_square",
+                  "oracle_stage_grads"):
             getattr(lib, f).restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
@@ -219,6 +224,31 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_landing_sum rejected its arguments")
         return shards
+
+    def stage_grads(self, shapes, N, L, grads, slots: Optional[List[np.ndarray]] = None,
+                    rank_range: Optional[Tuple[int, int]] = None):
+        """Slot-Reuse staging of contributors' bf16 gradients (grads[c][p], uint16
+        bits) into L slots of N * S elements (zero-filled when not given);
+        returns the slots. rank_range limits the copy to those ranks' rows."""
+        rows, rlen = self._shape_arrays(shapes)
+        P = len(shapes)
+        S = self.layout(shapes, N)["S"]
+        if slots is None:
+            slots = [np.zeros(N * S, np.uint16) for _ in range(L)]
+        if len(slots) != L or any(a.dtype != np.uint16 or a.size < N * S for a in slots):
+            raise ValueError("stage_grads needs L uint16 slots of at least N * S elements")
+        arrs = [np.ascontiguousarray(grads[c][p], dtype=np.uint16)
+                for c in range(L) for p in range(P)]
+        gp = (_U16P * max(len(arrs), 1))(*[self._p(a, _U16P) for a in arrs])
+        sp = (_U16P * L)(*[self._p(a, _U16P) for a in slots])
+        rb, re = rank_range if rank_range is not None else (0, N)
+        t0 = time.perf_counter()
+        rc = self.lib.oracle_stage_grads(P, self._p(rows, _I64P), self._p(rlen, _I64P), N, L,
+                                         rb, re, gp, sp)
+        self.last_call_s = time.perf_counter() - t0
+        if rc != 0:
+            raise ValueError("oracle_stage_grads rejected its arguments")
+        return slots
 
     def latin_square(self, M, L, dst, src):
         """(c, slice handled by each source GPU, destination GPU of each slice)."""

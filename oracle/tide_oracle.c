@@ -391,3 +391,40 @@ int oracle_latin_square(int32_t M, int32_t L, int32_t dst, int32_t src, int32_t 
         dst_gpu_of_slice[s] = ((s - *c) % L + L) % L;
     return 0;
 }
+
+/*
+ * Slot-Reuse staging (page 1 "When gradients can be freed also needs
+ * planning"; page 2 "What shipped"; page 3 abstract and Figure 7): each
+ * contributor's bf16 gradients are copied into a vacated all-gather slot so
+ * that the gradient storage can be freed; the reduce then reads the slot.
+ * Inside slot c, parameter p's T_p x K_p gradient is placed at element
+ * N * o_p, the group's parameter-major layout (each parameter padded to
+ * N * R_p rows; the page-1 worked example's "9 MB" address). Only the rows
+ * of ranks [rank_begin, rank_end) are copied (rank r holds rows
+ * r * R_p .. r * R_p + R_p - 1); padding rows are never written.
+ * slots[c] holds N * S elements.
+ */
+int oracle_stage_grads(int32_t P, const int64_t *rows, const int64_t *row_len, int32_t N,
+                       int32_t L, int32_t rank_begin, int32_t rank_end,
+                       const uint16_t *const *grads, uint16_t *const *slots)
+{
+    struct layout lay;
+    int rc = layout_alloc(&lay, P, rows, row_len, N);
+    if (rc != 0 || L < 1 || rank_begin < 0 || rank_end > N || rank_begin > rank_end) {
+        layout_free(&lay);
+        return -1;
+    }
+    for (int32_t c = 0; c < L; ++c)
+        for (int32_t p = 0; p < P; ++p)
+            for (int32_t r = rank_begin; r < rank_end; ++r) {
+                /* rank r holds rows [r R_p, r R_p + R_p), clipped to the true rows */
+                const int64_t t0 = (int64_t)r * lay.R[p];
+                const int64_t t1 = t0 + lay.R[p] < rows[p] ? t0 + lay.R[p] : rows[p];
+                for (int64_t t = t0; t < t1; ++t)
+                    for (int64_t k = 0; k < row_len[p]; ++k)
+                        slots[c][(int64_t)N * lay.o[p] + t * row_len[p] + k] =
+                            grads[(int64_t)c * P + p][t * row_len[p] + k];
+            }
+    layout_free(&lay);
+    return 0;
+}

@@ -11,6 +11,7 @@ import pytest
 
 import pins
 import pins_landing
+import pins_stage
 from oracle import Oracle
 from oracle import build as obuild
 
@@ -37,6 +38,24 @@ LANDING_MUTANTS = {
                                    "shards[b][f] = v;"),
     # Latin square with c = (src - dst) mod M
     "latin_sign": ("*c = ((dst - src) % M + M) % M;", "*c = ((src - dst) % M + M) % M;"),
+}
+
+STAGE_MUTANTS = {
+    # staged at o_p (the rank-major offset) instead of N * o_p
+    "stage_offset_unscaled": ("slots[c][(int64_t)N * lay.o[p] + t * row_len[p] + k] =",
+                              "slots[c][lay.o[p] + t * row_len[p] + k] ="),
+    # slot c receives the next contributor's gradients
+    "stage_wrong_contributor": ("grads[(int64_t)c * P + p][t * row_len[p] + k];",
+                                "grads[(int64_t)((c + 1) % L) * P + p][t * row_len[p] + k];"),
+    # the last row of every parameter left out
+    "stage_drops_last_row": ("const int64_t t1 = t0 + lay.R[p] < rows[p] ? t0 + lay.R[p] : rows[p];",
+                             "const int64_t t1 = t0 + lay.R[p] < rows[p] - 1 ? t0 + lay.R[p] : rows[p] - 1;"),
+    # the rank range applied to rows as if R_p were 1
+    "stage_range_by_row": ("const int64_t t0 = (int64_t)r * lay.R[p];",
+                           "const int64_t t0 = (int64_t)r;"),
+    # rows transposed with columns (row-major order lost)
+    "stage_transposed": ("slots[c][(int64_t)N * lay.o[p] + t * row_len[p] + k] =",
+                         "slots[c][(int64_t)N * lay.o[p] + ((rows[p] == row_len[p]) ? k * rows[p] + t : t * row_len[p] + k)] ="),
 }
 
 MUTANTS = {
@@ -94,12 +113,15 @@ def _build_mutant(tmp_path, name, old, new):
     return Oracle(lib)
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(LANDING_MUTANTS))
+ALL_MUTANTS = {**MUTANTS, **LANDING_MUTANTS, **STAGE_MUTANTS}
+
+
+@pytest.mark.parametrize("name", sorted(ALL_MUTANTS))
 def test_pins_catch_mutant(tmp_path, name):
-    old, new = MUTANTS[name] if name in MUTANTS else LANDING_MUTANTS[name]
+    old, new = ALL_MUTANTS[name]
     orc = _build_mutant(tmp_path, name, old, new)
     caught = []
-    for pin in pins.ALL_PINS + pins_landing.ALL_PINS:
+    for pin in pins.ALL_PINS + pins_landing.ALL_PINS + pins_stage.ALL_PINS:
         try:
             pin(orc)
         except (AssertionError, ValueError, IndexError):

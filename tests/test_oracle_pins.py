@@ -4,9 +4,10 @@ import pytest
 
 import pins
 import pins_landing
+import pins_stage
 
 
-@pytest.mark.parametrize("pin", pins.ALL_PINS + pins_landing.ALL_PINS, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("pin", pins.ALL_PINS + pins_landing.ALL_PINS + pins_stage.ALL_PINS, ids=lambda f: f.__name__)
 def test_pin(orc, pin):
     pin(orc)
 
