@@ -12,7 +12,7 @@ value = algorithmic bytes per step / time per step:
 Prints ONE JSON line on stdout; progress goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--parts] [--victim] [--no-cpu-baseline]
+                  [--parts] [--victim] [--stock] [--slot-reuse] [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -246,6 +246,59 @@ def stock_fsdp2(torch, tide, plan, cfg, grads, shards, out, p_tab, iters=3):
             "shards_equal_ours_bit_for_bit": exact}
 
 
+def slot_reuse_parts(torch, tide, plan, cfg, g_tab, out, valid, in_place_ms, iters=5, chunks=8):
+    """Slot-Reuse mode on this group: the staging copy of the L contributors'
+    gradients into vacated slots (kernel and runtime-copy engines), the reduce
+    reading the slots, and both together (whole group, and pipelined over
+    rank ranges), against the in-place reduce."""
+    n = cfg.N * plan.S
+    slots = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(cfg.L)]
+    s_tab = tide.slot_grads_table(plan, slots)
+    stage_bytes = 2 * cfg.L * valid * 2
+
+    def timed(fn, k=iters):
+        fn()
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        for _ in range(k):
+            fn()
+        e[1].record()
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / k
+
+    st_k = timed(lambda: tide.stage_grads_bf16(plan, g_tab, slots))
+    st_s = timed(lambda: tide.stage_grads_bf16(plan, g_tab, slots, engine="sdma"), 3)
+    rd = timed(lambda: tide.reduce_scatter_bf16_fp32(plan, s_tab, out))
+
+    def both():
+        tide.stage_grads_bf16(plan, g_tab, slots)
+        tide.reduce_scatter_bf16_fp32(plan, s_tab, out)
+    tot = timed(both)
+    bounds = [round(i * cfg.N / chunks) for i in range(chunks + 1)]
+    ranges = [(a, b) for a, b in zip(bounds, bounds[1:]) if b > a]
+    launches = [tide.Launch(rank_begin=a, rank_end=b) for a, b in ranges]
+
+    def piped():
+        for lc in launches:
+            tide.stage_grads_bf16(plan, g_tab, slots, launch=lc)
+            tide.reduce_scatter_bf16_fp32(plan, s_tab, out, launch=lc)
+    pip = timed(piped)
+    del slots, s_tab
+    torch.cuda.empty_cache()
+    return {"stage_kernel_ms": round(st_k, 4),
+            "stage_kernel_GBps": round(stage_bytes / (st_k / 1e3) / 1e9, 1),
+            "stage_runtime_copy_ms": round(st_s, 4),
+            "stage_runtime_copy_GBps": round(stage_bytes / (st_s / 1e3) / 1e9, 1),
+            "stage_bytes": stage_bytes,
+            "reduce_from_slots_ms": round(rd, 4),
+            "stage_plus_reduce_ms": round(tot, 4),
+            "stage_plus_reduce_pipelined_ms": round(pip, 4),
+            "pipeline_rank_ranges": len(ranges),
+            "in_place_reduce_ms": round(in_place_ms, 4),
+            "slot_reuse_over_in_place": round(tot / in_place_ms, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,6 +313,8 @@ def main():
                     help="GEMM-victim slowdown, budgeted and full grid")
     ap.add_argument("--stock", action="store_true",
                     help="also time the stock FSDP2 path (chunk_cat pack + sum, split_with_sizes_copy)")
+    ap.add_argument("--slot-reuse", action="store_true",
+                    help="also time the Slot-Reuse staging and the reduce reading the slots")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-ranks", type=int, default=0, help="ranks in the CPU sample (0: all)")
     args = ap.parse_args()
@@ -382,6 +437,12 @@ def main():
         parts["plain_copy_GBps"] = round(copy_ceiling_gbps(torch), 1)
         log("bench: sdma placement %.3f ms, plain copy %.1f GB/s" % (sd, parts["plain_copy_GBps"]))
 
+    slot = None
+    if args.slot_reuse:
+        log("bench: slot-reuse staging")
+        slot = slot_reuse_parts(torch, tide, plan, cfg, g_tab, out, valid, rs_avg)
+        log("bench: slot-reuse %s" % json.dumps(slot))
+
     stock = None
     if args.stock:
         log("bench: stock FSDP2 path")
@@ -437,6 +498,8 @@ def main():
         line["victim_gemm_256x8192x8192"] = victim
     if stock is not None:
         line["stock_fsdp2_same_gpu"] = stock
+    if slot is not None:
+        line["slot_reuse"] = slot
     print(json.dumps(line), flush=True)
 
 

@@ -177,6 +177,42 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* st
                                        uint16_t* const* params, void* stream, int32_t engine,
                                        const tide_launch* launch);
 
+/*
+ * Slot-Reuse staging (page 1 "When gradients can be freed also needs
+ * planning"; page 2 "What shipped"; page 3 abstract and Figure 7): copy each
+ * contributor's bf16 gradients into an all-gather slot that has just been
+ * vacated, so that the gradient storage can be released as soon as the copy
+ * has run; the level-1 reduce then reads the slot instead of the gradients.
+ *
+ *   grads:  L * P bf16 pointers, grads[c * P + p], as for
+ *           tide_reduce_scatter_bf16_fp32 (T_p x K_p row-major, 2-byte aligned).
+ *   slots:  L device pointers (2-byte aligned); slots[c] is contributor c's slot
+ *           of N * S bf16 elements, the size of the group's gathered
+ *           parameters. Parameter p goes to slots[c] + N * o_p, its place in the
+ *           group's parameter-major padded layout (tide_plan_map's param_major
+ *           at rank 0), rows in order; the padding rows after it are not
+ *           written. Pass grads'[c * P + p] = slots[c] + N * o_p to the reduce.
+ *   engine: TIDE_ENGINE_KERNEL: one copy kernel for all (c, p), 16-byte
+ *           accesses when every pointer of a parameter is 4-byte aligned;
+ *           TIDE_ENGINE_SDMA: one hipMemcpyAsync per (c, p) (the HIP runtime
+ *           may run device-to-device copies as its own blit kernels).
+ *   launch: rank_begin / rank_end restrict the copy to those ranks' rows (rank r
+ *           holds rows [r R_p, (r + 1) R_p)), so staging and the reduce can be
+ *           pipelined by rank range; FULL, or BUDGETED with place_blocks
+ *           workgroups per launch.
+ * Ordering: asynchronous on `stream`. The gradients may be released once work
+ * ordered after this call on `stream` may run (an event recorded after it, or
+ * a stream-ordered allocator's release on `stream`). The slot must not be
+ * refilled by the next all-gather before the reduce that reads it has run.
+ * The slots, and the gradient bytes read, are owned by the caller.
+ * Errors: INVALID_ARG (NULL pointer with work to do, slots overlapping one
+ * another or any gradient, engine not KERNEL / SDMA); ALIGNMENT (odd address);
+ * HIP (a launch or copy failed).
+ */
+tide_status tide_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* grads,
+                                  uint16_t* const* slots, void* stream, int32_t engine,
+                                  const tide_launch* launch);
+
 /* One round of node n's recursive-doubling all-gather schedule. */
 typedef struct tide_rd_step {
     int32_t round;        /* d = 0, 1, ... */
@@ -244,7 +280,8 @@ tide_status tide_latin_square(int32_t M, int32_t L, int32_t dst_node, int32_t sr
                               int32_t* slice_of_src_gpu, int32_t* dst_gpu_of_slice);
 
 /* Kernel launches a call with these options makes (op 0 = reduce-scatter,
- * 1 = placement with the kernel engine). Host-only. */
+ * 1 = placement with the kernel engine, 2 = Slot-Reuse staging with the
+ * kernel engine). Host-only. */
 tide_status tide_plan_launch_count(const tide_plan* plan, int32_t op, const tide_launch* launch,
                                    int64_t* launches);
 

@@ -26,6 +26,8 @@ from ._lib import (  # noqa: F401
     plan_create,
     rd_schedule,
     reduce_scatter_bf16_fp32,
+    slot_grads_table,
+    stage_grads_bf16,
     version,
 )
 

@@ -27,7 +27,7 @@ EXPORTS = ["tide_plan_create", "tide_plan_destroy", "tide_plan_dims", "tide_plan
            "tide_plan_map", "tide_reduce_scatter_bf16_fp32", "tide_allgather_place",
            "tide_plan_launch_count", "tide_status_string", "tide_last_error_detail",
            "tide_version", "tide_allgather_place_stage", "tide_rd_schedule",
-           "tide_landing_sum_fp32", "tide_latin_square"]
+           "tide_landing_sum_fp32", "tide_latin_square", "tide_stage_grads_bf16"]
 
 
 class TideError(RuntimeError):
@@ -103,6 +103,8 @@ def _load():
                                           ctypes.POINTER(Launch)]
     lib.tide_latin_square.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_int32, _I32P, _I32P, _I32P]
+    lib.tide_stage_grads_bf16.argtypes = [ctypes.c_void_p, _VPP, _VPP, ctypes.c_void_p,
+                                          ctypes.c_int32, ctypes.POINTER(Launch)]
     lib.tide_status_string.argtypes = [ctypes.c_int]
     lib.tide_status_string.restype = ctypes.c_char_p
     lib.tide_last_error_detail.argtypes = []
@@ -112,7 +114,7 @@ def _load():
     for f in ("tide_plan_create", "tide_plan_dims", "tide_plan_param", "tide_plan_map",
               "tide_reduce_scatter_bf16_fp32", "tide_allgather_place", "tide_plan_launch_count",
               "tide_allgather_place_stage", "tide_rd_schedule", "tide_landing_sum_fp32",
-              "tide_latin_square"):
+              "tide_latin_square", "tide_stage_grads_bf16"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -232,10 +234,15 @@ def params_table(plan: Plan, params: Sequence[object]) -> PointerTable:
 
 
 def _record(tensors, stream_obj):
+    """Tell torch's caching allocator that the tensors are used on a
+    non-default stream, so their memory is not handed out again before that
+    stream's work on them has run (tensors are assumed to be allocated on the
+    default stream; a caller that allocates on other streams records them
+    itself)."""
     import torch
     if stream_obj is None:
         return
-    if stream_obj == torch.cuda.current_stream(stream_obj.device):
+    if stream_obj == torch.cuda.default_stream(stream_obj.device):
         return
     for t in tensors:
         if t is not None and not isinstance(t, int):
@@ -300,6 +307,38 @@ def allgather_place_stage(plan: Plan, stage, first_rank: int, params: Sequence[o
                                             ctypes.byref(launch) if launch is not None else None)
     _check(st, "tide_allgather_place_stage")
     _record(tab.refs + [stage], sobj)
+
+
+def stage_grads_bf16(plan: Plan, grads: Sequence[Sequence[object]], slots: Sequence[object],
+                     stream=None, engine: Union[int, str] = ENGINE_KERNEL,
+                     launch: Optional[Launch] = None) -> None:
+    """Slot-Reuse staging (tide_stage_grads_bf16): contributor c's gradients
+    grads[c][p] (or a grads_table()) are copied into slots[c], a bf16 device
+    tensor of N * S elements, at each parameter's offset N * o_p."""
+    tab = grads if isinstance(grads, PointerTable) else grads_table(plan, grads)
+    if tab.n != plan.L * plan.P:
+        raise ValueError("pointer table holds %d entries, expected L*P=%d" % (tab.n, plan.L * plan.P))
+    if len(slots) != plan.L:
+        raise ValueError("need L=%d slots" % plan.L)
+    if isinstance(engine, str):
+        engine = {"kernel": ENGINE_KERNEL, "sdma": ENGINE_SDMA}[engine]
+    sa = (ctypes.c_void_p * plan.L)(*[_ptr(t) for t in slots])
+    sh, sobj = _stream_handle(stream)
+    st = _load().tide_stage_grads_bf16(plan.handle, tab.arr, sa, sh, int(engine),
+                                       ctypes.byref(launch) if launch is not None else None)
+    _check(st, "tide_stage_grads_bf16")
+    _record(tab.refs + list(slots), sobj)
+
+
+def slot_grads_table(plan: Plan, slots: Sequence[object]) -> PointerTable:
+    """The reduce's L*P gradient table reading the staged slots: entry c*P + p
+    is slots[c] + N * o_p (addresses; keeps the slot tensors alive)."""
+    if len(slots) != plan.L:
+        raise ValueError("need L=%d slots" % plan.L)
+    offs = [plan.N * plan.param(p)[4] * 2 for p in range(plan.P)]
+    tab = PointerTable([_ptr(slots[c]) + offs[p] for c in range(plan.L) for p in range(plan.P)])
+    tab.refs = list(slots)
+    return tab
 
 
 def rd_schedule(M: int, node: int, piece_bytes: int = 0, head_bytes: int = 0):

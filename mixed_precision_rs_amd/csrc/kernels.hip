@@ -440,6 +440,56 @@ __global__ __launch_bounds__(NT) void place_kernel(
     }
 }
 
+// Slot-Reuse staging: dst[p][c][f] = src[p][c][f] for the launch's true
+// indices f of each parameter (a plain copy; dst is the parameter's place in
+// contributor c's slot). Work item t is tile t mod ntiles of the placement
+// tiling, for contributor t / ntiles. With kFlagVector every pointer of the
+// parameter is 4-byte aligned, so 16-byte accesses at 8-element steps are
+// dword aligned.
+template <int NT>
+__global__ __launch_bounds__(NT) void stage_kernel(
+    const TileRec* __restrict__ tiles, int64_t ntiles, int64_t tile_lo, int64_t tile_hi,
+    int32_t rb, int32_t re, const ParamDev* __restrict__ params,
+    const uint16_t* const* __restrict__ src, uint16_t* const* __restrict__ dst,
+    const uint32_t* __restrict__ flags, int32_t L) {
+    constexpr int kSubs = NT / kThreads;
+    const int sub = (int)threadIdx.x / kThreads;
+    const int tid = (int)threadIdx.x % kThreads;
+    for (int64_t t = tile_lo + (int64_t)blockIdx.x * kSubs + sub; t < tile_hi;
+         t += (int64_t)gridDim.x * kSubs) {
+        const int64_t c = t / ntiles;
+        const TileRec rec = tiles[t - c * ntiles];
+        const ParamDev pd = params[rec.p];
+        const uint16_t* s = src[(int64_t)rec.p * L + c];
+        uint16_t* d = dst[(int64_t)rec.p * L + c];
+        const bool vec = (flags[rec.p] & kFlagVector) != 0;
+        const int64_t lo = (int64_t)rb * pd.s;
+        const int64_t end = min(rec.idx0 + kAgTile, min((int64_t)re * pd.s, pd.valid));
+        for (int64_t g0 = rec.idx0; g0 < end; g0 += kAgUnroll * kStep) {
+            const int64_t f0 = g0 + (int64_t)tid * kVec;
+            if (vec && g0 >= lo && g0 + kAgUnroll * kStep <= end) {
+                u32x4_a4 w[kAgUnroll];
+#pragma unroll
+                for (int u = 0; u < kAgUnroll; ++u)
+                    w[u] = TIDE_LD(gbl<u32x4_a4>(s + f0 + (int64_t)u * kStep));
+#pragma unroll
+                for (int u = 0; u < kAgUnroll; ++u)
+                    TIDE_ST(w[u], gbl_mut<u32x4_a4>(d + f0 + (int64_t)u * kStep));
+            } else {
+                const TIDE_GLOBAL uint16_t* gs = gbl<uint16_t>(s);
+                TIDE_GLOBAL uint16_t* gd = gbl_mut<uint16_t>(d);
+#pragma unroll 1
+                for (int u = 0; u < kAgUnroll; ++u)
+#pragma unroll 1
+                    for (int e = 0; e < kVec; ++e) {
+                        const int64_t f = f0 + (int64_t)u * kStep + e;
+                        if (f >= lo && f < end) gd[f] = gs[f];
+                    }
+            }
+        }
+    }
+}
+
 // Level-2 landing sum: shard_b[f] = fold_c inbox_{(s - c) mod L}[(s L + b) C + e]
 // with s = f / C, e = f % C. All M inboxes are read at the same offset (the
 // Latin-square seating puts a slice's copies at the same address on M
@@ -567,6 +617,19 @@ hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
     return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, lds, stream);
 }
 
+hipError_t launch_stage(int grid, int threads, size_t lds, hipStream_t stream,
+                        const TileRec* tiles, int64_t ntiles, int64_t tile_lo, int64_t tile_hi,
+                        int32_t rb, int32_t re, const ParamDev* params,
+                        const uint16_t* const* src, uint16_t* const* dst, const uint32_t* flags,
+                        int32_t L) {
+    void* args[] = {&tiles, &ntiles, &tile_lo, &tile_hi, &rb, &re, &params, &src, &dst, &flags,
+                    &L};
+    const void* fn = threads == kFatThreads
+                         ? reinterpret_cast<const void*>(&stage_kernel<kFatThreads>)
+                         : reinterpret_cast<const void*>(&stage_kernel<kThreads>);
+    return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, lds, stream);
+}
+
 hipError_t launch_landing(int M, int grid, int threads, size_t lds, hipStream_t stream,
                           const LandingPtrs& ptrs, int32_t L, int64_t S, int64_t C,
                           int64_t tiles_per_shard, int64_t tile_lo, int64_t tile_hi,
@@ -620,7 +683,9 @@ hipError_t allow_dynamic_lds_landing(int M, size_t lds) {
 hipError_t allow_dynamic_lds(int L, size_t lds) {
     // Dynamic LDS beyond the default per-workgroup limit needs opting in per kernel.
     const void* fns[] = {reinterpret_cast<const void*>(&place_kernel<kFatThreads>),
-                         reinterpret_cast<const void*>(&place_kernel<kThreads>)};
+                         reinterpret_cast<const void*>(&place_kernel<kThreads>),
+                         reinterpret_cast<const void*>(&stage_kernel<kFatThreads>),
+                         reinterpret_cast<const void*>(&stage_kernel<kThreads>)};
     for (const void* f : fns) {
         hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;

@@ -1,7 +1,7 @@
 // Host side of the C ABI declared in include/tide.h: the layout planner
 // (page 3 Table 2 notation), argument validation, per-device tables, the
 // per-call pointer-table ring, and the launch policies (full grid,
-// CU-budgeted, SDMA placement).
+// CU-budgeted, runtime copies for the placement and the staging).
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
@@ -295,8 +295,8 @@ tide_status get_dev_state(const tide_plan* plan, int dev, DevState** out) {
     TIDE_HIP_TRY(hipMemcpy(ds->params, pd.data(), pd.size() * sizeof(ParamDev),
                            hipMemcpyHostToDevice));
     const size_t P = (size_t)std::max<int32_t>(plan->P, 1);
-    size_t cap = std::max(P * (size_t)plan->L * sizeof(void*), P * sizeof(void*)) +
-                 P * sizeof(uint32_t);
+    // Largest per-call table: the staging's 2 * P * L pointers plus P flags.
+    size_t cap = 2 * P * (size_t)plan->L * sizeof(void*) + P * sizeof(uint32_t);
     cap = (cap + 255) / 256 * 256;
     ds->slot_cap = cap;
     TIDE_HIP_TRY(hipMalloc(&ds->ring_dev, cap * kRingSlots));
@@ -438,7 +438,8 @@ tide_status for_each_launch(const tide_plan* plan, int op, const tide_launch& l,
         const int64_t hi = std::min(ntiles, lo + per_launch);
         const int grid = (int)std::min<int64_t>(grid_cap, hi - lo);
         hipError_t e = launch(grid, threads, lds, lo, hi);
-        if (e != hipSuccess) return hip_fail(e, op == 0 ? "reduce launch" : "place launch");
+        if (e != hipSuccess)
+            return hip_fail(e, op == 0 ? "reduce launch" : op == 1 ? "place launch" : "stage launch");
     }
     return TIDE_OK;
 }
@@ -534,11 +535,13 @@ tide_status tide_plan_launch_count(const tide_plan* plan, int32_t op, const tide
                                    int64_t* launches) {
     try {
         if (!plan || !launches) return fail(TIDE_ERR_INVALID_ARG, "NULL argument");
-        if (op != 0 && op != 1) return fail(TIDE_ERR_INVALID_ARG, "op %d not 0 or 1", op);
+        if (op < 0 || op > 2) return fail(TIDE_ERR_INVALID_ARG, "op %d not 0, 1 or 2", op);
         tide_launch l;
         tide_status st = resolve_launch(plan, launch, &l);
         if (st != TIDE_OK) return st;
-        const int64_t n = (int64_t)build_tiles(plan, op, l.rank_begin, l.rank_end).size();
+        // The staging walks the placement tiling once per contributor.
+        int64_t n = (int64_t)build_tiles(plan, op == 0 ? 0 : 1, l.rank_begin, l.rank_end).size();
+        if (op == 2) n *= plan->L;
         *launches = count_launches(plan, op, l, n);
         return TIDE_OK;
     } catch (const std::bad_alloc&) {
@@ -749,6 +752,114 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* sh
             return launch_place(grid, threads, lds, stream, tt->dev, lo, hi, l.rank_begin,
                                 l.rank_end, ds->params, dptrs, dflags, shards, shard_stride,
                                 shard_elems, first_rank, plan->N);
+        });
+        tide_status st2 = release_slot(ds, slot, stream);
+        return st != TIDE_OK ? st : st2;
+    } catch (const std::bad_alloc&) {
+        return fail(TIDE_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return fail(TIDE_ERR_INVALID_ARG, "unexpected exception");
+    }
+}
+
+tide_status tide_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* grads,
+                                  uint16_t* const* slots, void* stream_v, int32_t engine,
+                                  const tide_launch* launch) {
+    try {
+        if (!plan) return fail(TIDE_ERR_INVALID_ARG, "plan is NULL");
+        tide_launch l;
+        tide_status st = resolve_launch(plan, launch, &l);
+        if (st != TIDE_OK) return st;
+        if (engine != TIDE_ENGINE_KERNEL && engine != TIDE_ENGINE_SDMA)
+            return fail(TIDE_ERR_INVALID_ARG, "engine %d is not KERNEL (0) or SDMA (1)", engine);
+        const int32_t P = plan->P, L = plan->L;
+        const int64_t slot_elems = (int64_t)plan->N * plan->S;   // fits: checked at plan creation
+        if (plan->S == 0 || l.rank_end == l.rank_begin) return TIDE_OK;
+        if (!slots) return fail(TIDE_ERR_INVALID_ARG, "slots is NULL");
+        if (P > 0 && !grads) return fail(TIDE_ERR_INVALID_ARG, "grads is NULL");
+        std::vector<Range> sr;
+        for (int32_t c = 0; c < L; ++c) {
+            const uintptr_t a = reinterpret_cast<uintptr_t>(slots[c]);
+            if (!a) return fail(TIDE_ERR_INVALID_ARG, "slots[%d] is NULL", c);
+            if (a & 1) return fail(TIDE_ERR_ALIGNMENT, "slots[%d] is not 2-byte aligned", c);
+            sr.push_back(Range{a, a + (uintptr_t)slot_elems * 2, c});
+        }
+        {
+            std::vector<Range> sorted = sr;
+            std::sort(sorted.begin(), sorted.end(),
+                      [](const Range& a, const Range& b) { return a.lo < b.lo; });
+            for (size_t i = 1; i < sorted.size(); ++i)
+                if (sorted[i].lo < sorted[i - 1].hi)
+                    return fail(TIDE_ERR_INVALID_ARG, "slots[%d] and slots[%d] overlap",
+                                sorted[i - 1].who, sorted[i].who);
+        }
+        // Per-call table: P*L sources, P*L destinations (both parameter-major,
+        // p * L + c), then P flag words.
+        const size_t np = (size_t)P * L;
+        std::vector<char> table(2 * np * sizeof(void*) + (size_t)P * sizeof(uint32_t));
+        const uint16_t** ts = reinterpret_cast<const uint16_t**>(table.data());
+        uint16_t** td = reinterpret_cast<uint16_t**>(table.data() + np * sizeof(void*));
+        uint32_t* fl = reinterpret_cast<uint32_t*>(table.data() + 2 * np * sizeof(void*));
+        for (int32_t p = 0; p < P; ++p) {
+            const ParamInfo& q = plan->prm[p];
+            uint32_t f = (l.flags & TIDE_FLAG_SCALAR_PATH) ? 0u : kFlagVector;
+            for (int32_t c = 0; c < L; ++c) {
+                const uint16_t* g = grads[(size_t)c * P + p];
+                uint16_t* d = slots[c] + (int64_t)plan->N * q.o;
+                ts[(size_t)p * L + c] = g;
+                td[(size_t)p * L + c] = d;
+                if (q.valid == 0) continue;
+                if (!g) return fail(TIDE_ERR_INVALID_ARG, "grads[%d] (c=%d, p=%d) is NULL", c * P + p, c, p);
+                const uintptr_t a = reinterpret_cast<uintptr_t>(g);
+                if (a & 1) return fail(TIDE_ERR_ALIGNMENT, "grads[%d] is not 2-byte aligned", c * P + p);
+                if ((a | reinterpret_cast<uintptr_t>(d)) & 3) f = 0;
+                const Range in{a, a + (uintptr_t)q.valid * 2, c * P + p};
+                for (const Range& r : sr)
+                    if (overlaps(in, r))
+                        return fail(TIDE_ERR_INVALID_ARG, "grads[%d] overlaps slots[%d]", c * P + p, r.who);
+            }
+            fl[p] = f;
+        }
+        hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+        if (engine == TIDE_ENGINE_SDMA) {
+            // One contiguous copy per (contributor, parameter): the rows of
+            // ranks [rank_begin, rank_end) are one run on both sides.
+            for (int32_t p = 0; p < P; ++p) {
+                const ParamInfo& q = plan->prm[p];
+                const int64_t lo = (int64_t)l.rank_begin * q.s;
+                const int64_t hi = std::min((int64_t)l.rank_end * q.s, q.valid);
+                if (hi <= lo) continue;
+                for (int32_t c = 0; c < L; ++c)
+                    TIDE_HIP_TRY(hipMemcpyAsync(td[(size_t)p * L + c] + lo, ts[(size_t)p * L + c] + lo,
+                                                (size_t)(hi - lo) * 2, hipMemcpyDeviceToDevice, stream));
+            }
+            return TIDE_OK;
+        }
+        std::lock_guard<std::mutex> lock(plan->mu);
+        int dev;
+        st = stream_device(stream, &dev);
+        if (st != TIDE_OK) return st;
+        DevState* ds;
+        st = get_dev_state(plan, dev, &ds);
+        if (st != TIDE_OK) return st;
+        TileTable* tt;
+        st = get_tiles(plan, ds, 1, l.rank_begin, l.rank_end, &tt);
+        if (st != TIDE_OK) return st;
+        if (tt->count == 0) return TIDE_OK;
+        int slot;
+        st = stage_table(ds, table.data(), table.size(), stream, &slot);
+        if (st != TIDE_OK) return st;
+        char* base = static_cast<char*>(ds->slots[slot].dev);
+        const uint16_t* const* dsrc = reinterpret_cast<const uint16_t* const*>(base);
+        uint16_t* const* ddst = reinterpret_cast<uint16_t* const*>(base + np * sizeof(void*));
+        const uint32_t* dflags = reinterpret_cast<const uint32_t*>(base + 2 * np * sizeof(void*));
+        st = prepare_budget(ds, L, l);
+        if (st != TIDE_OK) return st;
+        const int64_t ntiles = tt->count;
+        st = for_each_launch(plan, 2, l, ntiles * L,
+                             [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi) {
+            return launch_stage(grid, threads, lds, stream, tt->dev, ntiles, lo, hi, l.rank_begin,
+                                l.rank_end, ds->params, dsrc, ddst, dflags, L);
         });
         tide_status st2 = release_slot(ds, slot, stream);
         return st != TIDE_OK ? st : st2;

@@ -78,6 +78,15 @@ hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
                         const uint32_t* flags, const uint16_t* shards, int64_t shard_stride,
                         int64_t shard_elems, int32_t first_rank, int32_t nranks);
 
+// Slot-Reuse staging (kernels.hip): tiles [tile_lo, tile_hi) of L copies of
+// the placement tiling (ntiles tiles each); src / dst hold P * L pointers,
+// parameter-major (p * L + c).
+hipError_t launch_stage(int grid, int threads, size_t lds, hipStream_t stream,
+                        const TileRec* tiles, int64_t ntiles, int64_t tile_lo, int64_t tile_hi,
+                        int32_t rb, int32_t re, const ParamDev* params,
+                        const uint16_t* const* src, uint16_t* const* dst, const uint32_t* flags,
+                        int32_t L);
+
 // Level-2 landing sum (kernels.hip). The node's inbox and shard pointers travel
 // in the kernel arguments (at most kMaxLanding GPUs per node).
 constexpr int kMaxLanding = 64;

@@ -110,7 +110,10 @@ def test_launch_count(tide):
     assert b > 4
     assert plan.launch_count(0, tide.budgeted(max_launch_us=3000)) < b
     assert plan.launch_count(0, tide.Launch(rank_begin=3, rank_end=3)) == 0
-    assert _status(lambda: plan.launch_count(2)) == "TIDE_ERR_INVALID_ARG"
+    # Staging (op 2) walks the placement tiling once per contributor.
+    assert plan.launch_count(2) == 1
+    assert plan.launch_count(2, tide.budgeted()) >= plan.launch_count(1, tide.budgeted())
+    assert _status(lambda: plan.launch_count(3)) == "TIDE_ERR_INVALID_ARG"
     assert _status(lambda: plan.launch_count(0, tide.Launch(mode=7))) == "TIDE_ERR_INVALID_ARG"
     assert _status(lambda: plan.launch_count(0, tide.Launch(rank_begin=5, rank_end=2))) == \
         "TIDE_ERR_INVALID_ARG"
@@ -161,3 +164,37 @@ def test_compute_calls_validate_before_enqueue(tide):
         "TIDE_ERR_INVALID_ARG"
     assert _status(lambda: ag(plan, shards, [params[0], params[1] + 1, params[2]], stream=0)) == \
         "TIDE_ERR_ALIGNMENT"
+
+
+def test_stage_validates_before_enqueue(tide):
+    shapes = [(8, 4), (4, 4), (12, 4)]
+    plan = tide.plan_create(shapes, 4, 2)
+    NS = plan.N * plan.S
+    grads = [[FAKE + 0x100000 * (c * 3 + p) for p in range(3)] for c in range(2)]
+    slots = [FAKE + 0x10000000, FAKE + 0x10000000 + 2 * NS]
+    st = tide.stage_grads_bf16
+    assert _status(lambda: st(plan, grads, [slots[0], slots[0] + 2], stream=0)) == \
+        "TIDE_ERR_INVALID_ARG"                # the two slots overlap
+    assert _status(lambda: st(plan, grads, [slots[0], slots[1] + 1], stream=0)) == \
+        "TIDE_ERR_ALIGNMENT"
+    assert _status(lambda: st(plan, grads, [slots[0], 0], stream=0)) == "TIDE_ERR_INVALID_ARG"
+    bad = [list(g) for g in grads]
+    bad[0][1] = slots[1] + 64                 # a gradient inside a slot
+    assert _status(lambda: st(plan, bad, slots, stream=0)) == "TIDE_ERR_INVALID_ARG"
+    bad[0][1] = FAKE + 3
+    assert _status(lambda: st(plan, bad, slots, stream=0)) == "TIDE_ERR_ALIGNMENT"
+    bad[0][1] = 0
+    assert _status(lambda: st(plan, bad, slots, stream=0)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: st(plan, grads, slots, stream=0, engine=7)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: st(plan, grads, slots, stream=0, launch=tide.Launch(rank_end=9))) == \
+        "TIDE_ERR_INVALID_ARG"
+    # An empty rank range enqueues nothing and succeeds without a GPU.
+    assert _status(lambda: st(plan, grads, slots, stream=0,
+                              launch=tide.Launch(rank_begin=1, rank_end=1))) == "TIDE_OK"
+    # The reduce's table over the slots: slots[c] + N * o_p, in bytes.
+    tab = tide.slot_grads_table(plan, slots)
+    o = [plan.param(p)[4] for p in range(3)]
+    assert [tab.arr[i] for i in range(6)] == [slots[c] + 2 * 4 * o[p] for c in range(2)
+                                              for p in range(3)]
+    with pytest.raises(ValueError):
+        st(plan, grads, slots[:1], stream=0)
