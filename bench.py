@@ -268,7 +268,8 @@ def slot_reuse_parts(torch, tide, plan, cfg, g_tab, out, valid, in_place_ms, ite
         return e[0].elapsed_time(e[1]) / k
 
     st_k = timed(lambda: tide.stage_grads_bf16(plan, g_tab, slots))
-    st_s = timed(lambda: tide.stage_grads_bf16(plan, g_tab, slots, engine="sdma"), 3)
+    st_s = timed(lambda: tide.stage_grads_bf16(plan, g_tab, slots, engine="runtime"), 3)
+    st_d = timed(lambda: tide.stage_grads_bf16(plan, g_tab, slots, engine="sdma"), 1)
     rd = timed(lambda: tide.reduce_scatter_bf16_fp32(plan, s_tab, out))
 
     def both():
@@ -290,6 +291,8 @@ def slot_reuse_parts(torch, tide, plan, cfg, g_tab, out, valid, in_place_ms, ite
             "stage_kernel_GBps": round(stage_bytes / (st_k / 1e3) / 1e9, 1),
             "stage_runtime_copy_ms": round(st_s, 4),
             "stage_runtime_copy_GBps": round(stage_bytes / (st_s / 1e3) / 1e9, 1),
+            "stage_dma_engines_ms": round(st_d, 4),
+            "stage_dma_engines_GBps": round(stage_bytes / (st_d / 1e3) / 1e9, 1),
             "stage_bytes": stage_bytes,
             "reduce_from_slots_ms": round(rd, 4),
             "stage_plus_reduce_ms": round(tot, 4),
@@ -308,7 +311,8 @@ def main():
                     choices=["llama70b_layer", "qwen3_moe_layer", "padding_stress", "wan22_dit_block"])
     ap.add_argument("--mode", default="full", choices=["full", "budgeted"])
     ap.add_argument("--parts", action="store_true",
-                    help="also time the SDMA placement engine and a plain copy")
+                    help="also time the runtime-copy placement, the stage placement, the "
+                         "landing sum and a plain copy")
     ap.add_argument("--victim", action="store_true",
                     help="GEMM-victim slowdown, budgeted and full grid")
     ap.add_argument("--stock", action="store_true",
@@ -393,11 +397,11 @@ def main():
     }
     if args.parts:
         e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        tide.allgather_place(plan, shards, params, engine="sdma")
+        tide.allgather_place(plan, shards, params, engine="runtime")
         torch.cuda.synchronize()
         e[0].record()
         for _ in range(5):
-            tide.allgather_place(plan, shards, params, engine="sdma")
+            tide.allgather_place(plan, shards, params, engine="runtime")
         e[1].record()
         torch.cuda.synchronize()
         sd = e[0].elapsed_time(e[1]) / 5
@@ -432,10 +436,10 @@ def main():
         parts["landing_ms"] = round(lt, 4)
         parts["landing_GBps"] = round(lb / (lt / 1e3) / 1e9, 1)
         del inb, shd
-        parts["placement_sdma_ms"] = round(sd, 4)
-        parts["placement_sdma_GBps"] = round(ag_bytes / (sd / 1e3) / 1e9, 1)
+        parts["placement_runtime_copy_ms"] = round(sd, 4)
+        parts["placement_runtime_copy_GBps"] = round(ag_bytes / (sd / 1e3) / 1e9, 1)
         parts["plain_copy_GBps"] = round(copy_ceiling_gbps(torch), 1)
-        log("bench: sdma placement %.3f ms, plain copy %.1f GB/s" % (sd, parts["plain_copy_GBps"]))
+        log("bench: runtime-copy placement %.3f ms, plain copy %.1f GB/s" % (sd, parts["plain_copy_GBps"]))
 
     slot = None
     if args.slot_reuse:

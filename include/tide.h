@@ -61,11 +61,21 @@ typedef enum tide_status {
     TIDE_ERR_HIP = 6            /* a HIP runtime call failed (no GPU, bad stream, launch error) */
 } tide_status;
 
-/* Placement engine (page 1: the all-gather's data movement runs on copy
- * engines and uses no compute units; page 3 Table 1, AG SM budget 0). */
+/* Data-movement engine of the placement and the Slot-Reuse staging (page 1:
+ * the all-gather's data movement runs on copy engines and uses no compute
+ * units; page 3 Table 1, all-gather SM budget 0; page 3 Figure 2(b) step 4,
+ * copy-engine staging of bf16 slices). */
 typedef enum tide_engine {
-    TIDE_ENGINE_KERNEL = 0,     /* a HIP placement kernel */
-    TIDE_ENGINE_SDMA = 1        /* one hipMemcpy2DAsync per parameter (+1 for a partial rank) */
+    TIDE_ENGINE_KERNEL = 0,     /* this library's HIP kernels */
+    TIDE_ENGINE_RUNTIME = 1,    /* HIP runtime device-to-device copies (placement: one
+                                   hipMemcpy2DAsync per parameter, +1 for a partial rank;
+                                   staging: one hipMemcpyAsync per contributor and
+                                   parameter). The runtime runs these as its own blit
+                                   kernels, so they occupy compute units too. */
+    TIDE_ENGINE_SDMA = 2        /* the GPU's DMA engines, no compute units
+                                   (hipMemcpyDeviceToDeviceNoCU, one copy per contributor
+                                   and parameter). Staging only: the runtime has no
+                                   compute-unit-free strided copy for the placement. */
 } tide_engine;
 
 typedef enum tide_launch_mode {
@@ -156,8 +166,9 @@ tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t*
  * For every rank r in [rank_begin, rank_end), the true rows of rank r's piece
  * of every parameter are copied bit for bit to rows r * R_p.. of params[p];
  * padded rows are not written, and nothing else in params is touched.
- * engine selects the HIP kernel or the SDMA copy path; both write the same
- * bytes. The parameters must not overlap each other or the shards read.
+ * engine: TIDE_ENGINE_KERNEL or TIDE_ENGINE_RUNTIME; both write the same bytes
+ * (TIDE_ENGINE_SDMA returns UNSUPPORTED). The parameters must not overlap
+ * each other or the shards read.
  */
 tide_status tide_allgather_place(const tide_plan* plan, const uint16_t* shards,
                                  int64_t shard_stride, uint16_t* const* params, void* stream,
@@ -194,8 +205,10 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* st
  *           written. Pass grads'[c * P + p] = slots[c] + N * o_p to the reduce.
  *   engine: TIDE_ENGINE_KERNEL: one copy kernel for all (c, p), 16-byte
  *           accesses when every pointer of a parameter is 4-byte aligned;
- *           TIDE_ENGINE_SDMA: one hipMemcpyAsync per (c, p) (the HIP runtime
- *           may run device-to-device copies as its own blit kernels).
+ *           TIDE_ENGINE_RUNTIME: one hipMemcpyAsync per (c, p);
+ *           TIDE_ENGINE_SDMA: the same copies on the DMA engines, leaving the
+ *           compute units free (on MI355X about 60 GB/s on one stream, some
+ *           100x slower than the kernel: the local copy belongs on the CUs).
  *   launch: rank_begin / rank_end restrict the copy to those ranks' rows (rank r
  *           holds rows [r R_p, (r + 1) R_p)), so staging and the reduce can be
  *           pipelined by rank range; FULL, or BUDGETED with place_blocks
@@ -206,7 +219,7 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* st
  * refilled by the next all-gather before the reduce that reads it has run.
  * The slots, and the gradient bytes read, are owned by the caller.
  * Errors: INVALID_ARG (NULL pointer with work to do, slots overlapping one
- * another or any gradient, engine not KERNEL / SDMA); ALIGNMENT (odd address);
+ * another or any gradient, unknown engine); ALIGNMENT (odd address);
  * HIP (a launch or copy failed).
  */
 tide_status tide_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* grads,

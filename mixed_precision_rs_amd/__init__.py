@@ -5,7 +5,9 @@ gfx950 in csrc/). Importing this package loads libtide.so and fails loudly if
 it has not been built."""
 from ._lib import (  # noqa: F401
     ENGINE_KERNEL,
+    ENGINE_RUNTIME,
     ENGINE_SDMA,
+    ENGINES,
     EXPORTS,
     FLAG_SCALAR_PATH,
     LAUNCH_BUDGETED,

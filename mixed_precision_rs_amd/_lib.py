@@ -17,7 +17,9 @@ STATUS_NAMES = {0: "TIDE_OK", 1: "TIDE_ERR_INVALID_ARG", 2: "TIDE_ERR_ALIGNMENT"
                 3: "TIDE_ERR_OVERFLOW", 4: "TIDE_ERR_UNSUPPORTED", 5: "TIDE_ERR_NO_MEMORY",
                 6: "TIDE_ERR_HIP"}
 ENGINE_KERNEL = 0
-ENGINE_SDMA = 1
+ENGINE_RUNTIME = 1
+ENGINE_SDMA = 2
+ENGINES = {"kernel": 0, "runtime": 1, "sdma": 2}
 LAUNCH_FULL = 0
 LAUNCH_BUDGETED = 1
 FLAG_SCALAR_PATH = 0x1
@@ -279,7 +281,7 @@ def allgather_place(plan: Plan, shards, params: Sequence[object],
     if tab.n != plan.P:
         raise ValueError("pointer table holds %d entries, expected P=%d" % (tab.n, plan.P))
     if isinstance(engine, str):
-        engine = {"kernel": ENGINE_KERNEL, "sdma": ENGINE_SDMA}[engine]
+        engine = ENGINES[engine]
     arr = tab.arr
     stride = plan.S if shard_stride is None else int(shard_stride)
     sh, sobj = _stream_handle(stream)
@@ -299,7 +301,7 @@ def allgather_place_stage(plan: Plan, stage, first_rank: int, params: Sequence[o
     if tab.n != plan.P:
         raise ValueError("pointer table holds %d entries, expected P=%d" % (tab.n, plan.P))
     if isinstance(engine, str):
-        engine = {"kernel": ENGINE_KERNEL, "sdma": ENGINE_SDMA}[engine]
+        engine = ENGINES[engine]
     stride = plan.S if shard_stride is None else int(shard_stride)
     sh, sobj = _stream_handle(stream)
     st = _load().tide_allgather_place_stage(plan.handle, _ptr(stage), stride, int(first_rank),
@@ -321,7 +323,7 @@ def stage_grads_bf16(plan: Plan, grads: Sequence[Sequence[object]], slots: Seque
     if len(slots) != plan.L:
         raise ValueError("need L=%d slots" % plan.L)
     if isinstance(engine, str):
-        engine = {"kernel": ENGINE_KERNEL, "sdma": ENGINE_SDMA}[engine]
+        engine = ENGINES[engine]
     sa = (ctypes.c_void_p * plan.L)(*[_ptr(t) for t in slots])
     sh, sobj = _stream_handle(stream)
     st = _load().tide_stage_grads_bf16(plan.handle, tab.arr, sa, sh, int(engine),

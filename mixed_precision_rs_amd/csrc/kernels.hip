@@ -442,10 +442,13 @@ __global__ __launch_bounds__(NT) void place_kernel(
 
 // Slot-Reuse staging: dst[p][c][f] = src[p][c][f] for the launch's true
 // indices f of each parameter (a plain copy; dst is the parameter's place in
-// contributor c's slot). Work item t is tile t mod ntiles of the placement
+// contributor c's slot). Work item t is tile t mod ntiles of the staging
 // tiling, for contributor t / ntiles. With kFlagVector every pointer of the
 // parameter is 4-byte aligned, so 16-byte accesses at 8-element steps are
 // dword aligned.
+#ifndef TIDE_STAGE_NT
+#define TIDE_STAGE_NT 1
+#endif
 template <int NT>
 __global__ __launch_bounds__(NT) void stage_kernel(
     const TileRec* __restrict__ tiles, int64_t ntiles, int64_t tile_lo, int64_t tile_hi,
@@ -464,22 +467,34 @@ __global__ __launch_bounds__(NT) void stage_kernel(
         uint16_t* d = dst[(int64_t)rec.p * L + c];
         const bool vec = (flags[rec.p] & kFlagVector) != 0;
         const int64_t lo = (int64_t)rb * pd.s;
-        const int64_t end = min(rec.idx0 + kAgTile, min((int64_t)re * pd.s, pd.valid));
-        for (int64_t g0 = rec.idx0; g0 < end; g0 += kAgUnroll * kStep) {
+        const int64_t end = min(rec.idx0 + kStageTile, min((int64_t)re * pd.s, pd.valid));
+        for (int64_t g0 = rec.idx0; g0 < end; g0 += kStageUnroll * kStep) {
             const int64_t f0 = g0 + (int64_t)tid * kVec;
-            if (vec && g0 >= lo && g0 + kAgUnroll * kStep <= end) {
-                u32x4_a4 w[kAgUnroll];
+            if (vec && g0 >= lo && g0 + kStageUnroll * kStep <= end) {
+                u32x4_a4 w[kStageUnroll];
 #pragma unroll
-                for (int u = 0; u < kAgUnroll; ++u)
-                    w[u] = TIDE_LD(gbl<u32x4_a4>(s + f0 + (int64_t)u * kStep));
+                for (int u = 0; u < kStageUnroll; ++u) {
+                    const TIDE_GLOBAL u32x4_a4* a = gbl<u32x4_a4>(s + f0 + (int64_t)u * kStep);
+#if TIDE_STAGE_NT
+                    w[u] = __builtin_nontemporal_load(a);
+#else
+                    w[u] = *a;
+#endif
+                }
 #pragma unroll
-                for (int u = 0; u < kAgUnroll; ++u)
-                    TIDE_ST(w[u], gbl_mut<u32x4_a4>(d + f0 + (int64_t)u * kStep));
+                for (int u = 0; u < kStageUnroll; ++u) {
+                    TIDE_GLOBAL u32x4_a4* b = gbl_mut<u32x4_a4>(d + f0 + (int64_t)u * kStep);
+#if TIDE_STAGE_NT
+                    __builtin_nontemporal_store(w[u], b);
+#else
+                    *b = w[u];
+#endif
+                }
             } else {
                 const TIDE_GLOBAL uint16_t* gs = gbl<uint16_t>(s);
                 TIDE_GLOBAL uint16_t* gd = gbl_mut<uint16_t>(d);
 #pragma unroll 1
-                for (int u = 0; u < kAgUnroll; ++u)
+                for (int u = 0; u < kStageUnroll; ++u)
 #pragma unroll 1
                     for (int e = 0; e < kVec; ++e) {
                         const int64_t f = f0 + (int64_t)u * kStep + e;

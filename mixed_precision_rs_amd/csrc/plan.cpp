@@ -173,16 +173,17 @@ tide_status resolve_launch(const tide_plan* plan, const tide_launch* in, tide_la
 
 // Tiles of one op over ranks [rb, re). op 0: reduce over each parameter's
 // padded index space restricted to [rb * s_p, re * s_p); op 1: placement over
-// its true elements restricted the same way.
+// its true elements restricted the same way; op 2: staging, as op 1 with its
+// own tile size.
 std::vector<TileRec> build_tiles(const tide_plan* plan, int op, int rb, int re) {
     std::vector<TileRec> out;
-    const int64_t tile = op == 0 ? kRsTile : kAgTile;
+    const int64_t tile = op == 0 ? kRsTile : op == 1 ? kAgTile : kStageTile;
     for (int32_t p = 0; p < plan->P; ++p) {
         const ParamInfo& q = plan->prm[p];
         if (q.s == 0) continue;
         const int64_t lo = (int64_t)rb * q.s;
         int64_t hi = (int64_t)re * q.s;
-        if (op == 1) hi = std::min(hi, q.valid);
+        if (op != 0) hi = std::min(hi, q.valid);
         if (hi <= lo) continue;
         for (int64_t a = lo - lo % kVec; a < hi; a += tile) {
             TileRec t{};
@@ -246,7 +247,7 @@ std::vector<TileRec> build_tiles(const tide_plan* plan, int op, int rb, int re) 
 }
 
 int64_t tile_bytes(const tide_plan* plan, int op) {
-    return op == 0 ? kRsTile * (2 * (int64_t)plan->L + 4) : kAgTile * 4;
+    return op == 0 ? kRsTile * (2 * (int64_t)plan->L + 4) : op == 1 ? kAgTile * 4 : kStageTile * 4;
 }
 
 // Tiles one budgeted workgroup handles per launch.
@@ -539,8 +540,8 @@ tide_status tide_plan_launch_count(const tide_plan* plan, int32_t op, const tide
         tide_launch l;
         tide_status st = resolve_launch(plan, launch, &l);
         if (st != TIDE_OK) return st;
-        // The staging walks the placement tiling once per contributor.
-        int64_t n = (int64_t)build_tiles(plan, op == 0 ? 0 : 1, l.rank_begin, l.rank_end).size();
+        // The staging walks its tiling once per contributor.
+        int64_t n = (int64_t)build_tiles(plan, op, l.rank_begin, l.rank_end).size();
         if (op == 2) n *= plan->L;
         *launches = count_launches(plan, op, l, n);
         return TIDE_OK;
@@ -650,8 +651,13 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* sh
         tide_launch l;
         tide_status st = resolve_launch(plan, launch, &l);
         if (st != TIDE_OK) return st;
-        if (engine != TIDE_ENGINE_KERNEL && engine != TIDE_ENGINE_SDMA)
-            return fail(TIDE_ERR_INVALID_ARG, "engine %d is not KERNEL (0) or SDMA (1)", engine);
+        if (engine != TIDE_ENGINE_KERNEL && engine != TIDE_ENGINE_RUNTIME &&
+            engine != TIDE_ENGINE_SDMA)
+            return fail(TIDE_ERR_INVALID_ARG, "engine %d is not KERNEL (0), RUNTIME (1) or SDMA (2)",
+                        engine);
+        if (engine == TIDE_ENGINE_SDMA)
+            return fail(TIDE_ERR_UNSUPPORTED,
+                        "the placement has no DMA-engine path (no compute-unit-free strided copy)");
         const int32_t P = plan->P;
         if (shard_stride < plan->S)
             return fail(TIDE_ERR_INVALID_ARG, "shard_stride %lld < S %lld",
@@ -696,7 +702,7 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* sh
                 return fail(TIDE_ERR_INVALID_ARG, "params[%d] and params[%d] overlap", wr[i - 1].who,
                             wr[i].who);
         hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
-        if (engine == TIDE_ENGINE_SDMA) {
+        if (engine == TIDE_ENGINE_RUNTIME) {
             // One 2-D copy per parameter for its full pieces (rows of s_p
             // elements, source pitch = shard stride, destination contiguous),
             // split in two where a rotated stage wraps, plus one 1-D copy for
@@ -770,8 +776,10 @@ tide_status tide_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* 
         tide_launch l;
         tide_status st = resolve_launch(plan, launch, &l);
         if (st != TIDE_OK) return st;
-        if (engine != TIDE_ENGINE_KERNEL && engine != TIDE_ENGINE_SDMA)
-            return fail(TIDE_ERR_INVALID_ARG, "engine %d is not KERNEL (0) or SDMA (1)", engine);
+        if (engine != TIDE_ENGINE_KERNEL && engine != TIDE_ENGINE_RUNTIME &&
+            engine != TIDE_ENGINE_SDMA)
+            return fail(TIDE_ERR_INVALID_ARG, "engine %d is not KERNEL (0), RUNTIME (1) or SDMA (2)",
+                        engine);
         const int32_t P = plan->P, L = plan->L;
         const int64_t slot_elems = (int64_t)plan->N * plan->S;   // fits: checked at plan creation
         if (plan->S == 0 || l.rank_end == l.rank_begin) return TIDE_OK;
@@ -821,9 +829,11 @@ tide_status tide_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* 
             fl[p] = f;
         }
         hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
-        if (engine == TIDE_ENGINE_SDMA) {
+        if (engine != TIDE_ENGINE_KERNEL) {
             // One contiguous copy per (contributor, parameter): the rows of
             // ranks [rank_begin, rank_end) are one run on both sides.
+            const hipMemcpyKind kind = engine == TIDE_ENGINE_SDMA ? hipMemcpyDeviceToDeviceNoCU
+                                                                   : hipMemcpyDeviceToDevice;
             for (int32_t p = 0; p < P; ++p) {
                 const ParamInfo& q = plan->prm[p];
                 const int64_t lo = (int64_t)l.rank_begin * q.s;
@@ -831,7 +841,7 @@ tide_status tide_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* 
                 if (hi <= lo) continue;
                 for (int32_t c = 0; c < L; ++c)
                     TIDE_HIP_TRY(hipMemcpyAsync(td[(size_t)p * L + c] + lo, ts[(size_t)p * L + c] + lo,
-                                                (size_t)(hi - lo) * 2, hipMemcpyDeviceToDevice, stream));
+                                                (size_t)(hi - lo) * 2, kind, stream));
             }
             return TIDE_OK;
         }
@@ -843,7 +853,7 @@ tide_status tide_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* 
         st = get_dev_state(plan, dev, &ds);
         if (st != TIDE_OK) return st;
         TileTable* tt;
-        st = get_tiles(plan, ds, 1, l.rank_begin, l.rank_end, &tt);
+        st = get_tiles(plan, ds, 2, l.rank_begin, l.rank_end, &tt);
         if (st != TIDE_OK) return st;
         if (tt->count == 0) return TIDE_OK;
         int slot;

@@ -27,6 +27,13 @@ namespace tide {
 #define TIDE_AG_TILE_STEPS 2
 #endif
 
+#ifndef TIDE_STAGE_UNROLL
+#define TIDE_STAGE_UNROLL 2
+#endif
+#ifndef TIDE_STAGE_TILE_STEPS
+#define TIDE_STAGE_TILE_STEPS 2
+#endif
+
 constexpr int kThreads = TIDE_THREADS;     // workgroup size of the full grid (wave64s x 64)
 constexpr int kFatThreads = 1024;          // workgroup size of budgeted launches: 16 wave64s,
                                            // 4 independent quarters of kThreads
@@ -36,6 +43,9 @@ constexpr int kRsUnroll = TIDE_RS_UNROLL;  // steps whose loads a reduce thread 
 constexpr int kAgUnroll = TIDE_AG_UNROLL;  // same, placement
 constexpr int64_t kRsTile = (int64_t)TIDE_RS_TILE_STEPS * kStep;   // elements per reduce tile
 constexpr int64_t kAgTile = (int64_t)TIDE_AG_TILE_STEPS * kStep;   // elements per placement tile
+constexpr int kStageUnroll = TIDE_STAGE_UNROLL;                          // same, staging copy
+constexpr int64_t kStageTile = (int64_t)TIDE_STAGE_TILE_STEPS * kStep;   // elements per staging tile
+static_assert(kStageTile % (kStageUnroll * kStep) == 0, "tile must hold whole groups");
 static_assert(kRsTile % (kRsUnroll * kStep) == 0, "tile must hold whole groups");
 static_assert(kAgTile % (kAgUnroll * kStep) == 0, "tile must hold whole groups");
 static_assert(kFatThreads % kThreads == 0, "a fat workgroup is whole quarters");
@@ -79,8 +89,9 @@ hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
                         int64_t shard_elems, int32_t first_rank, int32_t nranks);
 
 // Slot-Reuse staging (kernels.hip): tiles [tile_lo, tile_hi) of L copies of
-// the placement tiling (ntiles tiles each); src / dst hold P * L pointers,
-// parameter-major (p * L + c).
+// the staging tiling (ntiles tiles of kStageTile elements over each
+// parameter's true elements); src / dst hold P * L pointers, parameter-major
+// (p * L + c).
 hipError_t launch_stage(int grid, int threads, size_t lds, hipStream_t stream,
                         const TileRec* tiles, int64_t ntiles, int64_t tile_lo, int64_t tile_hi,
                         int32_t rb, int32_t re, const ParamDev* params,

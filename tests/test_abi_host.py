@@ -156,6 +156,8 @@ def test_compute_calls_validate_before_enqueue(tide):
         "TIDE_ERR_INVALID_ARG"
     assert _status(lambda: ag(plan, shards + 1, params, stream=0)) == "TIDE_ERR_ALIGNMENT"
     assert _status(lambda: ag(plan, shards, params, stream=0, engine=5)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: ag(plan, shards, params, stream=0, engine="sdma")) == \
+        "TIDE_ERR_UNSUPPORTED"                # no compute-unit-free strided copy
     assert _status(lambda: ag(plan, shards, [params[0], params[0], params[2]], stream=0)) == \
         "TIDE_ERR_INVALID_ARG"                # two parameters overlap
     assert _status(lambda: ag(plan, shards, [shards + 4, params[1], params[2]], stream=0)) == \

@@ -11,7 +11,7 @@ Checks, per workload:
     output element equals L * f32(g) exactly in any summation order, so the
     WHOLE output is checked against a torch expression (pad + view) built from
     the oracle's layout;
-  * placement, kernel and SDMA engines: every parameter equals the
+  * placement, kernel and runtime-copy engines: every parameter equals the
     split-with-sizes view of the rank-major shards at the oracle's offsets.
 """
 import gc
@@ -160,7 +160,7 @@ def test_full_size(tide, orc, name):
     _check_identical(tide, orc, cfg, grads0)
     del grads0
     _free()
-    for eng in ("kernel", "sdma"):
+    for eng in ("kernel", "runtime"):
         say("%s: placement %s" % (name, eng))
         _check_place(tide, orc, cfg, eng)
     if name == "wan22_dit_block":

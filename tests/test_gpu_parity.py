@@ -73,8 +73,8 @@ def run_case(tide, orc, shapes, N, L, grads, *, stride_extra=0, out_off=0, grad_
 def test_worked_example_group(tide, orc):
     cfg = CONFIGS["worked_example"]
     grads = host_grads(cfg.shapes, cfg.L, seed=0, sigma=cfg.sigma)
-    say("worked example: full grid, kernel + sdma")
-    run_case(tide, orc, list(cfg.shapes), cfg.N, cfg.L, grads, engines=("kernel", "sdma"))
+    say("worked example: full grid, kernel + runtime copies")
+    run_case(tide, orc, list(cfg.shapes), cfg.N, cfg.L, grads, engines=("kernel", "runtime"))
     say("worked example: budgeted")
     run_case(tide, orc, list(cfg.shapes), cfg.N, cfg.L, grads, launch=tide.budgeted())
 
@@ -120,7 +120,7 @@ def test_fuzz(tide, orc, case):
         case, P, N, L, shapes, stride_extra, out_off, shard_off, mode, rr))
     run_case(tide, orc, shapes, N, L, grads, stride_extra=stride_extra, out_off=out_off,
              grad_offs=grad_offs, launch=launch, rank_range=rr, shard_off=shard_off,
-             param_offs=param_offs, engines=("kernel", "sdma"), seed=case)
+             param_offs=param_offs, engines=("kernel", "runtime"), seed=case)
 
 
 def test_multi_tile_ragged_group(tide, orc):
@@ -131,7 +131,7 @@ def test_multi_tile_ragged_group(tide, orc):
     N, L = 48, 8
     grads = host_grads(shapes, L, seed=3, sigma=1.0, outlier_frac=0.01)
     say("multi-tile group: %d params, %d elements" % (len(shapes), sum(t * k for t, k in shapes)))
-    run_case(tide, orc, shapes, N, L, grads, engines=("kernel", "sdma"))
+    run_case(tide, orc, shapes, N, L, grads, engines=("kernel", "runtime"))
     say("multi-tile group: budgeted, rank subset")
     run_case(tide, orc, shapes, N, L, grads, launch=tide.budgeted(max_launch_us=20),
              rank_range=(5, 29))
@@ -164,7 +164,7 @@ def test_empty_and_degenerate(tide, orc):
     for shapes, N, L in [([(0, 5), (3, 2), (0, 1)], 4, 2), ([(1, 1)], 1, 1),
                          ([(2, 3)], 64, 8), ([(5, 8192)], 1, 3)]:
         grads = host_grads(shapes, L, seed=N)
-        run_case(tide, orc, shapes, N, L, grads, engines=("kernel", "sdma"))
+        run_case(tide, orc, shapes, N, L, grads, engines=("kernel", "runtime"))
     plan = tide.plan_create([], 4, 2)
     tide.reduce_scatter_bf16_fp32(plan, [[], []], None)
     tide.allgather_place(plan, None, [])

@@ -83,7 +83,7 @@ GROUPS = [
 ]
 
 
-@pytest.mark.parametrize("engine", ["kernel", "sdma"])
+@pytest.mark.parametrize("engine", ["kernel", "runtime", "sdma"])
 @pytest.mark.parametrize("gi", range(len(GROUPS)))
 def test_stage_groups(tide, orc, gi, engine):
     shapes, N, L = GROUPS[gi]
@@ -129,7 +129,7 @@ def test_stage_fuzz(tide, orc, case):
         a = int(rng.integers(0, N))
         rr = (a, int(rng.integers(a, N + 1)))
     goff = [[int(rng.choice([0, 0, 1, 2, 8])) for _ in shapes] for _ in range(L)]
-    engine = "sdma" if rng.random() < 0.25 else "kernel"
+    engine = str(rng.choice(["kernel", "kernel", "runtime", "sdma"]))
     say("stage fuzz %d: N=%d L=%d shapes=%s mode=%d ranks=%s %s" % (case, N, L, shapes, mode,
                                                                     rr, engine))
     run_stage(tide, orc, shapes, N, L, grads, grad_offs=goff, slot_off=int(rng.choice([0, 1, 2])),
@@ -251,8 +251,8 @@ def test_stage_full_size(tide, orc, name):
     from test_gpu_fullsize import _check_pieces, _sample_pieces
     _check_pieces(orc, cfg, grads, out, S, _sample_pieces(cfg, np.random.default_rng(7)))
     if name == "wan22_dit_block":
-        say("%s: budgeted staging and SDMA staging" % name)
-        for kw in ({"launch": tide.budgeted()}, {"engine": "sdma"}):
+        say("%s: budgeted, runtime-copy and DMA-engine staging" % name)
+        for kw in ({"launch": tide.budgeted()}, {"engine": "runtime"}, {"engine": "sdma"}):
             s2 = [torch.zeros(n, dtype=torch.bfloat16, device=dev()) for _ in range(cfg.L)]
             tide.stage_grads_bf16(plan, g_tab, s2, **kw)
             torch.cuda.synchronize()

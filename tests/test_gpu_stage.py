@@ -20,7 +20,7 @@ def tide():
     return t
 
 
-@pytest.mark.parametrize("engine", ["kernel", "sdma"])
+@pytest.mark.parametrize("engine", ["kernel", "runtime"])
 def test_stage_placement(tide, orc, engine):
     groups = [([(8, 4), (4, 4), (12, 4)], 4),
               ([(37, 3), (5, 16), (640, 64), (3, 1), (100, 4096)], 8),
