@@ -318,23 +318,62 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
             } else
 #endif
             {
-                // Ragged edge: element by element, exact bounds.
+                // Ragged step: it crosses an end of the launch's range or of
+                // the tile, or the valid end, or the parameter has pointers
+                // that are not 16-byte aligned. A thread's group of 8
+                // elements that lies wholly inside the step's bounds and on
+                // one side of the valid end still goes as one vector; only
+                // a group that straddles a bound goes element by element.
 #pragma unroll 1
                 for (int u = 0; u < kRsUnroll; ++u) {
                     const int64_t fu = f0 + (int64_t)u * kStep;
-                    int64_t r, j;
-                    locate<kRsTile>(tr, pd.s, fu, r, j);
-#pragma unroll 1
-                    for (int e = 0; e < kVec; ++e, step(pd.s, r, j)) {
-                        const int64_t f = fu + e;
-                        if (f < tr.lo || f >= end) continue;
-                        float v = 0.0f;
-                        if (f < pd.valid) {
-                            v = widen(gbl<uint16_t>(g[0])[f]);
-#pragma unroll 1
-                            for (int c = 1; c < L; ++c) v = v + widen(gbl<uint16_t>(g[c])[f]);
+                    const bool whole = fu >= tr.lo && fu + kVec <= end;
+                    if (whole && vec && fu + kVec <= pd.valid) {
+                        float a[2][4];
+                        constexpr int kCUnroll = LT > 0 ? LT : 1;
+#pragma unroll kCUnroll
+                        for (int c = 0; c < L; ++c) {
+                            const u32x4 v = TIDE_LD(gbl<u32x4>(g[c] + fu));
+#pragma unroll
+                            for (int m = 0; m < 4; ++m) {
+                                const float lo = lo_bf16(v[m]), hi = hi_bf16(v[m]);
+                                float& x0 = a[m / 2][2 * (m % 2)];
+                                float& x1 = a[m / 2][2 * (m % 2) + 1];
+                                x0 = c == 0 ? lo : x0 + lo;
+                                x1 = c == 0 ? hi : x1 + hi;
+                            }
                         }
-                        out[r * out_stride + pd.o + j] = v;
+                        store4(tr, pd, fu, a[0], out, out_stride);
+                        store4(tr, pd, fu + 4, a[1], out, out_stride);
+                    } else if (whole && fu >= pd.valid) {
+                        const float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                        store4(tr, pd, fu, z, out, out_stride);
+                        store4(tr, pd, fu + 4, z, out, out_stride);
+                    } else {
+                        int64_t r, j;
+                        locate<kRsTile>(tr, pd.s, fu, r, j);
+#pragma unroll 1
+                        for (int e = 0; e < kVec; ++e, step(pd.s, r, j)) {
+                            const int64_t f = fu + e;
+                            if (f < tr.lo || f >= end) continue;
+                            float v = 0.0f;
+                            if (f < pd.valid) {
+                                if constexpr (LT > 0) {
+                                    // All L loads issued before the first add.
+                                    uint16_t h[LT > 0 ? LT : 1];
+#pragma unroll
+                                    for (int c = 0; c < LT; ++c) h[c] = gbl<uint16_t>(g[c])[f];
+                                    v = widen(h[0]);
+#pragma unroll
+                                    for (int c = 1; c < LT; ++c) v = v + widen(h[c]);
+                                } else {
+                                    v = widen(gbl<uint16_t>(g[0])[f]);
+#pragma unroll 1
+                                    for (int c = 1; c < L; ++c) v = v + widen(gbl<uint16_t>(g[c])[f]);
+                                }
+                            }
+                            out[r * out_stride + pd.o + j] = v;
+                        }
                     }
                 }
             }
@@ -422,10 +461,19 @@ __global__ __launch_bounds__(NT) void place_kernel(
                 for (int u = 0; u < kAgUnroll; ++u)
                     TIDE_ST(w[u], d4 + u * (kStep / kVec));
             } else {
+                // Ragged step: a thread's group of 8 that lies wholly inside
+                // the bounds still goes as one vector; only a group that
+                // straddles a bound (or a parameter without 16-byte pointers)
+                // goes element by element.
                 TIDE_GLOBAL uint16_t* d = gbl_mut<uint16_t>(dst);
 #pragma unroll 1
                 for (int u = 0; u < kAgUnroll; ++u) {
                     const int64_t fu = f0 + (int64_t)u * kStep;
+                    if (vec && fu >= tr.lo && fu + kVec <= end) {
+                        const u32x4 w = gather8(tr, pd, fu, shards, stride, shard_elems, first, nranks);
+                        TIDE_ST(w, gbl_mut<u32x4>(dst + fu));
+                        continue;
+                    }
                     int64_t r, j;
                     locate<kAgTile>(tr, pd.s, fu, r, j);
 #pragma unroll 1
@@ -491,15 +539,24 @@ __global__ __launch_bounds__(NT) void stage_kernel(
 #endif
                 }
             } else {
+                // Ragged step: whole groups of 8 inside the bounds as vectors,
+                // a group that straddles a bound element by element.
                 const TIDE_GLOBAL uint16_t* gs = gbl<uint16_t>(s);
                 TIDE_GLOBAL uint16_t* gd = gbl_mut<uint16_t>(d);
 #pragma unroll 1
-                for (int u = 0; u < kStageUnroll; ++u)
+                for (int u = 0; u < kStageUnroll; ++u) {
+                    const int64_t fu = f0 + (int64_t)u * kStep;
+                    if (vec && fu >= lo && fu + kVec <= end) {
+                        const u32x4_a4 w = TIDE_LD(gbl<u32x4_a4>(s + fu));
+                        TIDE_ST(w, gbl_mut<u32x4_a4>(d + fu));
+                        continue;
+                    }
 #pragma unroll 1
                     for (int e = 0; e < kVec; ++e) {
-                        const int64_t f = f0 + (int64_t)u * kStep + e;
+                        const int64_t f = fu + e;
                         if (f >= lo && f < end) gd[f] = gs[f];
                     }
+                }
             }
         }
     }

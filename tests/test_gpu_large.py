@@ -1,0 +1,99 @@
+"""Offsets beyond 2^31 elements: one parameter larger than 2^31 elements and a
+second whose rank-major pieces start beyond 2^31 in the output, through the
+reduce-scatter, the placement, and the Slot-Reuse staging.
+
+Checks: sampled pieces against the oracle (bit for bit), the identical-
+contributor whole-output closed form (2 * f32(g) in every true element, +0
+in padding), the placement against a torch view of the shards, and the
+staged slot against the gradients (torch on the device).
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import bits_of, dev, same_f32, say
+from workloads import device_grads, device_rank_major_bits
+
+pytestmark = pytest.mark.gpu
+
+# 262,201 x 8192 = 2,147,950,592 elements (> 2^31); N = 8 pads it by 7 rows.
+SHAPES = [(262_201, 8192), (19, 3)]
+N, L = 8, 2
+
+
+@pytest.fixture(scope="module")
+def tide():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mixed_precision_rs_amd as t
+    return t
+
+
+def _free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_beyond_int32(tide, orc):
+    assert SHAPES[0][0] * SHAPES[0][1] > 2 ** 31
+    plan = tide.plan_create(SHAPES, N, L)
+    S = plan.S
+    lay = orc.layout(SHAPES, N)
+    assert S == int(lay["S"]) and (N - 1) * S + int(lay["o"][1]) > 2 ** 31
+    say("large: generating %d x %d grads (%.1f GB)" % (L, len(SHAPES), L * 2 * sum(t * k for t, k in SHAPES) / 1e9))
+    grads = device_grads(SHAPES, L, seed=3)
+    out = torch.empty(N * S, dtype=torch.float32, device=dev())
+    out.view(torch.int32).fill_(0x7FC0DEAD)
+    tide.reduce_scatter_bf16_fp32(plan, grads, out)
+    torch.cuda.synchronize()
+    say("large: checking sampled pieces against the oracle")
+    for r, p in [(0, 0), (N - 1, 0), (3, 1), (N - 1, 1)]:
+        first, n = orc.piece_rows(SHAPES, N, r, p)
+        rows = [bits_of(grads[c][p][first:first + n]) for c in range(L)]
+        want = orc.reduce_piece(SHAPES, N, L, r, p, rows)
+        o, s = int(lay["o"][p]), int(lay["s"][p])
+        same_f32(bits_of(out[r * S + o: r * S + o + s]), want, "piece (r=%d, p=%d)" % (r, p))
+    del out, grads
+    _free()
+
+    say("large: identical contributors, whole output")
+    g0 = device_grads(SHAPES, 1, seed=4)[0]
+    out = torch.empty(N * S, dtype=torch.float32, device=dev())
+    tide.reduce_scatter_bf16_fp32(plan, [g0] * L, out)
+    torch.cuda.synchronize()
+    o2 = out.view(N, S)
+    for p, (t, k) in enumerate(SHAPES):
+        R, o, s = int(lay["R"][p]), int(lay["o"][p]), int(lay["s"][p])
+        got = o2[:, o:o + s].reshape(N * R, k)
+        assert torch.equal(got[:t].view(torch.int32),
+                           (g0[p].float() * float(L)).view(torch.int32)), p
+        assert torch.all(got[t:].view(torch.int32) == 0), p
+    del out, o2
+
+    say("large: Slot-Reuse staging")
+    slots = [torch.empty(N * S, dtype=torch.bfloat16, device=dev()) for _ in range(L)]
+    tide.stage_grads_bf16(plan, [g0] * L, slots)
+    torch.cuda.synchronize()
+    for c in range(L):
+        for p, (t, k) in enumerate(SHAPES):
+            at = N * int(lay["o"][p])
+            assert torch.equal(slots[c][at:at + t * k].view(torch.int16),
+                               g0[p].reshape(-1).view(torch.int16)), (c, p)
+    del slots, g0
+    _free()
+
+    say("large: placement")
+    sh = device_rank_major_bits(N * S, seed=6)
+    params = [torch.empty((t, k), dtype=torch.bfloat16, device=dev()) for t, k in SHAPES]
+    tide.allgather_place(plan, sh, params)
+    torch.cuda.synchronize()
+    v = sh.view(N, S)
+    for p, (t, k) in enumerate(SHAPES):
+        o, s = int(lay["o"][p]), int(lay["s"][p])
+        want = v[:, o:o + s].reshape(-1)[:t * k]
+        assert torch.equal(params[p].reshape(-1).view(torch.int16), want.view(torch.int16)), p
+    del sh, params, v
+    _free()
+    say("large: ok")
