@@ -12,7 +12,8 @@ value = algorithmic bytes per step / time per step:
 Prints ONE JSON line on stdout; progress goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--parts] [--victim] [--stock] [--slot-reuse] [--no-cpu-baseline]
+                  [--parts] [--victim] [--stock] [--slot-reuse] [--occupancy]
+                  [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -132,7 +133,7 @@ def copy_ceiling_gbps(torch, nbytes=4 << 30, iters=10):
     return 2 * nbytes / (ms / 1e3) / 1e9
 
 
-def victim_slowdown(torch, tide, plan, grads, out, shards, params, launch, reps=3, nb=4):
+def victim_slowdown(torch, tide, plan, grads, out, shards, params, launch, gs, cs, reps=3, nb=4):
     """Slowdown of a 256x8192x8192 bf16 GEMM while the reduce-scatter +
     placement run on another stream (median GEMM time, concurrent vs alone).
 
@@ -142,8 +143,6 @@ def victim_slowdown(torch, tide, plan, grads, out, shards, params, launch, reps=
     A = torch.randn(256, 8192, device="cuda", dtype=torch.bfloat16)
     Bs = [torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16) for _ in range(nb)]
     C = torch.empty(256, 8192, device="cuda", dtype=torch.bfloat16)
-    gs = torch.cuda.Stream()
-    cs = torch.cuda.Stream()
     for i in range(20):
         torch.matmul(A, Bs[i % nb], out=C)
     torch.cuda.synchronize()
@@ -194,6 +193,87 @@ def victim_slowdown(torch, tide, plan, grads, out, shards, params, launch, reps=
             "collective_ms": round(statistics.median(r[1] for r in res), 3),
             "gemms_counted": int(statistics.median(r[2] for r in res)),
             "gemms_counted_are": res[0][3] + " the collective window"}
+
+
+def occupancy_probe(torch, tide, plan, grads, out, shards, params, gs, cs, probes=500,
+                    probe_wgs=128, probe_threads=256, probe_lds=42496, probe_us=40):
+    """Where the budgeted collective's workgroups run, how long they live, and
+    whether GEMM-shaped occupants (the 256x8192x8192 GEMM's hipBLASLt kernel
+    runs 128 workgroups of 256 threads with 42,496 B of LDS) land on a CU that
+    a collective workgroup holds at the same time: the one-GPU analog of the
+    pages' SM-id probe. Both with the LDS reservation and without it."""
+    import numpy as np
+    cal = tide.trace_buffer(1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    tide.diag_occupy(1, 64, 0, 1000, cal)
+    torch.cuda.synchronize()
+    e0.record()
+    tide.diag_occupy(1, 64, 0, 10_000_000, cal)
+    e1.record()
+    torch.cuda.synchronize()
+    ticks_per_us = 1e7 / (e0.elapsed_time(e1) * 1e3)
+    spin = int(probe_us * ticks_per_us)
+    res = {"counter_ticks_per_us": round(ticks_per_us, 2),
+           "occupant": {"workgroups": probe_wgs, "threads": probe_threads, "lds_bytes": probe_lds,
+                        "spin_us": probe_us, "launches": probes}}
+    for name, flags in (("with_lds_reservation", 0), ("without_lds_reservation",
+                                                      tide.FLAG_NO_LDS_FENCE)):
+        b = tide.budgeted(flags=flags)
+        n_rs, n_ag = plan.trace_records(0, b), plan.trace_records(1, b)
+        t_rs, t_ag = tide.trace_buffer(n_rs), tide.trace_buffer(n_ag)
+        t_pr = tide.trace_buffer(probes * probe_wgs)
+        torch.cuda.synchronize()
+        cs.wait_stream(torch.cuda.current_stream())
+        gs.wait_stream(torch.cuda.current_stream())
+        tide.reduce_scatter_bf16_fp32(plan, grads, out, stream=cs, launch=tide.traced(b, t_rs))
+        tide.allgather_place(plan, shards, params, stream=cs, launch=tide.traced(b, t_ag))
+        for k in range(probes):
+            tide.diag_occupy(probe_wgs, probe_threads, probe_lds, spin,
+                             t_pr[k * probe_wgs * 3:], stream=gs)
+        torch.cuda.synchronize()
+        rs, ag = tide.decode_trace(t_rs, n_rs), tide.decode_trace(t_ag, n_ag)
+        pr = tide.decode_trace(t_pr, probes * probe_wgs)
+        cu = np.concatenate([rs["cu"], ag["cu"]])
+        cb = np.concatenate([rs["t_begin"], ag["t_begin"]]).astype(np.int64)
+        ce = np.concatenate([rs["t_end"], ag["t_end"]]).astype(np.int64)
+        w0, w1 = cb.min(), ce.max()
+        by_cu = {}
+        for c, a, z in zip(cu.tolist(), cb.tolist(), ce.tolist()):
+            by_cu.setdefault(c, []).append((a, z))
+        pb, pe = pr["t_begin"].astype(np.int64), pr["t_end"].astype(np.int64)
+        inside = (pb >= w0) & (pe <= w1)
+        shared = 0
+        for c, a, z in zip(pr["cu"][inside].tolist(), pb[inside].tolist(), pe[inside].tolist()):
+            if any(x < z and a < y for x, y in by_cu.get(c, ())):
+                shared += 1
+        n_in = int(inside.sum())
+        life = (ce - cb) / ticks_per_us
+        per_launch = [len(set(rs["cu"][k:k + b.reduce_blocks].tolist()))
+                      for k in range(0, n_rs, b.reduce_blocks)]
+        res[name] = {
+            "collective_ms": round((w1 - w0) / ticks_per_us / 1e3, 3),
+            "collective_workgroups": int(n_rs + n_ag),
+            "collective_distinct_cus": len(by_cu),
+            "reduce_launch_distinct_cus_median": float(np.median(per_launch)),
+            "collective_workgroup_life_us_median": round(float(np.median(life)), 1),
+            "collective_workgroup_life_us_p90": round(float(np.percentile(life, 90)), 1),
+            "occupant_workgroups_inside_window": n_in,
+            "occupant_workgroups_sharing_a_cu": shared,
+            "occupant_share_pct": round(100.0 * shared / max(n_in, 1), 2),
+            "occupant_life_us_median": round(float(np.median((pe - pb)[inside])) / ticks_per_us, 1)
+            if n_in else None,
+        }
+    # Full grid, for contrast.
+    n_full = plan.trace_records(0)
+    t_full = tide.trace_buffer(n_full)
+    tide.reduce_scatter_bf16_fp32(plan, grads, out, launch=tide.traced(tide.Launch(), t_full))
+    torch.cuda.synchronize()
+    fr = tide.decode_trace(t_full, n_full)
+    fl = (fr["t_end"].astype(np.int64) - fr["t_begin"].astype(np.int64)) / ticks_per_us
+    res["full_grid_reduce"] = {"workgroups": int(n_full),
+                               "distinct_cus": len(set(fr["cu"].tolist())),
+                               "workgroup_life_us_median": round(float(np.median(fl)), 2)}
+    return res
 
 
 def stock_fsdp2(torch, tide, plan, cfg, grads, shards, out, p_tab, iters=3):
@@ -319,6 +399,8 @@ def main():
                     help="also time the stock FSDP2 path (chunk_cat pack + sum, split_with_sizes_copy)")
     ap.add_argument("--slot-reuse", action="store_true",
                     help="also time the Slot-Reuse staging and the reduce reading the slots")
+    ap.add_argument("--occupancy", action="store_true",
+                    help="trace where budgeted workgroups run, beside GEMM-shaped occupants")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-ranks", type=int, default=0, help="ranks in the CPU sample (0: all)")
     args = ap.parse_args()
@@ -441,6 +523,19 @@ def main():
         parts["plain_copy_GBps"] = round(copy_ceiling_gbps(torch), 1)
         log("bench: runtime-copy placement %.3f ms, plain copy %.1f GB/s" % (sd, parts["plain_copy_GBps"]))
 
+    # Two side streams, created once: a GEMM (or occupant) stream and a
+    # collective stream. Reusing them keeps every measurement on the same pair
+    # of hardware queues (streams created later may share a queue with an
+    # earlier one, which would serialise the two).
+    gs = cs = None
+    if args.occupancy or args.victim:
+        gs, cs = torch.cuda.Stream(), torch.cuda.Stream()
+    occ = None
+    if args.occupancy:
+        log("bench: occupancy probe")
+        occ = occupancy_probe(torch, tide, plan, grads, out, shards, params, gs, cs)
+        log("bench: occupancy %s" % json.dumps(occ))
+
     slot = None
     if args.slot_reuse:
         log("bench: slot-reuse staging")
@@ -459,9 +554,12 @@ def main():
     if args.victim:
         log("bench: GEMM victim, budgeted")
         victim = {"budgeted_16_4": victim_slowdown(torch, tide, plan, grads, out, shards, params,
-                                                   tide.budgeted()),
+                                                   tide.budgeted(), gs, cs),
+                  "budgeted_16_4_without_lds_reservation": victim_slowdown(
+                      torch, tide, plan, grads, out, shards, params,
+                      tide.budgeted(flags=tide.FLAG_NO_LDS_FENCE), gs, cs),
                   "full_grid": victim_slowdown(torch, tide, plan, grads, out, shards, params,
-                                               tide.Launch())}
+                                               tide.Launch(), gs, cs)}
         log("bench: victim %s" % json.dumps(victim))
 
     cpu = None
@@ -504,6 +602,8 @@ def main():
         line["stock_fsdp2_same_gpu"] = stock
     if slot is not None:
         line["slot_reuse"] = slot
+    if occ is not None:
+        line["occupancy_probe"] = occ
     print(json.dumps(line), flush=True)
 
 

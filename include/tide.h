@@ -85,6 +85,16 @@ typedef enum tide_launch_mode {
                                    blocks, single blocks, each living 0.2-0.4 ms) */
 } tide_launch_mode;
 
+/* One workgroup of a traced launch (the analog of the pages' SM-id probe,
+ * page 3 Figure 3 and Table 5): where it ran and for how long. */
+typedef struct tide_trace_rec {
+    uint32_t hw_id;          /* HW_ID hardware register of the workgroup's first wave
+                                (bits 8-11 CU, 12 shader array, 13-15 shader engine) */
+    uint32_t xcc_id;         /* XCC_ID hardware register (bits 0-3: the accelerator die) */
+    uint64_t t_begin;        /* constant-rate real-time counter when the workgroup started */
+    uint64_t t_end;          /* same, once all of its waves had finished their work */
+} tide_trace_rec;
+
 /* Launch options. A zero-filled struct (or a NULL pointer) means: full grid,
  * all ranks. Fields equal to 0 take their defaults. */
 typedef struct tide_launch {
@@ -98,10 +108,18 @@ typedef struct tide_launch {
     int32_t rank_end;        /* one past the last rank; 0 -> N */
     int32_t flags;           /* TIDE_FLAG_* */
     int32_t reserved;        /* must be 0 */
+    tide_trace_rec* trace;   /* optional device array: when set, every workgroup of every launch
+                                of the call writes one record, launches in order, workgroups in
+                                blockIdx order (tide_plan_trace_records gives the count) */
+    int64_t trace_capacity;  /* records `trace` holds; a call that needs more fails with
+                                INVALID_ARG before enqueuing anything */
 } tide_launch;
 
 /* Force the element-at-a-time path everywhere (for testing the slow path). */
 #define TIDE_FLAG_SCALAR_PATH 0x1
+/* BUDGETED: launch without the LDS reservation that keeps other kernels'
+ * workgroups off the CUs a budgeted workgroup holds (for measuring its effect). */
+#define TIDE_FLAG_NO_LDS_FENCE 0x2
 
 /*
  * Build the layout of one parameter group (page 3 Table 2 notation).
@@ -297,6 +315,32 @@ tide_status tide_latin_square(int32_t M, int32_t L, int32_t dst_node, int32_t sr
  * kernel engine). Host-only. */
 tide_status tide_plan_launch_count(const tide_plan* plan, int32_t op, const tide_launch* launch,
                                    int64_t* launches);
+
+/* Trace records (workgroups) a call with these options launches, for op 0
+ * (reduce-scatter), 1 (placement, kernel engine) or 2 (staging, kernel engine).
+ * Host-only. */
+tide_status tide_plan_trace_records(const tide_plan* plan, int32_t op, const tide_launch* launch,
+                                    int64_t* records);
+
+/* Trace records (workgroups) tide_landing_sum_fp32 launches with these
+ * arguments. Host-only. */
+tide_status tide_landing_trace_records(int32_t L, int32_t M, int64_t S, int32_t accumulate,
+                                       const tide_launch* launch, int64_t* records);
+
+/*
+ * Diagnostic occupant: `workgroups` workgroups of `threads` threads, each
+ * reserving `lds_bytes` of LDS, each waiting `spin_ticks` ticks of the
+ * real-time counter (a bounded wait: it ends when the counter has advanced
+ * that far) and writing one tide_trace_rec to trace[blockIdx]. Launched beside
+ * a budgeted collective, its records show whether a workgroup shaped like a
+ * GEMM's (page 3 Figure 3: one wave of 256x8192x8192) lands on a CU that a
+ * collective workgroup holds. threads: a multiple of 64 in [64, 1024];
+ * lds_bytes <= 160 KiB; spin_ticks in [0, 10^8]; trace: device array of at
+ * least `workgroups` records. Async on `stream`.
+ * Errors: INVALID_ARG (out-of-range argument, NULL trace); HIP.
+ */
+tide_status tide_diag_occupy(int32_t workgroups, int32_t threads, int32_t lds_bytes,
+                             int64_t spin_ticks, tide_trace_rec* trace, void* stream);
 
 /* Static text for a status code. */
 const char* tide_status_string(tide_status status);

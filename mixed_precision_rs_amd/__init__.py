@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     ENGINE_SDMA,
     ENGINES,
     EXPORTS,
+    FLAG_NO_LDS_FENCE,
     FLAG_SCALAR_PATH,
     LAUNCH_BUDGETED,
     LAUNCH_FULL,
@@ -20,8 +21,11 @@ from ._lib import (  # noqa: F401
     allgather_place,
     allgather_place_stage,
     budgeted,
+    decode_trace,
+    diag_occupy,
     grads_table,
     landing_sum_fp32,
+    landing_trace_records,
     latin_square,
     lib,
     params_table,
@@ -30,6 +34,8 @@ from ._lib import (  # noqa: F401
     reduce_scatter_bf16_fp32,
     slot_grads_table,
     stage_grads_bf16,
+    trace_buffer,
+    traced,
     version,
 )
 

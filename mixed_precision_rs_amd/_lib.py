@@ -23,13 +23,15 @@ ENGINES = {"kernel": 0, "runtime": 1, "sdma": 2}
 LAUNCH_FULL = 0
 LAUNCH_BUDGETED = 1
 FLAG_SCALAR_PATH = 0x1
+FLAG_NO_LDS_FENCE = 0x2
 
 # Every symbol include/tide.h declares.
 EXPORTS = ["tide_plan_create", "tide_plan_destroy", "tide_plan_dims", "tide_plan_param",
            "tide_plan_map", "tide_reduce_scatter_bf16_fp32", "tide_allgather_place",
            "tide_plan_launch_count", "tide_status_string", "tide_last_error_detail",
            "tide_version", "tide_allgather_place_stage", "tide_rd_schedule",
-           "tide_landing_sum_fp32", "tide_latin_square", "tide_stage_grads_bf16"]
+           "tide_landing_sum_fp32", "tide_latin_square", "tide_stage_grads_bf16",
+           "tide_plan_trace_records", "tide_landing_trace_records", "tide_diag_occupy"]
 
 
 class TideError(RuntimeError):
@@ -49,11 +51,45 @@ class RdStep(ctypes.Structure):
 
 
 class Launch(ctypes.Structure):
-    """tide_launch. All-zero = full grid, all ranks."""
+    """tide_launch. All-zero = full grid, all ranks. `trace` is a device
+    address (see trace_buffer) or None."""
     _fields_ = [("mode", ctypes.c_int32), ("reduce_blocks", ctypes.c_int32),
                 ("place_blocks", ctypes.c_int32), ("max_launch_us", ctypes.c_int32),
                 ("rank_begin", ctypes.c_int32), ("rank_end", ctypes.c_int32),
-                ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("trace", ctypes.c_void_p), ("trace_capacity", ctypes.c_int64)]
+
+
+TRACE_REC_BYTES = 24          # sizeof(tide_trace_rec)
+
+
+def trace_buffer(records: int):
+    """A zeroed device buffer for `records` tide_trace_rec entries (int64 x 3 each)."""
+    import torch
+    return torch.zeros(max(records, 1) * 3, dtype=torch.int64, device="cuda")
+
+
+def traced(launch: Launch, buf, records: Optional[int] = None) -> Launch:
+    """Copy of `launch` that writes its workgroup records into `buf`."""
+    out = Launch()
+    ctypes.pointer(out)[0] = launch
+    out.trace = _ptr(buf)
+    out.trace_capacity = buf.numel() // 3 if records is None else int(records)
+    return out
+
+
+def decode_trace(buf, records: int):
+    """Host copy of the first `records` entries: dict of numpy arrays
+    (cu: a chip-wide CU key from XCC_ID and HW_ID's CU / shader-array /
+    shader-engine fields; xcc; t_begin; t_end in real-time counter ticks)."""
+    import numpy as np
+    a = buf[: records * 3].view(-1, 3).cpu().numpy()
+    w0 = a[:, 0].view(np.uint64)
+    hw = (w0 & np.uint64(0xFFFFFFFF)).astype(np.uint32)
+    xcc = ((w0 >> np.uint64(32)) & np.uint64(0xF)).astype(np.uint32)
+    cu = (xcc << np.uint32(8)) | ((hw >> np.uint32(8)) & np.uint32(0xFF))
+    return {"cu": cu, "xcc": xcc, "hw_id": hw, "t_begin": a[:, 1].view(np.uint64),
+            "t_end": a[:, 2].view(np.uint64)}
 
 
 def budgeted(reduce_blocks=16, place_blocks=4, max_launch_us=300, **kw) -> Launch:
@@ -107,6 +143,12 @@ def _load():
                                       ctypes.c_int32, _I32P, _I32P, _I32P]
     lib.tide_stage_grads_bf16.argtypes = [ctypes.c_void_p, _VPP, _VPP, ctypes.c_void_p,
                                           ctypes.c_int32, ctypes.POINTER(Launch)]
+    lib.tide_plan_trace_records.argtypes = [ctypes.c_void_p, ctypes.c_int32,
+                                            ctypes.POINTER(Launch), _I64P]
+    lib.tide_landing_trace_records.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                               ctypes.c_int32, ctypes.POINTER(Launch), _I64P]
+    lib.tide_diag_occupy.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     lib.tide_status_string.argtypes = [ctypes.c_int]
     lib.tide_status_string.restype = ctypes.c_char_p
     lib.tide_last_error_detail.argtypes = []
@@ -116,7 +158,8 @@ def _load():
     for f in ("tide_plan_create", "tide_plan_dims", "tide_plan_param", "tide_plan_map",
               "tide_reduce_scatter_bf16_fp32", "tide_allgather_place", "tide_plan_launch_count",
               "tide_allgather_place_stage", "tide_rd_schedule", "tide_landing_sum_fp32",
-              "tide_latin_square", "tide_stage_grads_bf16"):
+              "tide_latin_square", "tide_stage_grads_bf16", "tide_plan_trace_records",
+              "tide_landing_trace_records", "tide_diag_occupy"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -197,6 +240,14 @@ class Plan:
         _check(_load().tide_plan_map(self._h, r, p, *[ctypes.byref(x) for x in v]),
                "tide_plan_map")
         return tuple(int(x.value) for x in v)
+
+    def trace_records(self, op: int, launch: Optional[Launch] = None) -> int:
+        """Workgroups (trace records) a call of op 0 / 1 / 2 launches."""
+        n = ctypes.c_int64()
+        _check(_load().tide_plan_trace_records(self._h, op,
+                                               ctypes.byref(launch) if launch is not None else None,
+                                               ctypes.byref(n)), "tide_plan_trace_records")
+        return int(n.value)
 
     def launch_count(self, op: int, launch: Optional[Launch] = None) -> int:
         n = ctypes.c_int64()
@@ -367,6 +418,24 @@ def landing_sum_fp32(L: int, M: int, S: int, inboxes: Sequence[object], shards: 
                                        ctypes.byref(launch) if launch is not None else None)
     _check(st, "tide_landing_sum_fp32")
     _record(list(inboxes) + list(shards), sobj)
+
+
+def landing_trace_records(L: int, M: int, S: int, accumulate: bool = False,
+                          launch: Optional[Launch] = None) -> int:
+    n = ctypes.c_int64()
+    _check(_load().tide_landing_trace_records(L, M, S, 1 if accumulate else 0,
+                                              ctypes.byref(launch) if launch is not None else None,
+                                              ctypes.byref(n)), "tide_landing_trace_records")
+    return int(n.value)
+
+
+def diag_occupy(workgroups: int, threads: int, lds_bytes: int, spin_ticks: int, trace,
+                stream=None) -> None:
+    """tide_diag_occupy: a GEMM-shaped occupant that records where it ran."""
+    sh, sobj = _stream_handle(stream)
+    _check(_load().tide_diag_occupy(workgroups, threads, lds_bytes, spin_ticks, _ptr(trace), sh),
+           "tide_diag_occupy")
+    _record([trace], sobj)
 
 
 def latin_square(M: int, L: int, dst_node: int, src_node: int):

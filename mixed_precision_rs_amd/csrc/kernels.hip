@@ -198,6 +198,29 @@ __device__ __forceinline__ void store_run(const Span& t, const ParamDev& pd, int
     TIDE_ST(x, reinterpret_cast<f32x4_a4*>(out + r * stride + pd.o + j + 4 * lane));
 }
 
+// Workgroup tracing (tide_launch.trace): the real-time counter at the start,
+// and at the end, once every wave of the workgroup is done, one record with
+// the hardware ids of the CU it ran on. `trace` is a kernel argument, so the
+// branches are uniform and cost nothing when it is null.
+constexpr int kHwregAll = 31 << 11;            // s_getreg: 32 bits from offset 0
+constexpr int kHwregHwId = kHwregAll | 4;      // HW_ID
+constexpr int kHwregXccId = kHwregAll | 20;    // XCC_ID
+__device__ __forceinline__ uint64_t trace_begin(const tide_trace_rec* trace) {
+    return trace ? __builtin_amdgcn_s_memrealtime() : 0;
+}
+__device__ __forceinline__ void trace_end(tide_trace_rec* trace, int64_t base, uint64_t t_begin) {
+    if (!trace) return;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        tide_trace_rec r;
+        r.hw_id = __builtin_amdgcn_s_getreg(kHwregHwId);
+        r.xcc_id = __builtin_amdgcn_s_getreg(kHwregXccId);
+        r.t_begin = t_begin;
+        r.t_end = __builtin_amdgcn_s_memrealtime();
+        trace[base + blockIdx.x] = r;
+    }
+}
+
 // Reduce: out[rank piece] = fold_c widen(g[c][f]) for f < valid, +0 past it.
 // LT > 0: L known at compile time (fully unrolled); LT == 0: runtime L.
 // A workgroup of NT threads is NT / kThreads independent quarters of kThreads
@@ -206,7 +229,9 @@ template <int LT, int NT>
 __global__ __launch_bounds__(NT) void reduce_kernel(
     const TileRec* __restrict__ tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb, int32_t re,
     const ParamDev* __restrict__ params, const uint16_t* const* __restrict__ ptrs,
-    const uint32_t* __restrict__ flags, int Lrt, float* __restrict__ out, int64_t out_stride) {
+    const uint32_t* __restrict__ flags, int Lrt, float* __restrict__ out, int64_t out_stride,
+    tide_trace_rec* __restrict__ trace, int64_t trace_base) {
+    const uint64_t t_begin = trace_begin(trace);
     constexpr int kSubs = NT / kThreads;
     const int L = LT > 0 ? LT : Lrt;
     const int sub = (int)threadIdx.x / kThreads;          // wave-uniform
@@ -379,6 +404,7 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
             }
         }
     }
+    trace_end(trace, trace_base, t_begin);
 }
 
 // Position of rank r's shard in a stage buffer that starts with rank first.
@@ -431,7 +457,9 @@ __global__ __launch_bounds__(NT) void place_kernel(
     const TileRec* __restrict__ tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb, int32_t re,
     const ParamDev* __restrict__ params, uint16_t* const* __restrict__ ptrs,
     const uint32_t* __restrict__ flags, const uint16_t* __restrict__ shards, int64_t stride,
-    int64_t shard_elems, int32_t first, int32_t nranks) {
+    int64_t shard_elems, int32_t first, int32_t nranks, tide_trace_rec* __restrict__ trace,
+    int64_t trace_base) {
+    const uint64_t t_begin = trace_begin(trace);
     constexpr int kSubs = NT / kThreads;
     const int sub = (int)threadIdx.x / kThreads;
     const int tid = (int)threadIdx.x % kThreads;
@@ -486,6 +514,7 @@ __global__ __launch_bounds__(NT) void place_kernel(
             }
         }
     }
+    trace_end(trace, trace_base, t_begin);
 }
 
 // Slot-Reuse staging: dst[p][c][f] = src[p][c][f] for the launch's true
@@ -502,7 +531,9 @@ __global__ __launch_bounds__(NT) void stage_kernel(
     const TileRec* __restrict__ tiles, int64_t ntiles, int64_t tile_lo, int64_t tile_hi,
     int32_t rb, int32_t re, const ParamDev* __restrict__ params,
     const uint16_t* const* __restrict__ src, uint16_t* const* __restrict__ dst,
-    const uint32_t* __restrict__ flags, int32_t L) {
+    const uint32_t* __restrict__ flags, int32_t L, tide_trace_rec* __restrict__ trace,
+    int64_t trace_base) {
+    const uint64_t t_begin = trace_begin(trace);
     constexpr int kSubs = NT / kThreads;
     const int sub = (int)threadIdx.x / kThreads;
     const int tid = (int)threadIdx.x % kThreads;
@@ -560,6 +591,7 @@ __global__ __launch_bounds__(NT) void stage_kernel(
             }
         }
     }
+    trace_end(trace, trace_base, t_begin);
 }
 
 // Level-2 landing sum: shard_b[f] = fold_c inbox_{(s - c) mod L}[(s L + b) C + e]
@@ -570,7 +602,10 @@ template <int MT, int NT>
 __global__ __launch_bounds__(NT) void landing_kernel(LandingPtrs ptrs, int32_t L, int32_t Mrt,
                                                      int64_t S, int64_t C, int64_t tiles_per_shard,
                                                      int64_t tile_lo, int64_t tile_hi,
-                                                     int32_t accumulate, int32_t scalar) {
+                                                     int32_t accumulate, int32_t scalar,
+                                                     tide_trace_rec* __restrict__ trace,
+                                                     int64_t trace_base) {
+    const uint64_t t_begin = trace_begin(trace);
     constexpr int kSubs = NT / kThreads;
     const int M = MT > 0 ? MT : Mrt;
     const int sub = (int)threadIdx.x / kThreads;
@@ -620,17 +655,28 @@ __global__ __launch_bounds__(NT) void landing_kernel(LandingPtrs ptrs, int32_t L
             }
         }
     }
+    trace_end(trace, trace_base, t_begin);
+}
+
+// Diagnostic occupant (tide_diag_occupy): holds its CU's resources (threads,
+// the dynamic LDS of the launch) for spin_ticks of the real-time counter, then
+// records where it ran. The wait is bounded by the counter, so it always ends.
+__global__ __launch_bounds__(1024) void occupy_kernel(int64_t spin_ticks, tide_trace_rec* trace) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) < spin_ticks) __builtin_amdgcn_s_sleep(2);
+    trace_end(trace, 0, t0);
 }
 
 template <int MT>
 hipError_t launch_landing_t(int M, int grid, int threads, size_t lds, hipStream_t stream,
                             const LandingPtrs& ptrs, int32_t L, int64_t S, int64_t C,
                             int64_t tiles_per_shard, int64_t tile_lo, int64_t tile_hi,
-                            int32_t accumulate, int32_t scalar) {
+                            int32_t accumulate, int32_t scalar, tide_trace_rec* trace,
+                            int64_t trace_base) {
     LandingPtrs p = ptrs;
     int32_t Mrt = M;
     void* args[] = {&p, &L, &Mrt, &S, &C, &tiles_per_shard, &tile_lo, &tile_hi, &accumulate,
-                    &scalar};
+                    &scalar, &trace, &trace_base};
     const void* fn = threads == kFatThreads
                          ? reinterpret_cast<const void*>(&landing_kernel<MT, kFatThreads>)
                          : reinterpret_cast<const void*>(&landing_kernel<MT, kThreads>);
@@ -641,9 +687,10 @@ template <int LT>
 hipError_t launch_reduce_t(int L, int grid, int threads, size_t lds, hipStream_t stream,
                            const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                            int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
-                           const uint32_t* flags, float* out, int64_t out_stride) {
+                           const uint32_t* flags, float* out, int64_t out_stride,
+                           tide_trace_rec* trace, int64_t trace_base) {
     void* args[] = {&tiles, &tile_lo, &tile_hi, &rb, &re, &params, &ptrs, &flags, &L, &out,
-                    &out_stride};
+                    &out_stride, &trace, &trace_base};
     const void* fn = threads == kFatThreads
                          ? reinterpret_cast<const void*>(&reduce_kernel<LT, kFatThreads>)
                          : reinterpret_cast<const void*>(&reduce_kernel<LT, kThreads>);
@@ -655,11 +702,12 @@ hipError_t launch_reduce_t(int L, int grid, int threads, size_t lds, hipStream_t
 hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t stream,
                          const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                          int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
-                         const uint32_t* flags, float* out, int64_t out_stride) {
+                         const uint32_t* flags, float* out, int64_t out_stride,
+                         tide_trace_rec* trace, int64_t trace_base) {
 #define TIDE_REDUCE_CASE(n)                                                                   \
     case n:                                                                                   \
         return launch_reduce_t<n>(L, grid, threads, lds, stream, tiles, tile_lo, tile_hi, rb, \
-                                  re, params, ptrs, flags, out, out_stride);
+                                  re, params, ptrs, flags, out, out_stride, trace, trace_base);
     switch (L) {
         TIDE_REDUCE_CASE(1)
         TIDE_REDUCE_CASE(2)
@@ -671,7 +719,7 @@ hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t s
         TIDE_REDUCE_CASE(8)
         default:
             return launch_reduce_t<0>(L, grid, threads, lds, stream, tiles, tile_lo, tile_hi, rb,
-                                      re, params, ptrs, flags, out, out_stride);
+                                      re, params, ptrs, flags, out, out_stride, trace, trace_base);
     }
 #undef TIDE_REDUCE_CASE
 }
@@ -680,9 +728,10 @@ hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
                         const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                         int32_t re, const ParamDev* params, uint16_t* const* ptrs,
                         const uint32_t* flags, const uint16_t* shards, int64_t shard_stride,
-                        int64_t shard_elems, int32_t first_rank, int32_t nranks) {
+                        int64_t shard_elems, int32_t first_rank, int32_t nranks,
+                        tide_trace_rec* trace, int64_t trace_base) {
     void* args[] = {&tiles, &tile_lo, &tile_hi, &rb, &re, &params, &ptrs, &flags, &shards,
-                    &shard_stride, &shard_elems, &first_rank, &nranks};
+                    &shard_stride, &shard_elems, &first_rank, &nranks, &trace, &trace_base};
     const void* fn = threads == kFatThreads
                          ? reinterpret_cast<const void*>(&place_kernel<kFatThreads>)
                          : reinterpret_cast<const void*>(&place_kernel<kThreads>);
@@ -693,9 +742,9 @@ hipError_t launch_stage(int grid, int threads, size_t lds, hipStream_t stream,
                         const TileRec* tiles, int64_t ntiles, int64_t tile_lo, int64_t tile_hi,
                         int32_t rb, int32_t re, const ParamDev* params,
                         const uint16_t* const* src, uint16_t* const* dst, const uint32_t* flags,
-                        int32_t L) {
+                        int32_t L, tide_trace_rec* trace, int64_t trace_base) {
     void* args[] = {&tiles, &ntiles, &tile_lo, &tile_hi, &rb, &re, &params, &src, &dst, &flags,
-                    &L};
+                    &L, &trace, &trace_base};
     const void* fn = threads == kFatThreads
                          ? reinterpret_cast<const void*>(&stage_kernel<kFatThreads>)
                          : reinterpret_cast<const void*>(&stage_kernel<kThreads>);
@@ -705,11 +754,13 @@ hipError_t launch_stage(int grid, int threads, size_t lds, hipStream_t stream,
 hipError_t launch_landing(int M, int grid, int threads, size_t lds, hipStream_t stream,
                           const LandingPtrs& ptrs, int32_t L, int64_t S, int64_t C,
                           int64_t tiles_per_shard, int64_t tile_lo, int64_t tile_hi,
-                          int32_t accumulate, int32_t scalar) {
+                          int32_t accumulate, int32_t scalar, tide_trace_rec* trace,
+                          int64_t trace_base) {
 #define TIDE_LANDING_CASE(n)                                                                  \
     case n:                                                                                   \
         return launch_landing_t<n>(M, grid, threads, lds, stream, ptrs, L, S, C,             \
-                                   tiles_per_shard, tile_lo, tile_hi, accumulate, scalar);
+                                   tiles_per_shard, tile_lo, tile_hi, accumulate, scalar,     \
+                                   trace, trace_base);
     switch (M) {
         TIDE_LANDING_CASE(1)
         TIDE_LANDING_CASE(2)
@@ -721,9 +772,21 @@ hipError_t launch_landing(int M, int grid, int threads, size_t lds, hipStream_t 
         TIDE_LANDING_CASE(8)
         default:
             return launch_landing_t<0>(M, grid, threads, lds, stream, ptrs, L, S, C,
-                                       tiles_per_shard, tile_lo, tile_hi, accumulate, scalar);
+                                       tiles_per_shard, tile_lo, tile_hi, accumulate, scalar,
+                                       trace, trace_base);
     }
 #undef TIDE_LANDING_CASE
+}
+
+hipError_t launch_occupy(int grid, int threads, size_t lds, hipStream_t stream, int64_t spin_ticks,
+                         tide_trace_rec* trace) {
+    const void* fn = reinterpret_cast<const void*>(&occupy_kernel);
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    void* args[] = {&spin_ticks, &trace};
+    return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, lds, stream);
 }
 
 hipError_t allow_dynamic_lds_landing(int M, size_t lds) {

@@ -83,6 +83,7 @@ constexpr int kFullGridCap = TIDE_FULL_GRID_CAP;
 #define TIDE_RS_GROUP_ELEMS (1 << 20)
 #endif
 constexpr int kRingSlots = 8;
+constexpr int32_t kKnownFlags = TIDE_FLAG_SCALAR_PATH | TIDE_FLAG_NO_LDS_FENCE;
 
 struct TileTable {
     TileRec* dev = nullptr;
@@ -158,8 +159,9 @@ tide_status resolve_launch(const tide_plan* plan, const tide_launch* in, tide_la
         return fail(TIDE_ERR_INVALID_ARG, "launch.mode %d is not FULL (0) or BUDGETED (1)", l.mode);
     if (l.reduce_blocks < 0 || l.place_blocks < 0 || l.max_launch_us < 0)
         return fail(TIDE_ERR_INVALID_ARG, "negative launch budget");
-    if (l.reserved != 0 || (l.flags & ~TIDE_FLAG_SCALAR_PATH) != 0)
+    if (l.reserved != 0 || (l.flags & ~kKnownFlags) != 0)
         return fail(TIDE_ERR_INVALID_ARG, "unknown launch flags 0x%x", l.flags);
+    if (l.trace_capacity < 0) return fail(TIDE_ERR_INVALID_ARG, "negative trace_capacity");
     if (l.reduce_blocks == 0) l.reduce_blocks = kDefaultReduceBlocks;
     if (l.place_blocks == 0) l.place_blocks = kDefaultPlaceBlocks;
     if (l.max_launch_us == 0) l.max_launch_us = kDefaultMaxLaunchUs;
@@ -434,14 +436,36 @@ tide_status for_each_launch(const tide_plan* plan, int op, const tide_launch& l,
         grid_cap = blocks;
     }
     const int threads = l.mode == TIDE_LAUNCH_FULL ? kThreads : kBudgetThreads;
-    const size_t lds = l.mode == TIDE_LAUNCH_FULL ? 0 : kBudgetLds;
+    const size_t lds =
+        l.mode == TIDE_LAUNCH_FULL || (l.flags & TIDE_FLAG_NO_LDS_FENCE) ? 0 : kBudgetLds;
+    int64_t trace_base = 0;
     for (int64_t lo = 0; lo < ntiles; lo += per_launch) {
         const int64_t hi = std::min(ntiles, lo + per_launch);
         const int grid = (int)std::min<int64_t>(grid_cap, hi - lo);
-        hipError_t e = launch(grid, threads, lds, lo, hi);
+        hipError_t e = launch(grid, threads, lds, lo, hi, trace_base);
+        trace_base += grid;
         if (e != hipSuccess)
             return hip_fail(e, op == 0 ? "reduce launch" : op == 1 ? "place launch" : "stage launch");
     }
+    return TIDE_OK;
+}
+
+// Workgroups (trace records) of all launches for_each_launch makes.
+int64_t launch_records(const tide_plan* plan, int op, const tide_launch& l, int64_t ntiles) {
+    int64_t n = 0;
+    (void)for_each_launch(plan, op, l, ntiles,
+                          [&](int grid, int, size_t, int64_t, int64_t, int64_t) {
+        n += grid;
+        return hipSuccess;
+    });
+    return n;
+}
+
+// A traced call must have room for every record before anything is enqueued.
+tide_status check_trace(const tide_launch& l, int64_t records) {
+    if (l.trace && records > l.trace_capacity)
+        return fail(TIDE_ERR_INVALID_ARG, "trace holds %lld records, the call needs %lld",
+                    (long long)l.trace_capacity, (long long)records);
     return TIDE_OK;
 }
 
@@ -610,6 +634,8 @@ tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t*
         st = get_tiles(plan, ds, 0, l.rank_begin, l.rank_end, &tt);
         if (st != TIDE_OK) return st;
         if (tt->count == 0) return TIDE_OK;
+        st = check_trace(l, launch_records(plan, 0, l, tt->count));
+        if (st != TIDE_OK) return st;
         int slot;
         st = stage_table(ds, table.data(), table.size(), stream, &slot);
         if (st != TIDE_OK) return st;
@@ -620,9 +646,11 @@ tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t*
         st = prepare_budget(ds, L, l);
         if (st != TIDE_OK) return st;
         st = for_each_launch(plan, 0, l, tt->count,
-                             [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi) {
+                             [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi,
+                                 int64_t tb) {
             return launch_reduce(L, grid, threads, lds, stream, tt->dev, lo, hi, l.rank_begin,
-                                 l.rank_end, ds->params, dptrs, dflags, out, out_stride);
+                                 l.rank_end, ds->params, dptrs, dflags, out, out_stride, l.trace,
+                                 tb);
         });
         tide_status st2 = release_slot(ds, slot, stream);
         return st != TIDE_OK ? st : st2;
@@ -745,6 +773,8 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* sh
         st = get_tiles(plan, ds, 1, l.rank_begin, l.rank_end, &tt);
         if (st != TIDE_OK) return st;
         if (tt->count == 0) return TIDE_OK;
+        st = check_trace(l, launch_records(plan, 1, l, tt->count));
+        if (st != TIDE_OK) return st;
         int slot;
         st = stage_table(ds, table.data(), table.size(), stream, &slot);
         if (st != TIDE_OK) return st;
@@ -754,10 +784,11 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* sh
         st = prepare_budget(ds, plan->L, l);
         if (st != TIDE_OK) return st;
         st = for_each_launch(plan, 1, l, tt->count,
-                             [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi) {
+                             [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi,
+                                 int64_t tb) {
             return launch_place(grid, threads, lds, stream, tt->dev, lo, hi, l.rank_begin,
                                 l.rank_end, ds->params, dptrs, dflags, shards, shard_stride,
-                                shard_elems, first_rank, plan->N);
+                                shard_elems, first_rank, plan->N, l.trace, tb);
         });
         tide_status st2 = release_slot(ds, slot, stream);
         return st != TIDE_OK ? st : st2;
@@ -856,6 +887,8 @@ tide_status tide_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* 
         st = get_tiles(plan, ds, 2, l.rank_begin, l.rank_end, &tt);
         if (st != TIDE_OK) return st;
         if (tt->count == 0) return TIDE_OK;
+        st = check_trace(l, launch_records(plan, 2, l, tt->count * L));
+        if (st != TIDE_OK) return st;
         int slot;
         st = stage_table(ds, table.data(), table.size(), stream, &slot);
         if (st != TIDE_OK) return st;
@@ -867,9 +900,10 @@ tide_status tide_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* 
         if (st != TIDE_OK) return st;
         const int64_t ntiles = tt->count;
         st = for_each_launch(plan, 2, l, ntiles * L,
-                             [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi) {
+                             [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi,
+                                 int64_t tb) {
             return launch_stage(grid, threads, lds, stream, tt->dev, ntiles, lo, hi, l.rank_begin,
-                                l.rank_end, ds->params, dsrc, ddst, dflags, L);
+                                l.rank_end, ds->params, dsrc, ddst, dflags, L, l.trace, tb);
         });
         tide_status st2 = release_slot(ds, slot, stream);
         return st != TIDE_OK ? st : st2;
@@ -894,28 +928,88 @@ tide_status tide_latin_square(int32_t M, int32_t L, int32_t dst_node, int32_t sr
     return TIDE_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The landing sum's launches: each is (grid, threads, lds, tile_lo, tile_hi).
+template <typename F>
+hipError_t for_each_landing_launch(int32_t L, int32_t M, int64_t S, int32_t accumulate,
+                                   const tide_launch& l, F&& launch) {
+    const int64_t tiles_per_shard = (S + kLandTile - 1) / kLandTile;
+    const int64_t ntiles = tiles_per_shard * L;
+    if (ntiles == 0) return hipSuccess;
+    if (l.mode == TIDE_LAUNCH_FULL)
+        return launch((int)std::min<int64_t>(ntiles, kFullGridCap), kThreads, (size_t)0,
+                      (int64_t)0, ntiles, (int64_t)0);
+    const size_t lds = (l.flags & TIDE_FLAG_NO_LDS_FENCE) ? 0 : kBudgetLds;
+    const int64_t tile_b = kLandTile * (4 * (int64_t)M + 4 + 4 * accumulate);
+    const int64_t per_block = std::max<int64_t>(1, (int64_t)l.max_launch_us * kWgBytesPerUs / tile_b);
+    const int64_t per_launch = (int64_t)l.place_blocks * per_block;
+    int64_t base = 0;
+    for (int64_t lo = 0; lo < ntiles; lo += per_launch) {
+        const int64_t hi = std::min(ntiles, lo + per_launch);
+        const int grid = (int)std::min<int64_t>(l.place_blocks, hi - lo);
+        hipError_t e = launch(grid, kBudgetThreads, lds, lo, hi, base);
+        if (e != hipSuccess) return e;
+        base += grid;
+    }
+    return hipSuccess;
+}
+
+// Validates and completes the landing sum's launch options.
+tide_status landing_launch(int32_t L, int32_t M, int64_t S, int32_t accumulate,
+                           const tide_launch* launch, tide_launch* out) {
+    if (L < 1 || L > kMaxLanding)
+        return fail(TIDE_ERR_INVALID_ARG, "L = %d not in [1, %d]", L, kMaxLanding);
+    if (M < 1 || M > L) return fail(TIDE_ERR_INVALID_ARG, "M = %d not in [1, L = %d]", M, L);
+    if (S < 0) return fail(TIDE_ERR_INVALID_ARG, "S = %lld < 0", (long long)S);
+    if (accumulate != 0 && accumulate != 1)
+        return fail(TIDE_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+    tide_launch l{};
+    if (launch) l = *launch;
+    if (l.rank_begin != 0 || l.rank_end != 0)
+        return fail(TIDE_ERR_INVALID_ARG, "rank_begin / rank_end do not apply to the landing sum");
+    if (l.mode != TIDE_LAUNCH_FULL && l.mode != TIDE_LAUNCH_BUDGETED)
+        return fail(TIDE_ERR_INVALID_ARG, "launch.mode %d is not FULL (0) or BUDGETED (1)", l.mode);
+    if (l.reduce_blocks < 0 || l.place_blocks < 0 || l.max_launch_us < 0)
+        return fail(TIDE_ERR_INVALID_ARG, "negative launch budget");
+    if (l.reserved != 0 || (l.flags & ~kKnownFlags) != 0)
+        return fail(TIDE_ERR_INVALID_ARG, "unknown launch flags 0x%x", l.flags);
+    if (l.trace_capacity < 0) return fail(TIDE_ERR_INVALID_ARG, "negative trace_capacity");
+    if (l.place_blocks == 0) l.place_blocks = kDefaultPlaceBlocks;
+    if (l.max_launch_us == 0) l.max_launch_us = kDefaultMaxLaunchUs;
+    *out = l;
+    return TIDE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tide_status tide_landing_trace_records(int32_t L, int32_t M, int64_t S, int32_t accumulate,
+                                       const tide_launch* launch, int64_t* records) {
+    if (!records) return fail(TIDE_ERR_INVALID_ARG, "records is NULL");
+    tide_launch l;
+    tide_status st = landing_launch(L, M, S, accumulate, launch, &l);
+    if (st != TIDE_OK) return st;
+    int64_t n = 0;
+    (void)for_each_landing_launch(L, M, S, accumulate, l,
+                                  [&](int grid, int, size_t, int64_t, int64_t, int64_t) {
+        n += grid;
+        return hipSuccess;
+    });
+    *records = n;
+    return TIDE_OK;
+}
+
 tide_status tide_landing_sum_fp32(int32_t L, int32_t M, int64_t S, const float* const* inboxes,
                                   float* const* shards, int32_t accumulate, void* stream_v,
                                   const tide_launch* launch) {
     try {
-        if (L < 1 || L > kMaxLanding)
-            return fail(TIDE_ERR_INVALID_ARG, "L = %d not in [1, %d]", L, kMaxLanding);
-        if (M < 1 || M > L) return fail(TIDE_ERR_INVALID_ARG, "M = %d not in [1, L = %d]", M, L);
-        if (S < 0) return fail(TIDE_ERR_INVALID_ARG, "S = %lld < 0", (long long)S);
-        if (accumulate != 0 && accumulate != 1)
-            return fail(TIDE_ERR_INVALID_ARG, "accumulate must be 0 or 1");
-        tide_launch l{};
-        if (launch) l = *launch;
-        if (l.rank_begin != 0 || l.rank_end != 0)
-            return fail(TIDE_ERR_INVALID_ARG, "rank_begin / rank_end do not apply to the landing sum");
-        if (l.mode != TIDE_LAUNCH_FULL && l.mode != TIDE_LAUNCH_BUDGETED)
-            return fail(TIDE_ERR_INVALID_ARG, "launch.mode %d is not FULL (0) or BUDGETED (1)", l.mode);
-        if (l.reduce_blocks < 0 || l.place_blocks < 0 || l.max_launch_us < 0)
-            return fail(TIDE_ERR_INVALID_ARG, "negative launch budget");
-        if (l.reserved != 0 || (l.flags & ~TIDE_FLAG_SCALAR_PATH) != 0)
-            return fail(TIDE_ERR_INVALID_ARG, "unknown launch flags 0x%x", l.flags);
-        if (l.place_blocks == 0) l.place_blocks = kDefaultPlaceBlocks;
-        if (l.max_launch_us == 0) l.max_launch_us = kDefaultMaxLaunchUs;
+        tide_launch l;
+        tide_status st = landing_launch(L, M, S, accumulate, launch, &l);
+        if (st != TIDE_OK) return st;
         if (S == 0) return TIDE_OK;
         if (!inboxes || !shards) return fail(TIDE_ERR_INVALID_ARG, "inboxes / shards is NULL");
         const int64_t C = S / L + (S % L != 0);
@@ -942,20 +1036,21 @@ tide_status tide_landing_sum_fp32(int32_t L, int32_t M, int64_t S, const float* 
             for (const Range& r : rd)
                 if (overlaps(w, r))
                     return fail(TIDE_ERR_INVALID_ARG, "shards[%d] overlaps inboxes[%d]", w.who, r.who);
+        int64_t records = 0;
+        (void)for_each_landing_launch(L, M, S, accumulate, l,
+                                      [&](int grid, int, size_t, int64_t, int64_t, int64_t) {
+            records += grid;
+            return hipSuccess;
+        });
+        st = check_trace(l, records);
+        if (st != TIDE_OK) return st;
         hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
         const int64_t tiles_per_shard = (S + kLandTile - 1) / kLandTile;
-        const int64_t ntiles = tiles_per_shard * L;
         const int32_t scalar = (l.flags & TIDE_FLAG_SCALAR_PATH) ? 1 : 0;
-        if (l.mode == TIDE_LAUNCH_FULL) {
-            const int grid = (int)std::min<int64_t>(ntiles, kFullGridCap);
-            TIDE_HIP_TRY(launch_landing(M, grid, kThreads, 0, stream, ptrs, L, S, C,
-                                        tiles_per_shard, 0, ntiles, accumulate, scalar));
-            return TIDE_OK;
-        }
-        if (kBudgetLds > 0) {
+        if (l.mode == TIDE_LAUNCH_BUDGETED && kBudgetLds > 0 && !(l.flags & TIDE_FLAG_NO_LDS_FENCE)) {
             std::lock_guard<std::mutex> lock(g_landing_lds_mu);
             int dev = 0;
-            tide_status st = stream_device(stream, &dev);
+            st = stream_device(stream, &dev);
             if (st != TIDE_OK) return st;
             const int key = M <= 8 ? M : 0;
             const uint64_t bit = (uint64_t)1 << key;
@@ -964,15 +1059,11 @@ tide_status tide_landing_sum_fp32(int32_t L, int32_t M, int64_t S, const float* 
                 g_landing_lds_done[dev] |= bit;
             }
         }
-        const int64_t tile_b = kLandTile * (4 * (int64_t)M + 4 + 4 * accumulate);
-        const int64_t per_block = std::max<int64_t>(1, (int64_t)l.max_launch_us * kWgBytesPerUs / tile_b);
-        const int64_t per_launch = (int64_t)l.place_blocks * per_block;
-        for (int64_t lo = 0; lo < ntiles; lo += per_launch) {
-            const int64_t hi = std::min(ntiles, lo + per_launch);
-            const int grid = (int)std::min<int64_t>(l.place_blocks, hi - lo);
-            TIDE_HIP_TRY(launch_landing(M, grid, kBudgetThreads, kBudgetLds, stream, ptrs, L, S, C,
-                                        tiles_per_shard, lo, hi, accumulate, scalar));
-        }
+        TIDE_HIP_TRY(for_each_landing_launch(L, M, S, accumulate, l,
+                     [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi, int64_t tb) {
+            return launch_landing(M, grid, threads, lds, stream, ptrs, L, S, C, tiles_per_shard,
+                                  lo, hi, accumulate, scalar, l.trace, tb);
+        }));
         return TIDE_OK;
     } catch (const std::bad_alloc&) {
         return fail(TIDE_ERR_NO_MEMORY, "host allocation failed");
@@ -1029,5 +1120,39 @@ const char* tide_status_string(tide_status s) {
 const char* tide_last_error_detail(void) { return g_detail.c_str(); }
 
 int32_t tide_version(void) { return (1 << 16) | 0; }
+
+tide_status tide_plan_trace_records(const tide_plan* plan, int32_t op, const tide_launch* launch,
+                                    int64_t* records) {
+    try {
+        if (!plan || !records) return fail(TIDE_ERR_INVALID_ARG, "NULL argument");
+        if (op < 0 || op > 2) return fail(TIDE_ERR_INVALID_ARG, "op %d not 0, 1 or 2", op);
+        tide_launch l;
+        tide_status st = resolve_launch(plan, launch, &l);
+        if (st != TIDE_OK) return st;
+        int64_t n = (int64_t)build_tiles(plan, op, l.rank_begin, l.rank_end).size();
+        if (op == 2) n *= plan->L;
+        *records = launch_records(plan, op, l, n);
+        return TIDE_OK;
+    } catch (const std::bad_alloc&) {
+        return fail(TIDE_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return fail(TIDE_ERR_INVALID_ARG, "unexpected exception");
+    }
+}
+
+tide_status tide_diag_occupy(int32_t workgroups, int32_t threads, int32_t lds_bytes,
+                             int64_t spin_ticks, tide_trace_rec* trace, void* stream_v) {
+    if (workgroups < 1) return fail(TIDE_ERR_INVALID_ARG, "workgroups = %d < 1", workgroups);
+    if (threads < 64 || threads > 1024 || threads % 64)
+        return fail(TIDE_ERR_INVALID_ARG, "threads = %d is not a multiple of 64 in [64, 1024]", threads);
+    if (lds_bytes < 0 || lds_bytes > 160 * 1024)
+        return fail(TIDE_ERR_INVALID_ARG, "lds_bytes = %d not in [0, 160 KiB]", lds_bytes);
+    if (spin_ticks < 0 || spin_ticks > 100000000)
+        return fail(TIDE_ERR_INVALID_ARG, "spin_ticks = %lld not in [0, 1e8]", (long long)spin_ticks);
+    if (!trace) return fail(TIDE_ERR_INVALID_ARG, "trace is NULL");
+    TIDE_HIP_TRY(launch_occupy(workgroups, threads, (size_t)lds_bytes,
+                               reinterpret_cast<hipStream_t>(stream_v), spin_ticks, trace));
+    return TIDE_OK;
+}
 
 }  // extern "C"

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tide.h"
+
 namespace tide {
 
 // Tuning knobs (overridable at build time for measurement sweeps). Defaults
@@ -76,17 +78,21 @@ constexpr uint32_t kFlagVector = 1u;  // every pointer of this parameter allows 
 
 // Launch wrappers (kernels.hip). threads is kThreads or kFatThreads; lds is
 // dynamic LDS reserved per workgroup (unused by the kernels: it only keeps
-// other kernels' workgroups off the CU). Return the launch's hipError_t.
+// other kernels' workgroups off the CU). trace, when not null, receives one
+// record per workgroup at trace[trace_base + blockIdx.x]. Return the launch's
+// hipError_t.
 hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t stream,
                          const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                          int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
-                         const uint32_t* flags, float* out, int64_t out_stride);
+                         const uint32_t* flags, float* out, int64_t out_stride,
+                         tide_trace_rec* trace, int64_t trace_base);
 
 hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
                         const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                         int32_t re, const ParamDev* params, uint16_t* const* ptrs,
                         const uint32_t* flags, const uint16_t* shards, int64_t shard_stride,
-                        int64_t shard_elems, int32_t first_rank, int32_t nranks);
+                        int64_t shard_elems, int32_t first_rank, int32_t nranks,
+                        tide_trace_rec* trace, int64_t trace_base);
 
 // Slot-Reuse staging (kernels.hip): tiles [tile_lo, tile_hi) of L copies of
 // the staging tiling (ntiles tiles of kStageTile elements over each
@@ -96,7 +102,7 @@ hipError_t launch_stage(int grid, int threads, size_t lds, hipStream_t stream,
                         const TileRec* tiles, int64_t ntiles, int64_t tile_lo, int64_t tile_hi,
                         int32_t rb, int32_t re, const ParamDev* params,
                         const uint16_t* const* src, uint16_t* const* dst, const uint32_t* flags,
-                        int32_t L);
+                        int32_t L, tide_trace_rec* trace, int64_t trace_base);
 
 // Level-2 landing sum (kernels.hip). The node's inbox and shard pointers travel
 // in the kernel arguments (at most kMaxLanding GPUs per node).
@@ -109,7 +115,11 @@ struct LandingPtrs {
 hipError_t launch_landing(int M, int grid, int threads, size_t lds, hipStream_t stream,
                           const LandingPtrs& ptrs, int32_t L, int64_t S, int64_t C,
                           int64_t tiles_per_shard, int64_t tile_lo, int64_t tile_hi,
-                          int32_t accumulate, int32_t scalar);
+                          int32_t accumulate, int32_t scalar, tide_trace_rec* trace,
+                          int64_t trace_base);
+// Diagnostic occupant (tide_diag_occupy).
+hipError_t launch_occupy(int grid, int threads, size_t lds, hipStream_t stream, int64_t spin_ticks,
+                         tide_trace_rec* trace);
 hipError_t allow_dynamic_lds_landing(int M, size_t lds);
 
 // Allow `lds` bytes of dynamic LDS on every kernel variant for L contributors.

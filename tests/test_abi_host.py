@@ -200,3 +200,41 @@ def test_stage_validates_before_enqueue(tide):
                                               for p in range(3)]
     with pytest.raises(ValueError):
         st(plan, grads, slots[:1], stream=0)
+
+
+def test_trace_record_counts_and_flags(tide):
+    from workloads.configs import CONFIGS
+    cfg = CONFIGS["wan22_dit_block"]
+    plan = tide.plan_create(cfg.shapes, cfg.N, cfg.L)
+    # Full grid: one launch, one workgroup per tile.
+    full = plan.trace_records(0)
+    assert full > 1000 and plan.launch_count(0) == 1
+    # Budgeted: every launch has at most reduce_blocks (placement: place_blocks) workgroups.
+    b = tide.budgeted()
+    n_rs, l_rs = plan.trace_records(0, b), plan.launch_count(0, b)
+    assert (l_rs - 1) * 16 < n_rs <= l_rs * 16
+    n_ag, l_ag = plan.trace_records(1, b), plan.launch_count(1, b)
+    assert (l_ag - 1) * 4 < n_ag <= l_ag * 4
+    assert plan.trace_records(2, b) <= plan.launch_count(2, b) * 4
+    # The fence flag is accepted and changes no count; unknown flags are not.
+    nf = tide.budgeted(flags=tide.FLAG_NO_LDS_FENCE)
+    assert plan.trace_records(0, nf) == n_rs
+    assert _status(lambda: plan.trace_records(0, tide.Launch(flags=0x4))) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: plan.trace_records(3)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: plan.trace_records(0, tide.Launch(trace_capacity=-1))) == \
+        "TIDE_ERR_INVALID_ARG"
+    S = plan.S
+    assert tide.landing_trace_records(8, 8, S) >= 1
+    lb = tide.landing_trace_records(8, 8, S, launch=tide.budgeted())
+    assert lb > 4 and lb % 4 in (0, 1, 2, 3)
+    assert _status(lambda: tide.landing_trace_records(8, 9, S)) == "TIDE_ERR_INVALID_ARG"
+
+
+def test_diag_occupy_validates(tide):
+    occ = tide.diag_occupy
+    assert _status(lambda: occ(0, 256, 0, 10, FAKE, stream=0)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: occ(4, 65, 0, 10, FAKE, stream=0)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: occ(4, 2048, 0, 10, FAKE, stream=0)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: occ(4, 256, 200 * 1024, 10, FAKE, stream=0)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: occ(4, 256, 0, 10 ** 9, FAKE, stream=0)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: occ(4, 256, 0, 10, 0, stream=0)) == "TIDE_ERR_INVALID_ARG"
