@@ -207,3 +207,54 @@ def test_no_device_allocation_on_repeat(tide):
     torch.cuda.synchronize()
     free1, _ = torch.cuda.mem_get_info()
     assert free1 == free0
+
+
+def test_concurrent_host_threads(tide, orc):
+    """Host threads calling the library at the same time (ctypes releases the
+    GIL), each on its own stream: two share one plan (its per-call table ring
+    and table cache), two have plans of their own. Every thread's final
+    results must equal the oracle's."""
+    import threading
+    shapes, N, L = [(129, 33), (64, 1), (7, 500), (300, 16)], 4, 3
+    shared = tide.plan_create(shapes, N, L)
+    want_rs, jobs = {}, []
+    for i in range(4):
+        grads = host_grads(shapes, L, seed=100 + i)
+        want_rs[i] = orc.reduce_scatter(shapes, N, L, grads).reshape(-1)
+        g_dev = [[to_dev_bf16(grads[c][p], (t, k)) for p, (t, k) in enumerate(shapes)]
+                 for c in range(L)]
+        plan = shared if i < 2 else tide.plan_create(shapes, N, L)
+        sh_bits = host_rank_major_bits(N * plan.S, seed=200 + i)
+        sh = to_dev_bf16(sh_bits, (N * plan.S,))
+        want_ag = orc.allgather_place(shapes, N, sh_bits)
+        jobs.append(dict(plan=plan, g=g_dev, sh=sh, want_ag=want_ag,
+                         out=torch.empty(N * plan.S, dtype=torch.float32, device=dev()),
+                         params=[torch.empty((t, k), dtype=torch.bfloat16, device=dev())
+                                 for t, k in shapes],
+                         stream=torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    errors = []
+
+    def work(i):
+        j = jobs[i]
+        try:
+            for it in range(25):
+                launch = tide.budgeted(max_launch_us=5) if it % 3 == 0 else None
+                tide.reduce_scatter_bf16_fp32(j["plan"], j["g"], j["out"], stream=j["stream"],
+                                              launch=launch)
+                tide.allgather_place(j["plan"], j["sh"], j["params"], stream=j["stream"],
+                                     launch=launch)
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append((i, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i, j in enumerate(jobs):
+        same_f32(bits_of(j["out"]), want_rs[i], "thread %d reduce-scatter" % i)
+        for p in range(len(shapes)):
+            same_u16(bits_of(j["params"][p]), j["want_ag"][p], "thread %d placement %d" % (i, p))
