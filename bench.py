@@ -113,7 +113,37 @@ def cpu_baseline(orc, cfg, plan, grads, shards, out, ranks, reps=3):
                   "placement, same bits copied from the GPU; median of %d runs: %.2f s reduce + "
                   "%.2f s placement on one core" % (ranks - 1, N, len(cfg.shapes), reps, t_rs, t_ag),
         "gpu_shards_bit_exact_on_sample": exact,
+        "host": host_info(),
     }
+
+
+def host_info():
+    """The host the CPU baseline ran on: CPU model and the cores this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cores_available": len(os.sched_getaffinity(0))}
+
+
+def gpu_clocks():
+    """Current GPU clock state as rocm-smi reports it (None if it cannot be read)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        if r.returncode != 0:
+            return None
+        d = json.loads(r.stdout)
+        card = d.get("card0") or next(iter(d.values()))
+        return {k: v for k, v in card.items() if "clock" in k.lower()}
+    except Exception:  # noqa: BLE001 - a missing or failing tool only drops this field
+        return None
 
 
 def copy_ceiling_gbps(torch, nbytes=4 << 30, iters=10):
@@ -571,6 +601,7 @@ def main():
         log("bench: cpu %s" % json.dumps(cpu))
 
     traffic = counter_traffic(cfg.name)
+    clocks = gpu_clocks()
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -595,6 +626,7 @@ def main():
                      "traffic": traffic, "kernel": "reduce_kernel<%d>" % cfg.L},
         "cpu_baseline": cpu,
         "parts": parts,
+        "gpu_clocks_after_run": clocks,
     }
     if victim is not None:
         line["victim_gemm_256x8192x8192"] = victim
