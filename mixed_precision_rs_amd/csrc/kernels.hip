@@ -113,11 +113,12 @@ constexpr int kHalf = kWave * 4;           // elements of one run
 
 #if !TIDE_RS_SPLIT_STORE
 // Write 8 fp32 results for flat indices f..f+7 (all inside the tile's range).
+template <int64_t kTile>
 __device__ __forceinline__ void store8(const Span& t, const ParamDev& pd, int64_t f,
                                        const float (&a)[kVec], float* __restrict__ out,
                                        int64_t stride) {
     int64_t r, j;
-    locate<kRsTile>(t, pd.s, f, r, j);
+    locate<kTile>(t, pd.s, f, r, j);
     if (j + kVec <= pd.s) {
         float* dst = out + r * stride + pd.o + j;
         const f32x4_a4 x0 = {a[0], a[1], a[2], a[3]};
@@ -136,11 +137,12 @@ __device__ __forceinline__ void store8(const Span& t, const ParamDev& pd, int64_
 #endif
 
 // Write 4 fp32 results for flat indices f..f+3 (all inside the tile's range).
+template <int64_t kTile>
 __device__ __forceinline__ void store4(const Span& t, const ParamDev& pd, int64_t f,
                                        const float (&a)[4], float* __restrict__ out,
                                        int64_t stride) {
     int64_t r, j;
-    locate<kRsTile>(t, pd.s, f, r, j);
+    locate<kTile>(t, pd.s, f, r, j);
     if (j + 4 <= pd.s) {
         const f32x4_a4 x = {a[0], a[1], a[2], a[3]};
         TIDE_ST(x, reinterpret_cast<f32x4_a4*>(out + r * stride + pd.o + j));
@@ -185,13 +187,14 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t n) {
 // mid-line (prefix offsets that are not multiples of 4 elements) cost about
 // 3.5% of bandwidth; neither realigning them across lanes nor plain
 // write-back stores recovered it on MI355X.
+template <int64_t kTile>
 __device__ __forceinline__ void store_run(const Span& t, const ParamDev& pd, int64_t f_run,
                                           int lane, const float (&a)[4],
                                           float* __restrict__ out, int64_t stride) {
     int64_t r, j;
-    locate<kRsTile>(t, pd.s, f_run, r, j);
+    locate<kTile>(t, pd.s, f_run, r, j);
     if (j + kHalf > pd.s) {                   // the run crosses into the next rank's piece
-        store4(t, pd, f_run + 4 * lane, a, out, stride);
+        store4<kTile>(t, pd, f_run + 4 * lane, a, out, stride);
         return;
     }
     const f32x4_a4 x = {a[0], a[1], a[2], a[3]};
@@ -233,6 +236,10 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
     tide_trace_rec* __restrict__ trace, int64_t trace_base) {
     const uint64_t t_begin = trace_begin(trace);
     constexpr int kSubs = NT / kThreads;
+    // Budgeted (fat) workgroups walk longer tiles with more loads in flight:
+    // one workgroup per CU has no other workgroups to hide its latency.
+    constexpr int64_t kTileR = NT == kFatThreads ? kRsTileFat : kRsTile;
+    constexpr int kUR = NT == kFatThreads ? kRsUnrollFat : kRsUnroll;
     const int L = LT > 0 ? LT : Lrt;
     const int sub = (int)threadIdx.x / kThreads;          // wave-uniform
     const int tid = (int)threadIdx.x % kThreads;
@@ -248,9 +255,9 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
         const bool vec = (flags[rec.p] & kFlagVector) != 0;
         const Span tr{rec.idx0, rec.idx0 - (int64_t)rec.r0 * pd.s, (int64_t)rb * pd.s,
                       (int64_t)re * pd.s, rec.r0};
-        const int64_t end = min(tr.idx0 + kRsTile, tr.hi);
-        for (int64_t g0 = tr.idx0; g0 < end; g0 += kRsUnroll * kStep) {
-            const int64_t g1 = g0 + kRsUnroll * kStep;
+        const int64_t end = min(tr.idx0 + kTileR, tr.hi);
+        for (int64_t g0 = tr.idx0; g0 < end; g0 += kUR * kStep) {
+            const int64_t g1 = g0 + kUR * kStep;
             const bool interior = vec && g0 >= tr.lo && g1 <= end;
             const int64_t f0 = g0 + (int64_t)tid * kVec;
 #if TIDE_RS_SPLIT_STORE
@@ -260,19 +267,19 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
             if (interior && g1 <= pd.valid) {
                 // All loads are independent of the adds: they are all issued
                 // before the first add waits.
-                float a[kRsUnroll][2][4];
+                float a[kUR][2][4];
                 constexpr int kCUnroll = LT > 0 ? LT : 1;
 #pragma unroll kCUnroll
                 for (int c = 0; c < L; ++c) {
                     const TIDE_GLOBAL u32x2* gc = gbl<u32x2>(g[c] + fh);
-                    u32x2 v[kRsUnroll][2];
+                    u32x2 v[kUR][2];
 #pragma unroll
-                    for (int u = 0; u < kRsUnroll; ++u)
+                    for (int u = 0; u < kUR; ++u)
 #pragma unroll
                         for (int h = 0; h < 2; ++h)
                             v[u][h] = TIDE_LD(gc + (u * kStep + h * kHalf) / 4);
 #pragma unroll
-                    for (int u = 0; u < kRsUnroll; ++u) {
+                    for (int u = 0; u < kUR; ++u) {
 #pragma unroll
                         for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -289,35 +296,35 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
                     }
                 }
 #pragma unroll
-                for (int u = 0; u < kRsUnroll; ++u)
+                for (int u = 0; u < kUR; ++u)
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
-                        store_run(tr, pd, fw + (int64_t)u * kStep + h * kHalf, lane, a[u][h],
+                        store_run<kTileR>(tr, pd, fw + (int64_t)u * kStep + h * kHalf, lane, a[u][h],
                                   out, out_stride);
             } else if (interior && g0 >= pd.valid) {
                 const float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int u = 0; u < kRsUnroll; ++u)
+                for (int u = 0; u < kUR; ++u)
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
-                        store_run(tr, pd, fw + (int64_t)u * kStep + h * kHalf, lane, z, out,
+                        store_run<kTileR>(tr, pd, fw + (int64_t)u * kStep + h * kHalf, lane, z, out,
                                   out_stride);
             } else
 #else
             if (interior && g1 <= pd.valid) {
-                // All L * kRsUnroll loads are independent of the adds, so they
+                // All L * kUR loads are independent of the adds, so they
                 // are all issued before the first add waits.
-                float a[kRsUnroll][kVec];
+                float a[kUR][kVec];
                 constexpr int kCUnroll = LT > 0 ? LT : 1;
 #pragma unroll kCUnroll
                 for (int c = 0; c < L; ++c) {
                     const TIDE_GLOBAL u32x4* gc = gbl<u32x4>(g[c] + f0);
-                    u32x4 v[kRsUnroll];
+                    u32x4 v[kUR];
 #pragma unroll
-                    for (int u = 0; u < kRsUnroll; ++u)
+                    for (int u = 0; u < kUR; ++u)
                         v[u] = TIDE_LD(gc + u * (kStep / kVec));
 #pragma unroll
-                    for (int u = 0; u < kRsUnroll; ++u) {
+                    for (int u = 0; u < kUR; ++u) {
 #pragma unroll
                         for (int m = 0; m < 4; ++m) {
                             if (c == 0) {
@@ -331,15 +338,15 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
                     }
                 }
 #pragma unroll
-                for (int u = 0; u < kRsUnroll; ++u)
-                    store8(tr, pd, f0 + (int64_t)u * kStep, a[u], out, out_stride);
+                for (int u = 0; u < kUR; ++u)
+                    store8<kTileR>(tr, pd, f0 + (int64_t)u * kStep, a[u], out, out_stride);
             } else if (interior && g0 >= pd.valid) {
                 float z[kVec];
 #pragma unroll
                 for (int e = 0; e < kVec; ++e) z[e] = 0.0f;
 #pragma unroll
-                for (int u = 0; u < kRsUnroll; ++u)
-                    store8(tr, pd, f0 + (int64_t)u * kStep, z, out, out_stride);
+                for (int u = 0; u < kUR; ++u)
+                    store8<kTileR>(tr, pd, f0 + (int64_t)u * kStep, z, out, out_stride);
             } else
 #endif
             {
@@ -350,7 +357,7 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
                 // one side of the valid end still goes as one vector; only
                 // a group that straddles a bound goes element by element.
 #pragma unroll 1
-                for (int u = 0; u < kRsUnroll; ++u) {
+                for (int u = 0; u < kUR; ++u) {
                     const int64_t fu = f0 + (int64_t)u * kStep;
                     const bool whole = fu >= tr.lo && fu + kVec <= end;
                     if (whole && vec && fu + kVec <= pd.valid) {
@@ -368,15 +375,15 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
                                 x1 = c == 0 ? hi : x1 + hi;
                             }
                         }
-                        store4(tr, pd, fu, a[0], out, out_stride);
-                        store4(tr, pd, fu + 4, a[1], out, out_stride);
+                        store4<kTileR>(tr, pd, fu, a[0], out, out_stride);
+                        store4<kTileR>(tr, pd, fu + 4, a[1], out, out_stride);
                     } else if (whole && fu >= pd.valid) {
                         const float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                        store4(tr, pd, fu, z, out, out_stride);
-                        store4(tr, pd, fu + 4, z, out, out_stride);
+                        store4<kTileR>(tr, pd, fu, z, out, out_stride);
+                        store4<kTileR>(tr, pd, fu + 4, z, out, out_stride);
                     } else {
                         int64_t r, j;
-                        locate<kRsTile>(tr, pd.s, fu, r, j);
+                        locate<kTileR>(tr, pd.s, fu, r, j);
 #pragma unroll 1
                         for (int e = 0; e < kVec; ++e, step(pd.s, r, j)) {
                             const int64_t f = fu + e;
@@ -414,11 +421,12 @@ __device__ __forceinline__ int64_t stage_pos(int64_t r, int32_t first, int32_t n
 }
 
 // 8 bf16 of the rank-major shards for flat parameter indices f..f+7.
+template <int64_t kTile>
 __device__ __forceinline__ u32x4 gather8(const Span& t, const ParamDev& pd, int64_t f,
                                          const uint16_t* __restrict__ shards, int64_t stride,
                                          int64_t shard_elems, int32_t first, int32_t n) {
     int64_t r, j;
-    locate<kAgTile>(t, pd.s, f, r, j);
+    locate<kTile>(t, pd.s, f, r, j);
     if (j + kVec <= pd.s) {
         const int64_t e = stage_pos(r, first, n) * stride + pd.o + j;
         const uint16_t* src = shards + e;
@@ -461,6 +469,8 @@ __global__ __launch_bounds__(NT) void place_kernel(
     int64_t trace_base) {
     const uint64_t t_begin = trace_begin(trace);
     constexpr int kSubs = NT / kThreads;
+    constexpr int64_t kTileA = NT == kFatThreads ? kAgTileFat : kAgTile;
+    constexpr int kUA = NT == kFatThreads ? kAgUnrollFat : kAgUnroll;
     const int sub = (int)threadIdx.x / kThreads;
     const int tid = (int)threadIdx.x % kThreads;
     const bool one_each = kSubs == 1 && (int64_t)gridDim.x == tile_hi - tile_lo;
@@ -474,19 +484,19 @@ __global__ __launch_bounds__(NT) void place_kernel(
         const bool vec = (flags[rec.p] & kFlagVector) != 0;
         const Span tr{rec.idx0, rec.idx0 - (int64_t)rec.r0 * pd.s, (int64_t)rb * pd.s,
                       min((int64_t)re * pd.s, pd.valid), rec.r0};
-        const int64_t end = min(tr.idx0 + kAgTile, tr.hi);
-        for (int64_t g0 = tr.idx0; g0 < end; g0 += kAgUnroll * kStep) {
-            const int64_t g1 = g0 + kAgUnroll * kStep;
+        const int64_t end = min(tr.idx0 + kTileA, tr.hi);
+        for (int64_t g0 = tr.idx0; g0 < end; g0 += kUA * kStep) {
+            const int64_t g1 = g0 + kUA * kStep;
             const int64_t f0 = g0 + (int64_t)tid * kVec;
             if (vec && g0 >= tr.lo && g1 <= end) {
-                u32x4 w[kAgUnroll];
+                u32x4 w[kUA];
 #pragma unroll
-                for (int u = 0; u < kAgUnroll; ++u)
-                    w[u] = gather8(tr, pd, f0 + (int64_t)u * kStep, shards, stride, shard_elems,
+                for (int u = 0; u < kUA; ++u)
+                    w[u] = gather8<kTileA>(tr, pd, f0 + (int64_t)u * kStep, shards, stride, shard_elems,
                                    first, nranks);
                 TIDE_GLOBAL u32x4* d4 = gbl_mut<u32x4>(dst + f0);
 #pragma unroll
-                for (int u = 0; u < kAgUnroll; ++u)
+                for (int u = 0; u < kUA; ++u)
                     TIDE_ST(w[u], d4 + u * (kStep / kVec));
             } else {
                 // Ragged step: a thread's group of 8 that lies wholly inside
@@ -495,15 +505,15 @@ __global__ __launch_bounds__(NT) void place_kernel(
                 // goes element by element.
                 TIDE_GLOBAL uint16_t* d = gbl_mut<uint16_t>(dst);
 #pragma unroll 1
-                for (int u = 0; u < kAgUnroll; ++u) {
+                for (int u = 0; u < kUA; ++u) {
                     const int64_t fu = f0 + (int64_t)u * kStep;
                     if (vec && fu >= tr.lo && fu + kVec <= end) {
-                        const u32x4 w = gather8(tr, pd, fu, shards, stride, shard_elems, first, nranks);
+                        const u32x4 w = gather8<kTileA>(tr, pd, fu, shards, stride, shard_elems, first, nranks);
                         TIDE_ST(w, gbl_mut<u32x4>(dst + fu));
                         continue;
                     }
                     int64_t r, j;
-                    locate<kAgTile>(tr, pd.s, fu, r, j);
+                    locate<kTileA>(tr, pd.s, fu, r, j);
 #pragma unroll 1
                     for (int e = 0; e < kVec; ++e, step(pd.s, r, j)) {
                         const int64_t f = fu + e;
@@ -535,6 +545,8 @@ __global__ __launch_bounds__(NT) void stage_kernel(
     int64_t trace_base) {
     const uint64_t t_begin = trace_begin(trace);
     constexpr int kSubs = NT / kThreads;
+    constexpr int64_t kTileS = NT == kFatThreads ? kStageTileFat : kStageTile;
+    constexpr int kUS = NT == kFatThreads ? kStageUnrollFat : kStageUnroll;
     const int sub = (int)threadIdx.x / kThreads;
     const int tid = (int)threadIdx.x % kThreads;
     for (int64_t t = tile_lo + (int64_t)blockIdx.x * kSubs + sub; t < tile_hi;
@@ -546,13 +558,13 @@ __global__ __launch_bounds__(NT) void stage_kernel(
         uint16_t* d = dst[(int64_t)rec.p * L + c];
         const bool vec = (flags[rec.p] & kFlagVector) != 0;
         const int64_t lo = (int64_t)rb * pd.s;
-        const int64_t end = min(rec.idx0 + kStageTile, min((int64_t)re * pd.s, pd.valid));
-        for (int64_t g0 = rec.idx0; g0 < end; g0 += kStageUnroll * kStep) {
+        const int64_t end = min(rec.idx0 + kTileS, min((int64_t)re * pd.s, pd.valid));
+        for (int64_t g0 = rec.idx0; g0 < end; g0 += kUS * kStep) {
             const int64_t f0 = g0 + (int64_t)tid * kVec;
-            if (vec && g0 >= lo && g0 + kStageUnroll * kStep <= end) {
-                u32x4_a4 w[kStageUnroll];
+            if (vec && g0 >= lo && g0 + kUS * kStep <= end) {
+                u32x4_a4 w[kUS];
 #pragma unroll
-                for (int u = 0; u < kStageUnroll; ++u) {
+                for (int u = 0; u < kUS; ++u) {
                     const TIDE_GLOBAL u32x4_a4* a = gbl<u32x4_a4>(s + f0 + (int64_t)u * kStep);
 #if TIDE_STAGE_NT
                     w[u] = __builtin_nontemporal_load(a);
@@ -561,7 +573,7 @@ __global__ __launch_bounds__(NT) void stage_kernel(
 #endif
                 }
 #pragma unroll
-                for (int u = 0; u < kStageUnroll; ++u) {
+                for (int u = 0; u < kUS; ++u) {
                     TIDE_GLOBAL u32x4_a4* b = gbl_mut<u32x4_a4>(d + f0 + (int64_t)u * kStep);
 #if TIDE_STAGE_NT
                     __builtin_nontemporal_store(w[u], b);
@@ -575,7 +587,7 @@ __global__ __launch_bounds__(NT) void stage_kernel(
                 const TIDE_GLOBAL uint16_t* gs = gbl<uint16_t>(s);
                 TIDE_GLOBAL uint16_t* gd = gbl_mut<uint16_t>(d);
 #pragma unroll 1
-                for (int u = 0; u < kStageUnroll; ++u) {
+                for (int u = 0; u < kUS; ++u) {
                     const int64_t fu = f0 + (int64_t)u * kStep;
                     if (vec && fu >= lo && fu + kVec <= end) {
                         const u32x4_a4 w = TIDE_LD(gbl<u32x4_a4>(s + fu));

@@ -59,15 +59,24 @@ constexpr int kDefaultMaxLaunchUs = 300;
 #ifndef TIDE_BUDGET_LDS
 #define TIDE_BUDGET_LDS (128 * 1024)
 #endif
-// Bytes one budgeted workgroup streams per microsecond with a CU to itself
-// (about 35 GB/s measured on MI355X: per-CU streaming is latency-bound);
-// sizes the budgeted launches so a workgroup lives about max_launch_us.
-#ifndef TIDE_WG_BYTES_PER_US
-#define TIDE_WG_BYTES_PER_US 35000
+// Bytes one budgeted workgroup streams per microsecond with a CU to itself,
+// per operation (measured on MI355X: per-workgroup streaming is latency
+// bound); sizes the budgeted launches so a workgroup lives about
+// max_launch_us.
+#ifndef TIDE_WG_BYTES_PER_US_RS
+#define TIDE_WG_BYTES_PER_US_RS 45000
+#endif
+#ifndef TIDE_WG_BYTES_PER_US_AG
+#define TIDE_WG_BYTES_PER_US_AG 54000
+#endif
+#ifndef TIDE_WG_BYTES_PER_US_LANDING
+#define TIDE_WG_BYTES_PER_US_LANDING 35000
 #endif
 constexpr int kBudgetThreads = TIDE_BUDGET_THREADS;
 constexpr size_t kBudgetLds = TIDE_BUDGET_LDS;
-constexpr int64_t kWgBytesPerUs = TIDE_WG_BYTES_PER_US;
+constexpr int64_t kWgBytesPerUsRs = TIDE_WG_BYTES_PER_US_RS;
+constexpr int64_t kWgBytesPerUsAg = TIDE_WG_BYTES_PER_US_AG;       // placement and staging
+constexpr int64_t kWgBytesPerUsLanding = TIDE_WG_BYTES_PER_US_LANDING;
 // Full mode: at most this many workgroups per launch (they loop over tiles).
 #ifndef TIDE_FULL_GRID_CAP
 #define TIDE_FULL_GRID_CAP (1 << 30)
@@ -103,7 +112,7 @@ struct Slot {
 struct DevState {
     int device = -1;
     ParamDev* params = nullptr;
-    std::map<std::tuple<int, int, int>, TileTable> tiles;   // (op, rank_begin, rank_end)
+    std::map<std::tuple<int, int, int>, TileTable> tiles;   // (op + 4 * budgeted, rank_begin, rank_end)
     size_t slot_cap = 0;
     char* ring_dev = nullptr;
     char* ring_host = nullptr;
@@ -173,13 +182,19 @@ tide_status resolve_launch(const tide_plan* plan, const tide_launch* in, tide_la
     return TIDE_OK;
 }
 
+// Elements per tile of one op, for full-grid (fat = false) or budgeted launches.
+int64_t tile_elems(int op, bool fat) {
+    if (op == 0) return fat ? kRsTileFat : kRsTile;
+    if (op == 1) return fat ? kAgTileFat : kAgTile;
+    return fat ? kStageTileFat : kStageTile;
+}
+
 // Tiles of one op over ranks [rb, re). op 0: reduce over each parameter's
 // padded index space restricted to [rb * s_p, re * s_p); op 1: placement over
-// its true elements restricted the same way; op 2: staging, as op 1 with its
-// own tile size.
-std::vector<TileRec> build_tiles(const tide_plan* plan, int op, int rb, int re) {
+// its true elements restricted the same way; op 2: staging, as op 1.
+std::vector<TileRec> build_tiles(const tide_plan* plan, int op, int rb, int re, bool fat) {
     std::vector<TileRec> out;
-    const int64_t tile = op == 0 ? kRsTile : op == 1 ? kAgTile : kStageTile;
+    const int64_t tile = tile_elems(op, fat);
     for (int32_t p = 0; p < plan->P; ++p) {
         const ParamInfo& q = plan->prm[p];
         if (q.s == 0) continue;
@@ -248,13 +263,15 @@ std::vector<TileRec> build_tiles(const tide_plan* plan, int op, int rb, int re) 
     return out;
 }
 
+// Bytes a budgeted tile moves.
 int64_t tile_bytes(const tide_plan* plan, int op) {
-    return op == 0 ? kRsTile * (2 * (int64_t)plan->L + 4) : op == 1 ? kAgTile * 4 : kStageTile * 4;
+    return op == 0 ? tile_elems(0, true) * (2 * (int64_t)plan->L + 4) : tile_elems(op, true) * 4;
 }
 
 // Tiles one budgeted workgroup handles per launch.
 int64_t budget_tiles_per_block(const tide_plan* plan, int op, const tide_launch& l) {
-    const int64_t per = ((int64_t)l.max_launch_us * kWgBytesPerUs) / tile_bytes(plan, op);
+    const int64_t rate = op == 0 ? kWgBytesPerUsRs : kWgBytesPerUsAg;
+    const int64_t per = ((int64_t)l.max_launch_us * rate) / tile_bytes(plan, op);
     return std::max<int64_t>(1, per);
 }
 
@@ -314,15 +331,15 @@ tide_status get_dev_state(const tide_plan* plan, int dev, DevState** out) {
     return TIDE_OK;
 }
 
-tide_status get_tiles(const tide_plan* plan, DevState* ds, int op, int rb, int re,
+tide_status get_tiles(const tide_plan* plan, DevState* ds, int op, int rb, int re, bool fat,
                       TileTable** out) {
-    auto key = std::make_tuple(op, rb, re);
+    auto key = std::make_tuple(op + (fat ? 4 : 0), rb, re);
     auto it = ds->tiles.find(key);
     if (it != ds->tiles.end()) {
         *out = &it->second;
         return TIDE_OK;
     }
-    std::vector<TileRec> t = build_tiles(plan, op, rb, re);
+    std::vector<TileRec> t = build_tiles(plan, op, rb, re, fat);
     TileTable tt;
     tt.count = (int64_t)t.size();
     if (!t.empty()) {
@@ -565,7 +582,7 @@ tide_status tide_plan_launch_count(const tide_plan* plan, int32_t op, const tide
         tide_status st = resolve_launch(plan, launch, &l);
         if (st != TIDE_OK) return st;
         // The staging walks its tiling once per contributor.
-        int64_t n = (int64_t)build_tiles(plan, op, l.rank_begin, l.rank_end).size();
+        int64_t n = (int64_t)build_tiles(plan, op, l.rank_begin, l.rank_end, l.mode == TIDE_LAUNCH_BUDGETED).size();
         if (op == 2) n *= plan->L;
         *launches = count_launches(plan, op, l, n);
         return TIDE_OK;
@@ -631,7 +648,7 @@ tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t*
         st = get_dev_state(plan, dev, &ds);
         if (st != TIDE_OK) return st;
         TileTable* tt;
-        st = get_tiles(plan, ds, 0, l.rank_begin, l.rank_end, &tt);
+        st = get_tiles(plan, ds, 0, l.rank_begin, l.rank_end, l.mode == TIDE_LAUNCH_BUDGETED, &tt);
         if (st != TIDE_OK) return st;
         if (tt->count == 0) return TIDE_OK;
         st = check_trace(l, launch_records(plan, 0, l, tt->count));
@@ -770,7 +787,7 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* sh
         st = get_dev_state(plan, dev, &ds);
         if (st != TIDE_OK) return st;
         TileTable* tt;
-        st = get_tiles(plan, ds, 1, l.rank_begin, l.rank_end, &tt);
+        st = get_tiles(plan, ds, 1, l.rank_begin, l.rank_end, l.mode == TIDE_LAUNCH_BUDGETED, &tt);
         if (st != TIDE_OK) return st;
         if (tt->count == 0) return TIDE_OK;
         st = check_trace(l, launch_records(plan, 1, l, tt->count));
@@ -884,7 +901,7 @@ tide_status tide_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* 
         st = get_dev_state(plan, dev, &ds);
         if (st != TIDE_OK) return st;
         TileTable* tt;
-        st = get_tiles(plan, ds, 2, l.rank_begin, l.rank_end, &tt);
+        st = get_tiles(plan, ds, 2, l.rank_begin, l.rank_end, l.mode == TIDE_LAUNCH_BUDGETED, &tt);
         if (st != TIDE_OK) return st;
         if (tt->count == 0) return TIDE_OK;
         st = check_trace(l, launch_records(plan, 2, l, tt->count * L));
@@ -944,7 +961,8 @@ hipError_t for_each_landing_launch(int32_t L, int32_t M, int64_t S, int32_t accu
                       (int64_t)0, ntiles, (int64_t)0);
     const size_t lds = (l.flags & TIDE_FLAG_NO_LDS_FENCE) ? 0 : kBudgetLds;
     const int64_t tile_b = kLandTile * (4 * (int64_t)M + 4 + 4 * accumulate);
-    const int64_t per_block = std::max<int64_t>(1, (int64_t)l.max_launch_us * kWgBytesPerUs / tile_b);
+    const int64_t per_block =
+        std::max<int64_t>(1, (int64_t)l.max_launch_us * kWgBytesPerUsLanding / tile_b);
     const int64_t per_launch = (int64_t)l.place_blocks * per_block;
     int64_t base = 0;
     for (int64_t lo = 0; lo < ntiles; lo += per_launch) {
@@ -1129,7 +1147,7 @@ tide_status tide_plan_trace_records(const tide_plan* plan, int32_t op, const tid
         tide_launch l;
         tide_status st = resolve_launch(plan, launch, &l);
         if (st != TIDE_OK) return st;
-        int64_t n = (int64_t)build_tiles(plan, op, l.rank_begin, l.rank_end).size();
+        int64_t n = (int64_t)build_tiles(plan, op, l.rank_begin, l.rank_end, l.mode == TIDE_LAUNCH_BUDGETED).size();
         if (op == 2) n *= plan->L;
         *records = launch_records(plan, op, l, n);
         return TIDE_OK;

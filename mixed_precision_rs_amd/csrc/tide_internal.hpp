@@ -32,6 +32,28 @@ namespace tide {
 #ifndef TIDE_STAGE_UNROLL
 #define TIDE_STAGE_UNROLL 2
 #endif
+// Budgeted (fat, 1024-thread) workgroups: one per CU, so each needs more
+// loads in flight and fewer tile setups per byte (measured on MI355X: the
+// reduce streams 45 instead of 35 GB/s per workgroup, the placement 54
+// instead of 40).
+#ifndef TIDE_RS_FAT_TILE_STEPS
+#define TIDE_RS_FAT_TILE_STEPS 8
+#endif
+#ifndef TIDE_RS_FAT_UNROLL
+#define TIDE_RS_FAT_UNROLL 2
+#endif
+#ifndef TIDE_AG_FAT_TILE_STEPS
+#define TIDE_AG_FAT_TILE_STEPS 8
+#endif
+#ifndef TIDE_AG_FAT_UNROLL
+#define TIDE_AG_FAT_UNROLL 4
+#endif
+#ifndef TIDE_STAGE_FAT_TILE_STEPS
+#define TIDE_STAGE_FAT_TILE_STEPS 8
+#endif
+#ifndef TIDE_STAGE_FAT_UNROLL
+#define TIDE_STAGE_FAT_UNROLL 4
+#endif
 #ifndef TIDE_STAGE_TILE_STEPS
 #define TIDE_STAGE_TILE_STEPS 2
 #endif
@@ -48,6 +70,15 @@ constexpr int64_t kAgTile = (int64_t)TIDE_AG_TILE_STEPS * kStep;   // elements p
 constexpr int kStageUnroll = TIDE_STAGE_UNROLL;                          // same, staging copy
 constexpr int64_t kStageTile = (int64_t)TIDE_STAGE_TILE_STEPS * kStep;   // elements per staging tile
 static_assert(kStageTile % (kStageUnroll * kStep) == 0, "tile must hold whole groups");
+constexpr int kRsUnrollFat = TIDE_RS_FAT_UNROLL;
+constexpr int64_t kRsTileFat = (int64_t)TIDE_RS_FAT_TILE_STEPS * kStep;
+constexpr int kAgUnrollFat = TIDE_AG_FAT_UNROLL;
+constexpr int64_t kAgTileFat = (int64_t)TIDE_AG_FAT_TILE_STEPS * kStep;
+constexpr int kStageUnrollFat = TIDE_STAGE_FAT_UNROLL;
+constexpr int64_t kStageTileFat = (int64_t)TIDE_STAGE_FAT_TILE_STEPS * kStep;
+static_assert(kRsTileFat % (kRsUnrollFat * kStep) == 0, "tile must hold whole groups");
+static_assert(kAgTileFat % (kAgUnrollFat * kStep) == 0, "tile must hold whole groups");
+static_assert(kStageTileFat % (kStageUnrollFat * kStep) == 0, "tile must hold whole groups");
 static_assert(kRsTile % (kRsUnroll * kStep) == 0, "tile must hold whole groups");
 static_assert(kAgTile % (kAgUnroll * kStep) == 0, "tile must hold whole groups");
 static_assert(kFatThreads % kThreads == 0, "a fat workgroup is whole quarters");
