@@ -342,6 +342,12 @@ tide_status tide_landing_trace_records(int32_t L, int32_t M, int64_t S, int32_t 
 tide_status tide_diag_occupy(int32_t workgroups, int32_t threads, int32_t lds_bytes,
                              int64_t spin_ticks, tide_trace_rec* trace, void* stream);
 
+/* HIP events the plan holds across its devices: per-call table uploads, the
+ * readers of each table slot (one per stream with pending work), and the pool
+ * of spare events. Bounded by the ring size and the number of streams in use,
+ * not by the number of calls. Host-only (diagnostic). */
+tide_status tide_plan_event_count(const tide_plan* plan, int64_t* events);
+
 /* Static text for a status code. */
 const char* tide_status_string(tide_status status);
 

@@ -31,7 +31,8 @@ EXPORTS = ["tide_plan_create", "tide_plan_destroy", "tide_plan_dims", "tide_plan
            "tide_plan_launch_count", "tide_status_string", "tide_last_error_detail",
            "tide_version", "tide_allgather_place_stage", "tide_rd_schedule",
            "tide_landing_sum_fp32", "tide_latin_square", "tide_stage_grads_bf16",
-           "tide_plan_trace_records", "tide_landing_trace_records", "tide_diag_occupy"]
+           "tide_plan_trace_records", "tide_landing_trace_records", "tide_diag_occupy",
+           "tide_plan_event_count"]
 
 
 class TideError(RuntimeError):
@@ -147,6 +148,7 @@ def _load():
                                             ctypes.POINTER(Launch), _I64P]
     lib.tide_landing_trace_records.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                                ctypes.c_int32, ctypes.POINTER(Launch), _I64P]
+    lib.tide_plan_event_count.argtypes = [ctypes.c_void_p, _I64P]
     lib.tide_diag_occupy.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     lib.tide_status_string.argtypes = [ctypes.c_int]
@@ -159,7 +161,7 @@ def _load():
               "tide_reduce_scatter_bf16_fp32", "tide_allgather_place", "tide_plan_launch_count",
               "tide_allgather_place_stage", "tide_rd_schedule", "tide_landing_sum_fp32",
               "tide_latin_square", "tide_stage_grads_bf16", "tide_plan_trace_records",
-              "tide_landing_trace_records", "tide_diag_occupy"):
+              "tide_landing_trace_records", "tide_diag_occupy", "tide_plan_event_count"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -240,6 +242,12 @@ class Plan:
         _check(_load().tide_plan_map(self._h, r, p, *[ctypes.byref(x) for x in v]),
                "tide_plan_map")
         return tuple(int(x.value) for x in v)
+
+    def event_count(self) -> int:
+        """HIP events the plan holds (tide_plan_event_count)."""
+        n = ctypes.c_int64()
+        _check(_load().tide_plan_event_count(self._h, ctypes.byref(n)), "tide_plan_event_count")
+        return int(n.value)
 
     def trace_records(self, op: int, launch: Optional[Launch] = None) -> int:
         """Workgroups (trace records) a call of op 0 / 1 / 2 launches."""

@@ -82,12 +82,6 @@ constexpr int64_t kWgBytesPerUsLanding = TIDE_WG_BYTES_PER_US_LANDING;
 #define TIDE_FULL_GRID_CAP (1 << 30)
 #endif
 constexpr int kFullGridCap = TIDE_FULL_GRID_CAP;
-#ifndef TIDE_TILE_ORDER_RANK_MAJOR
-#define TIDE_TILE_ORDER_RANK_MAJOR 0
-#endif
-#ifndef TIDE_TILE_INTERLEAVE
-#define TIDE_TILE_INTERLEAVE 1
-#endif
 #ifndef TIDE_RS_GROUP_ELEMS
 #define TIDE_RS_GROUP_ELEMS (1 << 20)
 #endif
@@ -99,6 +93,13 @@ struct TileTable {
     int64_t count = 0;
 };
 
+// A call that read a slot: the last such call on `stream` is marked by `ev`
+// (work on one stream completes in order, so one event per stream suffices).
+struct Reader {
+    hipStream_t stream;
+    hipEvent_t ev;
+};
+
 struct Slot {
     void* dev = nullptr;
     void* host = nullptr;
@@ -106,7 +107,7 @@ struct Slot {
     bool loaded = false;
     hipStream_t upload_stream = nullptr;
     hipEvent_t upload_done = nullptr;      // recorded after the upload copy
-    std::vector<hipEvent_t> readers;       // recorded after each call that read the slot
+    std::vector<Reader> readers;           // per stream, recorded after its last call that read the slot
 };
 
 struct DevState {
@@ -131,9 +132,9 @@ struct DevState {
         (void)hipFree(ring_dev);
         if (ring_host) (void)hipHostFree(ring_host);
         for (auto& s : slots) {
-            for (hipEvent_t e : s.readers) {
-                (void)hipEventSynchronize(e);
-                (void)hipEventDestroy(e);
+            for (const Reader& r : s.readers) {
+                (void)hipEventSynchronize(r.ev);
+                (void)hipEventDestroy(r.ev);
             }
             if (s.upload_done) (void)hipEventDestroy(s.upload_done);
         }
@@ -232,32 +233,6 @@ std::vector<TileRec> build_tiles(const tide_plan* plan, int op, int rb, int re, 
             if (group[a.p] != group[b.p]) return group[a.p] < group[b.p];
             return a.r0 != b.r0 ? a.r0 < b.r0 : a.p < b.p;
         });
-    }
-#endif
-#if TIDE_TILE_ORDER_RANK_MAJOR
-    // The same tiles (a partition of the index space) walked rank by rank.
-    std::stable_sort(out.begin(), out.end(), [](const TileRec& a, const TileRec& b) {
-        return a.r0 != b.r0 ? a.r0 < b.r0 : a.p < b.p;
-    });
-#endif
-#if TIDE_TILE_INTERLEAVE > 1
-    // Within each group of TIDE_TILE_INTERLEAVE consecutive parameters, walk
-    // the parameters' tiles round robin.
-    {
-        std::vector<int64_t> first(plan->P + 1, 0);
-        for (const TileRec& t : out) first[t.p + 1]++;
-        for (int32_t p = 0; p < plan->P; ++p) first[p + 1] += first[p];
-        std::vector<std::pair<std::pair<int64_t, int64_t>, size_t>> key(out.size());
-        for (size_t i = 0; i < out.size(); ++i) {
-            const int32_t p = out[i].p;
-            key[i] = {{p / TIDE_TILE_INTERLEAVE, (int64_t)i - first[p]}, i};
-        }
-        std::stable_sort(key.begin(), key.end(), [](const auto& a, const auto& b) {
-            return a.first < b.first;
-        });
-        std::vector<TileRec> re(out.size());
-        for (size_t i = 0; i < key.size(); ++i) re[i] = out[key[i].second];
-        out.swap(re);
     }
 #endif
     return out;
@@ -385,9 +360,9 @@ tide_status stage_table(DevState* ds, const void* bytes, size_t n, hipStream_t s
     const int k = ds->next_slot;
     ds->next_slot = (k + 1) % kRingSlots;
     Slot& s = ds->slots[k];
-    for (hipEvent_t e : s.readers) {          // earlier readers of this slot must be done
-        TIDE_HIP_TRY(hipEventSynchronize(e));
-        ds->event_pool.push_back(e);
+    for (const Reader& r : s.readers) {       // earlier readers of this slot must be done
+        TIDE_HIP_TRY(hipEventSynchronize(r.ev));
+        ds->event_pool.push_back(r.ev);
     }
     s.readers.clear();
     s.loaded = false;
@@ -402,7 +377,29 @@ tide_status stage_table(DevState* ds, const void* bytes, size_t n, hipStream_t s
     return TIDE_OK;
 }
 
+// Mark the end of a call that read `slot` on `stream`. A stream that read the
+// slot before re-records its event; readers on other streams whose events
+// have completed are dropped, so the list stays as short as the number of
+// streams with work still pending on the slot.
 tide_status release_slot(DevState* ds, int slot, hipStream_t stream) {
+    std::vector<Reader>& readers = ds->slots[slot].readers;
+    for (const Reader& r : readers)
+        if (r.stream == stream) {
+            TIDE_HIP_TRY(hipEventRecord(r.ev, stream));
+            return TIDE_OK;
+        }
+    for (size_t i = 0; i < readers.size();) {
+        const hipError_t q = hipEventQuery(readers[i].ev);
+        if (q == hipSuccess) {
+            ds->event_pool.push_back(readers[i].ev);
+            readers[i] = readers.back();
+            readers.pop_back();
+        } else if (q == hipErrorNotReady) {
+            ++i;
+        } else {
+            return hip_fail(q, "hipEventQuery");
+        }
+    }
     hipEvent_t ev;
     tide_status st = take_event(ds, &ev);
     if (st != TIDE_OK) return st;
@@ -411,7 +408,7 @@ tide_status release_slot(DevState* ds, int slot, hipStream_t stream) {
         ds->event_pool.push_back(ev);
         return hip_fail(e, "hipEventRecord");
     }
-    ds->slots[slot].readers.push_back(ev);
+    readers.push_back(Reader{stream, ev});
     return TIDE_OK;
 }
 
@@ -1138,6 +1135,18 @@ const char* tide_status_string(tide_status s) {
 const char* tide_last_error_detail(void) { return g_detail.c_str(); }
 
 int32_t tide_version(void) { return (1 << 16) | 0; }
+
+tide_status tide_plan_event_count(const tide_plan* plan, int64_t* events) {
+    if (!plan || !events) return fail(TIDE_ERR_INVALID_ARG, "NULL argument");
+    std::lock_guard<std::mutex> lock(plan->mu);
+    int64_t n = 0;
+    for (const auto& d : plan->devs) {
+        n += (int64_t)d->event_pool.size();
+        for (const Slot& sl : d->slots) n += (int64_t)sl.readers.size() + (sl.upload_done ? 1 : 0);
+    }
+    *events = n;
+    return TIDE_OK;
+}
 
 tide_status tide_plan_trace_records(const tide_plan* plan, int32_t op, const tide_launch* launch,
                                     int64_t* records) {

@@ -258,3 +258,28 @@ def test_concurrent_host_threads(tide, orc):
         same_f32(bits_of(j["out"]), want_rs[i], "thread %d reduce-scatter" % i)
         for p in range(len(shapes)):
             same_u16(bits_of(j["params"][p]), j["want_ag"][p], "thread %d placement %d" % (i, p))
+
+
+def test_events_do_not_grow_with_calls(tide):
+    """Repeated calls that reuse the same per-call tables keep a bounded number
+    of HIP events (one reader event per stream and slot, not one per call)."""
+    shapes, N, L = [(64, 32), (9, 1)], 4, 2
+    plan = tide.plan_create(shapes, N, L)
+    g = [[torch.zeros((t, k), dtype=torch.bfloat16, device=dev()) for t, k in shapes]
+         for _ in range(L)]
+    out = torch.empty(N * plan.S, dtype=torch.float32, device=dev())
+    sh = torch.zeros(N * plan.S, dtype=torch.bfloat16, device=dev())
+    params = [torch.empty((t, k), dtype=torch.bfloat16, device=dev()) for t, k in shapes]
+    g_tab, p_tab = tide.grads_table(plan, g), tide.params_table(plan, params)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    counts = []
+    for it in range(600):
+        s = side if it % 2 else torch.cuda.current_stream()
+        tide.reduce_scatter_bf16_fp32(plan, g_tab, out, stream=s)
+        tide.allgather_place(plan, sh, p_tab, stream=s)
+        if it % 100 == 99:
+            counts.append(plan.event_count())
+    torch.cuda.synchronize()
+    assert max(counts) <= 8 * 3 + 8, counts        # ring slots x (upload + two streams) + spares
+    assert counts[-1] <= counts[0] + 2, counts
