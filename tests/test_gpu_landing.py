@@ -117,3 +117,27 @@ def test_two_level_pipeline(tide, orc):
                 flat = orc.reduce_scatter(shapes, N, M * L, [row for node in gbn for row in node])
                 for b in range(L):
                     same_f32(bits_of(shards[b]), flat[dst * L + b], "flat dst %d shard %d" % (dst, b))
+
+
+def test_landing_full_size(tide, orc):
+    """The landing sum at the size the benchmark times: L = M = 8 partials of
+    the Llama-3.1-70B layer group's shard (S = 13,369,600), full grid and
+    budgeted, every element against the oracle."""
+    from workloads.configs import CONFIGS
+    cfg = CONFIGS["llama70b_layer"]
+    L = M = cfg.L
+    S = int(orc.layout(cfg.shapes, cfg.N)["S"])
+    C = -(-S // L)
+    g = torch.Generator(device=dev())
+    g.manual_seed(11)
+    inb = [torch.randn(L * L * C, generator=g, device=dev()) for _ in range(L)]
+    h_in = [t.cpu().numpy() for t in inb]
+    say("landing full size: oracle over %d x %d floats" % (L, L * L * C))
+    want = orc.landing_sum(L, M, S, h_in)
+    for kind, launch in (("full", tide.Launch()), ("budgeted", tide.budgeted())):
+        shards = [torch.empty(S, dtype=torch.float32, device=dev()) for _ in range(L)]
+        tide.landing_sum_fp32(L, M, S, inb, shards, launch=launch)
+        torch.cuda.synchronize()
+        for b in range(L):
+            same_f32(bits_of(shards[b]), want[b], "%s shard %d" % (kind, b))
+        del shards

@@ -68,3 +68,36 @@ def test_recursive_doubling_end_to_end(tide, orc):
         torch.cuda.synchronize()
         for p in range(len(shapes)):
             same_u16(bits_of(params[p]), want[p], "node %d param %d" % (n, p))
+
+
+@pytest.mark.parametrize("name", ["llama70b_layer", "qwen3_moe_layer"])
+def test_stage_placement_full_size(tide, orc, name):
+    """Stage-order placement at the benchmark's size, half the ranks rotated
+    (stage slot k holds rank (N/2 + k) mod N): every parameter equals the
+    torch view of the unrotated shards; one parameter also against the oracle."""
+    from gpu_util import dev
+    from workloads import device_rank_major_bits
+    from workloads.configs import CONFIGS
+    cfg = CONFIGS[name]
+    N = cfg.N
+    plan = tide.plan_create(cfg.shapes, N, 1)
+    S = plan.S
+    lay = orc.layout(cfg.shapes, N)
+    rank_major = device_rank_major_bits(N * S, seed=3)
+    first = N // 2
+    stage = torch.roll(rank_major.view(N, S), shifts=-first, dims=0).contiguous().view(-1)
+    params = [torch.empty((t, k), dtype=torch.bfloat16, device=dev()) for t, k in cfg.shapes]
+    say("%s: stage-order placement, first rank %d" % (name, first))
+    tide.allgather_place_stage(plan, stage, first, params)
+    torch.cuda.synchronize()
+    v = rank_major.view(N, S)
+    for p, (t, k) in enumerate(cfg.shapes):
+        o, s = int(lay["o"][p]), int(lay["s"][p])
+        want = v[:, o:o + s].reshape(-1)[:t * k]
+        assert torch.equal(params[p].reshape(-1).view(torch.int16), want.view(torch.int16)), p
+    p = int(np.argmin([t * k for t, k in cfg.shapes]))
+    sub = [cfg.shapes[p]]
+    o, s = int(lay["o"][p]), int(lay["s"][p])
+    sub_stage = bits_of(stage.view(N, S)[:, o:o + s].contiguous())
+    want = orc.allgather_place_stage(sub, N, sub_stage, first)[0]
+    same_u16(bits_of(params[p]), want, "%s param %d vs oracle" % (name, p))
