@@ -113,6 +113,15 @@ typedef struct tide_launch {
                                 blockIdx order (tide_plan_trace_records gives the count) */
     int64_t trace_capacity;  /* records `trace` holds; a call that needs more fails with
                                 INVALID_ARG before enqueuing anything */
+    uint32_t* write_counts;  /* optional device array (debug): every element the call writes adds
+                                one (atomically) at its index, so a test can check that each
+                                output element lands exactly once. Indices: reduce-scatter
+                                r * out_stride + o_p + j (N * out_stride entries); placement
+                                N * o_p + f, f the element of parameter p (N * S entries);
+                                staging c * N * S + N * o_p + f (L * N * S entries); landing
+                                b * S + f (L * S entries). Kernel engine only. */
+    int64_t write_counts_elems; /* entries `write_counts` holds; fewer than the call needs is
+                                INVALID_ARG */
 } tide_launch;
 
 /* Force the element-at-a-time path everywhere (for testing the slow path). */

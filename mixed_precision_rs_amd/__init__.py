@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     allgather_place,
     allgather_place_stage,
     budgeted,
+    counted,
     decode_trace,
     diag_occupy,
     grads_table,

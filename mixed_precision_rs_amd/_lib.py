@@ -58,7 +58,8 @@ class Launch(ctypes.Structure):
                 ("place_blocks", ctypes.c_int32), ("max_launch_us", ctypes.c_int32),
                 ("rank_begin", ctypes.c_int32), ("rank_end", ctypes.c_int32),
                 ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("trace", ctypes.c_void_p), ("trace_capacity", ctypes.c_int64)]
+                ("trace", ctypes.c_void_p), ("trace_capacity", ctypes.c_int64),
+                ("write_counts", ctypes.c_void_p), ("write_counts_elems", ctypes.c_int64)]
 
 
 TRACE_REC_BYTES = 24          # sizeof(tide_trace_rec)
@@ -76,6 +77,16 @@ def traced(launch: Launch, buf, records: Optional[int] = None) -> Launch:
     ctypes.pointer(out)[0] = launch
     out.trace = _ptr(buf)
     out.trace_capacity = buf.numel() // 3 if records is None else int(records)
+    return out
+
+
+def counted(launch: Launch, counts) -> Launch:
+    """Copy of `launch` that adds one per written element into `counts` (a
+    zeroed int32 device tensor; see tide_launch.write_counts for the indices)."""
+    out = Launch()
+    ctypes.pointer(out)[0] = launch
+    out.write_counts = _ptr(counts)
+    out.write_counts_elems = counts.numel()
     return out
 
 

@@ -108,21 +108,37 @@ __device__ __forceinline__ void step(int64_t s, int64_t& r, int64_t& j) {
 constexpr int kWave = 64;
 constexpr int kHalf = kWave * 4;           // elements of one run
 
+// Debug write counts (tide_launch.write_counts): in the kernels instantiated
+// with CNT, every element written adds one to counts[idx .. idx + n). The
+// normal kernels (CNT false) carry no trace of it.
+template <bool CNT>
+__device__ __forceinline__ void count_writes(uint32_t* counts, int64_t idx, int n) {
+    if constexpr (CNT) {
+        for (int e = 0; e < n; ++e) atomicAdd(counts + idx + e, 1u);
+    } else {
+        (void)counts;
+        (void)idx;
+        (void)n;
+    }
+}
+
 
 // Write 4 fp32 results for flat indices f..f+3 (all inside the tile's range).
-template <int64_t kTile>
+template <int64_t kTile, bool CNT>
 __device__ __forceinline__ void store4(const Span& t, const ParamDev& pd, int64_t f,
                                        const float (&a)[4], float* __restrict__ out,
-                                       int64_t stride) {
+                                       int64_t stride, uint32_t* counts) {
     int64_t r, j;
     locate<kTile>(t, pd.s, f, r, j);
     if (j + 4 <= pd.s) {
         const f32x4_a4 x = {a[0], a[1], a[2], a[3]};
         TIDE_ST(x, reinterpret_cast<f32x4_a4*>(out + r * stride + pd.o + j));
+        count_writes<CNT>(counts, r * stride + pd.o + j, 4);
     } else {
 #pragma unroll 1
         for (int e = 0; e < 4; ++e) {
             out[r * stride + pd.o + j] = a[e];
+            count_writes<CNT>(counts, r * stride + pd.o + j, 1);
             step(pd.s, r, j);
         }
     }
@@ -160,18 +176,20 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t n) {
 // mid-line (prefix offsets that are not multiples of 4 elements) cost about
 // 3.5% of bandwidth; neither realigning them across lanes nor plain
 // write-back stores recovered it on MI355X.
-template <int64_t kTile>
+template <int64_t kTile, bool CNT>
 __device__ __forceinline__ void store_run(const Span& t, const ParamDev& pd, int64_t f_run,
                                           int lane, const float (&a)[4],
-                                          float* __restrict__ out, int64_t stride) {
+                                          float* __restrict__ out, int64_t stride,
+                                          uint32_t* counts) {
     int64_t r, j;
     locate<kTile>(t, pd.s, f_run, r, j);
     if (j + kHalf > pd.s) {                   // the run crosses into the next rank's piece
-        store4<kTile>(t, pd, f_run + 4 * lane, a, out, stride);
+        store4<kTile, CNT>(t, pd, f_run + 4 * lane, a, out, stride, counts);
         return;
     }
     const f32x4_a4 x = {a[0], a[1], a[2], a[3]};
     TIDE_ST(x, reinterpret_cast<f32x4_a4*>(out + r * stride + pd.o + j + 4 * lane));
+    count_writes<CNT>(counts, r * stride + pd.o + j + 4 * lane, 4);
 }
 
 // Workgroup tracing (tide_launch.trace): the real-time counter at the start,
@@ -201,12 +219,12 @@ __device__ __forceinline__ void trace_end(tide_trace_rec* trace, int64_t base, u
 // LT > 0: L known at compile time (fully unrolled); LT == 0: runtime L.
 // A workgroup of NT threads is NT / kThreads independent quarters of kThreads
 // threads; each quarter walks its own tiles (no barrier between quarters).
-template <int LT, int NT>
+template <int LT, int NT, bool CNT>
 __global__ __launch_bounds__(NT) void reduce_kernel(
     const TileRec* __restrict__ tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb, int32_t re,
     const ParamDev* __restrict__ params, const uint16_t* const* __restrict__ ptrs,
     const uint32_t* __restrict__ flags, int Lrt, float* __restrict__ out, int64_t out_stride,
-    tide_trace_rec* __restrict__ trace, int64_t trace_base) {
+    tide_trace_rec* __restrict__ trace, int64_t trace_base, uint32_t* __restrict__ counts) {
     const uint64_t t_begin = trace_begin(trace);
     constexpr int kSubs = NT / kThreads;
     // Budgeted (fat) workgroups walk longer tiles with more loads in flight:
@@ -271,16 +289,16 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
                 for (int u = 0; u < kUR; ++u)
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
-                        store_run<kTileR>(tr, pd, fw + (int64_t)u * kStep + h * kHalf, lane, a[u][h],
-                                  out, out_stride);
+                        store_run<kTileR, CNT>(tr, pd, fw + (int64_t)u * kStep + h * kHalf, lane, a[u][h],
+                                  out, out_stride, counts);
             } else if (interior && g0 >= pd.valid) {
                 const float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int u = 0; u < kUR; ++u)
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
-                        store_run<kTileR>(tr, pd, fw + (int64_t)u * kStep + h * kHalf, lane, z, out,
-                                  out_stride);
+                        store_run<kTileR, CNT>(tr, pd, fw + (int64_t)u * kStep + h * kHalf, lane, z, out,
+                                  out_stride, counts);
             } else {
                 // Ragged step: it crosses an end of the launch's range or of
                 // the tile, or the valid end, or the parameter has pointers
@@ -307,12 +325,12 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
                                 x1 = c == 0 ? hi : x1 + hi;
                             }
                         }
-                        store4<kTileR>(tr, pd, fu, a[0], out, out_stride);
-                        store4<kTileR>(tr, pd, fu + 4, a[1], out, out_stride);
+                        store4<kTileR, CNT>(tr, pd, fu, a[0], out, out_stride, counts);
+                        store4<kTileR, CNT>(tr, pd, fu + 4, a[1], out, out_stride, counts);
                     } else if (whole && fu >= pd.valid) {
                         const float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                        store4<kTileR>(tr, pd, fu, z, out, out_stride);
-                        store4<kTileR>(tr, pd, fu + 4, z, out, out_stride);
+                        store4<kTileR, CNT>(tr, pd, fu, z, out, out_stride, counts);
+                        store4<kTileR, CNT>(tr, pd, fu + 4, z, out, out_stride, counts);
                     } else {
                         int64_t r, j;
                         locate<kTileR>(tr, pd.s, fu, r, j);
@@ -337,6 +355,7 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
                                 }
                             }
                             out[r * out_stride + pd.o + j] = v;
+                            count_writes<CNT>(counts, r * out_stride + pd.o + j, 1);
                         }
                     }
                 }
@@ -392,13 +411,13 @@ __device__ __forceinline__ u32x4 gather8(const Span& t, const ParamDev& pd, int6
 }
 
 // Placement: param[f] = shards[rank(f) * stride + o_p + offset(f)] for true f.
-template <int NT>
+template <int NT, bool CNT>
 __global__ __launch_bounds__(NT) void place_kernel(
     const TileRec* __restrict__ tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb, int32_t re,
     const ParamDev* __restrict__ params, uint16_t* const* __restrict__ ptrs,
     const uint32_t* __restrict__ flags, const uint16_t* __restrict__ shards, int64_t stride,
     int64_t shard_elems, int32_t first, int32_t nranks, tide_trace_rec* __restrict__ trace,
-    int64_t trace_base) {
+    int64_t trace_base, uint32_t* __restrict__ counts) {
     const uint64_t t_begin = trace_begin(trace);
     constexpr int kSubs = NT / kThreads;
     constexpr int64_t kTileA = NT == kFatThreads ? kAgTileFat : kAgTile;
@@ -414,6 +433,7 @@ __global__ __launch_bounds__(NT) void place_kernel(
         const ParamDev pd = params[rec.p];
         uint16_t* dst = ptrs[rec.p];
         const bool vec = (flags[rec.p] & kFlagVector) != 0;
+        const int64_t cbase = (int64_t)nranks * pd.o;   // write counts: N * o_p + f
         const Span tr{rec.idx0, rec.idx0 - (int64_t)rec.r0 * pd.s, (int64_t)rb * pd.s,
                       min((int64_t)re * pd.s, pd.valid), rec.r0};
         const int64_t end = min(tr.idx0 + kTileA, tr.hi);
@@ -428,8 +448,10 @@ __global__ __launch_bounds__(NT) void place_kernel(
                                    first, nranks);
                 TIDE_GLOBAL u32x4* d4 = gbl_mut<u32x4>(dst + f0);
 #pragma unroll
-                for (int u = 0; u < kUA; ++u)
+                for (int u = 0; u < kUA; ++u) {
                     TIDE_ST(w[u], d4 + u * (kStep / kVec));
+                    count_writes<CNT>(counts, cbase + f0 + (int64_t)u * kStep, kVec);
+                }
             } else {
                 // Ragged step: a thread's group of 8 that lies wholly inside
                 // the bounds still goes as one vector; only a group that
@@ -442,6 +464,7 @@ __global__ __launch_bounds__(NT) void place_kernel(
                     if (vec && fu >= tr.lo && fu + kVec <= end) {
                         const u32x4 w = gather8<kTileA>(tr, pd, fu, shards, stride, shard_elems, first, nranks);
                         TIDE_ST(w, gbl_mut<u32x4>(dst + fu));
+                        count_writes<CNT>(counts, cbase + fu, kVec);
                         continue;
                     }
                     int64_t r, j;
@@ -451,6 +474,7 @@ __global__ __launch_bounds__(NT) void place_kernel(
                         const int64_t f = fu + e;
                         if (f < tr.lo || f >= end) continue;
                         d[f] = shards[stage_pos(r, first, nranks) * stride + pd.o + j];
+                        count_writes<CNT>(counts, cbase + f, 1);
                     }
                 }
             }
@@ -465,16 +489,13 @@ __global__ __launch_bounds__(NT) void place_kernel(
 // tiling, for contributor t / ntiles. With kFlagVector every pointer of the
 // parameter is 4-byte aligned, so 16-byte accesses at 8-element steps are
 // dword aligned.
-#ifndef TIDE_STAGE_NT
-#define TIDE_STAGE_NT 1
-#endif
-template <int NT>
+template <int NT, bool CNT>
 __global__ __launch_bounds__(NT) void stage_kernel(
     const TileRec* __restrict__ tiles, int64_t ntiles, int64_t tile_lo, int64_t tile_hi,
     int32_t rb, int32_t re, const ParamDev* __restrict__ params,
     const uint16_t* const* __restrict__ src, uint16_t* const* __restrict__ dst,
     const uint32_t* __restrict__ flags, int32_t L, tide_trace_rec* __restrict__ trace,
-    int64_t trace_base) {
+    int64_t trace_base, uint32_t* __restrict__ counts, int64_t slot_elems, int32_t nranks) {
     const uint64_t t_begin = trace_begin(trace);
     constexpr int kSubs = NT / kThreads;
     constexpr int64_t kTileS = NT == kFatThreads ? kStageTileFat : kStageTile;
@@ -491,27 +512,18 @@ __global__ __launch_bounds__(NT) void stage_kernel(
         const bool vec = (flags[rec.p] & kFlagVector) != 0;
         const int64_t lo = (int64_t)rb * pd.s;
         const int64_t end = min(rec.idx0 + kTileS, min((int64_t)re * pd.s, pd.valid));
+        const int64_t cbase = c * slot_elems + (int64_t)nranks * pd.o;   // write counts
         for (int64_t g0 = rec.idx0; g0 < end; g0 += kUS * kStep) {
             const int64_t f0 = g0 + (int64_t)tid * kVec;
             if (vec && g0 >= lo && g0 + kUS * kStep <= end) {
                 u32x4_a4 w[kUS];
 #pragma unroll
-                for (int u = 0; u < kUS; ++u) {
-                    const TIDE_GLOBAL u32x4_a4* a = gbl<u32x4_a4>(s + f0 + (int64_t)u * kStep);
-#if TIDE_STAGE_NT
-                    w[u] = __builtin_nontemporal_load(a);
-#else
-                    w[u] = *a;
-#endif
-                }
+                for (int u = 0; u < kUS; ++u)
+                    w[u] = TIDE_LD(gbl<u32x4_a4>(s + f0 + (int64_t)u * kStep));
 #pragma unroll
                 for (int u = 0; u < kUS; ++u) {
-                    TIDE_GLOBAL u32x4_a4* b = gbl_mut<u32x4_a4>(d + f0 + (int64_t)u * kStep);
-#if TIDE_STAGE_NT
-                    __builtin_nontemporal_store(w[u], b);
-#else
-                    *b = w[u];
-#endif
+                    TIDE_ST(w[u], gbl_mut<u32x4_a4>(d + f0 + (int64_t)u * kStep));
+                    count_writes<CNT>(counts, cbase + f0 + (int64_t)u * kStep, kVec);
                 }
             } else {
                 // Ragged step: whole groups of 8 inside the bounds as vectors,
@@ -524,12 +536,16 @@ __global__ __launch_bounds__(NT) void stage_kernel(
                     if (vec && fu >= lo && fu + kVec <= end) {
                         const u32x4_a4 w = TIDE_LD(gbl<u32x4_a4>(s + fu));
                         TIDE_ST(w, gbl_mut<u32x4_a4>(d + fu));
+                        count_writes<CNT>(counts, cbase + fu, kVec);
                         continue;
                     }
 #pragma unroll 1
                     for (int e = 0; e < kVec; ++e) {
                         const int64_t f = fu + e;
-                        if (f >= lo && f < end) gd[f] = gs[f];
+                        if (f >= lo && f < end) {
+                            gd[f] = gs[f];
+                            count_writes<CNT>(counts, cbase + f, 1);
+                        }
                     }
                 }
             }
@@ -542,13 +558,14 @@ __global__ __launch_bounds__(NT) void stage_kernel(
 // with s = f / C, e = f % C. All M inboxes are read at the same offset (the
 // Latin-square seating puts a slice's copies at the same address on M
 // GPUs), 16 bytes per lane, so each wave reads M contiguous 1 KiB runs.
-template <int MT, int NT>
+template <int MT, int NT, bool CNT>
 __global__ __launch_bounds__(NT) void landing_kernel(LandingPtrs ptrs, int32_t L, int32_t Mrt,
                                                      int64_t S, int64_t C, int64_t tiles_per_shard,
                                                      int64_t tile_lo, int64_t tile_hi,
                                                      int32_t accumulate, int32_t scalar,
                                                      tide_trace_rec* __restrict__ trace,
-                                                     int64_t trace_base) {
+                                                     int64_t trace_base,
+                                                     uint32_t* __restrict__ counts) {
     const uint64_t t_begin = trace_begin(trace);
     constexpr int kSubs = NT / kThreads;
     const int M = MT > 0 ? MT : Mrt;
@@ -579,6 +596,7 @@ __global__ __launch_bounds__(NT) void landing_kernel(LandingPtrs ptrs, int32_t L
                 TIDE_GLOBAL f32x4_a4* dst = gbl_mut<f32x4_a4>(shard + f);
                 if (accumulate) acc = *dst + acc;
                 TIDE_ST(acc, dst);
+                count_writes<CNT>(counts, b * S + f, 4);
             } else {
 #pragma unroll 1
                 for (int k = 0; k < 4 && f + k < end; ++k) {
@@ -595,6 +613,7 @@ __global__ __launch_bounds__(NT) void landing_kernel(LandingPtrs ptrs, int32_t L
                     }
                     TIDE_GLOBAL float* dst = gbl_mut<float>(shard + ff);
                     *dst = accumulate ? *dst + acc : acc;
+                    count_writes<CNT>(counts, b * S + ff, 1);
                 }
             }
         }
@@ -616,14 +635,19 @@ hipError_t launch_landing_t(int M, int grid, int threads, size_t lds, hipStream_
                             const LandingPtrs& ptrs, int32_t L, int64_t S, int64_t C,
                             int64_t tiles_per_shard, int64_t tile_lo, int64_t tile_hi,
                             int32_t accumulate, int32_t scalar, tide_trace_rec* trace,
-                            int64_t trace_base) {
+                            int64_t trace_base, uint32_t* counts) {
     LandingPtrs p = ptrs;
     int32_t Mrt = M;
     void* args[] = {&p, &L, &Mrt, &S, &C, &tiles_per_shard, &tile_lo, &tile_hi, &accumulate,
-                    &scalar, &trace, &trace_base};
-    const void* fn = threads == kFatThreads
-                         ? reinterpret_cast<const void*>(&landing_kernel<MT, kFatThreads>)
-                         : reinterpret_cast<const void*>(&landing_kernel<MT, kThreads>);
+                    &scalar, &trace, &trace_base, &counts};
+    // Counted calls (debug) take the runtime-M kernel with counting compiled in.
+    const void* fn =
+        counts ? (threads == kFatThreads
+                      ? reinterpret_cast<const void*>(&landing_kernel<0, kFatThreads, true>)
+                      : reinterpret_cast<const void*>(&landing_kernel<0, kThreads, true>))
+               : (threads == kFatThreads
+                      ? reinterpret_cast<const void*>(&landing_kernel<MT, kFatThreads, false>)
+                      : reinterpret_cast<const void*>(&landing_kernel<MT, kThreads, false>));
     return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, lds, stream);
 }
 
@@ -632,12 +656,17 @@ hipError_t launch_reduce_t(int L, int grid, int threads, size_t lds, hipStream_t
                            const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                            int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
                            const uint32_t* flags, float* out, int64_t out_stride,
-                           tide_trace_rec* trace, int64_t trace_base) {
+                           tide_trace_rec* trace, int64_t trace_base, uint32_t* counts) {
     void* args[] = {&tiles, &tile_lo, &tile_hi, &rb, &re, &params, &ptrs, &flags, &L, &out,
-                    &out_stride, &trace, &trace_base};
-    const void* fn = threads == kFatThreads
-                         ? reinterpret_cast<const void*>(&reduce_kernel<LT, kFatThreads>)
-                         : reinterpret_cast<const void*>(&reduce_kernel<LT, kThreads>);
+                    &out_stride, &trace, &trace_base, &counts};
+    // Counted calls (debug) take the runtime-L kernel with counting compiled in.
+    const void* fn =
+        counts ? (threads == kFatThreads
+                      ? reinterpret_cast<const void*>(&reduce_kernel<0, kFatThreads, true>)
+                      : reinterpret_cast<const void*>(&reduce_kernel<0, kThreads, true>))
+               : (threads == kFatThreads
+                      ? reinterpret_cast<const void*>(&reduce_kernel<LT, kFatThreads, false>)
+                      : reinterpret_cast<const void*>(&reduce_kernel<LT, kThreads, false>));
     return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, lds, stream);
 }
 
@@ -647,11 +676,12 @@ hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t s
                          const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                          int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
                          const uint32_t* flags, float* out, int64_t out_stride,
-                         tide_trace_rec* trace, int64_t trace_base) {
+                         tide_trace_rec* trace, int64_t trace_base, uint32_t* counts) {
 #define TIDE_REDUCE_CASE(n)                                                                   \
     case n:                                                                                   \
         return launch_reduce_t<n>(L, grid, threads, lds, stream, tiles, tile_lo, tile_hi, rb, \
-                                  re, params, ptrs, flags, out, out_stride, trace, trace_base);
+                                  re, params, ptrs, flags, out, out_stride, trace, trace_base, \
+                                  counts);
     switch (L) {
         TIDE_REDUCE_CASE(1)
         TIDE_REDUCE_CASE(2)
@@ -663,7 +693,8 @@ hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t s
         TIDE_REDUCE_CASE(8)
         default:
             return launch_reduce_t<0>(L, grid, threads, lds, stream, tiles, tile_lo, tile_hi, rb,
-                                      re, params, ptrs, flags, out, out_stride, trace, trace_base);
+                                      re, params, ptrs, flags, out, out_stride, trace, trace_base,
+                                      counts);
     }
 #undef TIDE_REDUCE_CASE
 }
@@ -673,12 +704,17 @@ hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
                         int32_t re, const ParamDev* params, uint16_t* const* ptrs,
                         const uint32_t* flags, const uint16_t* shards, int64_t shard_stride,
                         int64_t shard_elems, int32_t first_rank, int32_t nranks,
-                        tide_trace_rec* trace, int64_t trace_base) {
+                        tide_trace_rec* trace, int64_t trace_base, uint32_t* counts) {
     void* args[] = {&tiles, &tile_lo, &tile_hi, &rb, &re, &params, &ptrs, &flags, &shards,
-                    &shard_stride, &shard_elems, &first_rank, &nranks, &trace, &trace_base};
-    const void* fn = threads == kFatThreads
-                         ? reinterpret_cast<const void*>(&place_kernel<kFatThreads>)
-                         : reinterpret_cast<const void*>(&place_kernel<kThreads>);
+                    &shard_stride, &shard_elems, &first_rank, &nranks, &trace, &trace_base,
+                    &counts};
+    const void* fn =
+        counts ? (threads == kFatThreads
+                      ? reinterpret_cast<const void*>(&place_kernel<kFatThreads, true>)
+                      : reinterpret_cast<const void*>(&place_kernel<kThreads, true>))
+               : (threads == kFatThreads
+                      ? reinterpret_cast<const void*>(&place_kernel<kFatThreads, false>)
+                      : reinterpret_cast<const void*>(&place_kernel<kThreads, false>));
     return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, lds, stream);
 }
 
@@ -686,12 +722,17 @@ hipError_t launch_stage(int grid, int threads, size_t lds, hipStream_t stream,
                         const TileRec* tiles, int64_t ntiles, int64_t tile_lo, int64_t tile_hi,
                         int32_t rb, int32_t re, const ParamDev* params,
                         const uint16_t* const* src, uint16_t* const* dst, const uint32_t* flags,
-                        int32_t L, tide_trace_rec* trace, int64_t trace_base) {
+                        int32_t L, tide_trace_rec* trace, int64_t trace_base, uint32_t* counts,
+                        int64_t slot_elems, int32_t nranks) {
     void* args[] = {&tiles, &ntiles, &tile_lo, &tile_hi, &rb, &re, &params, &src, &dst, &flags,
-                    &L, &trace, &trace_base};
-    const void* fn = threads == kFatThreads
-                         ? reinterpret_cast<const void*>(&stage_kernel<kFatThreads>)
-                         : reinterpret_cast<const void*>(&stage_kernel<kThreads>);
+                    &L, &trace, &trace_base, &counts, &slot_elems, &nranks};
+    const void* fn =
+        counts ? (threads == kFatThreads
+                      ? reinterpret_cast<const void*>(&stage_kernel<kFatThreads, true>)
+                      : reinterpret_cast<const void*>(&stage_kernel<kThreads, true>))
+               : (threads == kFatThreads
+                      ? reinterpret_cast<const void*>(&stage_kernel<kFatThreads, false>)
+                      : reinterpret_cast<const void*>(&stage_kernel<kThreads, false>));
     return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, lds, stream);
 }
 
@@ -699,12 +740,12 @@ hipError_t launch_landing(int M, int grid, int threads, size_t lds, hipStream_t 
                           const LandingPtrs& ptrs, int32_t L, int64_t S, int64_t C,
                           int64_t tiles_per_shard, int64_t tile_lo, int64_t tile_hi,
                           int32_t accumulate, int32_t scalar, tide_trace_rec* trace,
-                          int64_t trace_base) {
+                          int64_t trace_base, uint32_t* counts) {
 #define TIDE_LANDING_CASE(n)                                                                  \
     case n:                                                                                   \
         return launch_landing_t<n>(M, grid, threads, lds, stream, ptrs, L, S, C,             \
                                    tiles_per_shard, tile_lo, tile_hi, accumulate, scalar,     \
-                                   trace, trace_base);
+                                   trace, trace_base, counts);
     switch (M) {
         TIDE_LANDING_CASE(1)
         TIDE_LANDING_CASE(2)
@@ -717,7 +758,7 @@ hipError_t launch_landing(int M, int grid, int threads, size_t lds, hipStream_t 
         default:
             return launch_landing_t<0>(M, grid, threads, lds, stream, ptrs, L, S, C,
                                        tiles_per_shard, tile_lo, tile_hi, accumulate, scalar,
-                                       trace, trace_base);
+                                       trace, trace_base, counts);
     }
 #undef TIDE_LANDING_CASE
 }
@@ -737,10 +778,13 @@ hipError_t allow_dynamic_lds_landing(int M, size_t lds) {
 #define TIDE_LDS_LANDING_CASE(n)                                                              \
     case n: {                                                                                 \
         hipError_t e = hipFuncSetAttribute(                                                   \
-            reinterpret_cast<const void*>(&landing_kernel<n, kFatThreads>),                   \
+            reinterpret_cast<const void*>(&landing_kernel<n, kFatThreads, false>),            \
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                            \
         if (e != hipSuccess) return e;                                                        \
-        return hipFuncSetAttribute(reinterpret_cast<const void*>(&landing_kernel<n, kThreads>), \
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&landing_kernel<0, kFatThreads, true>), \
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);        \
+        if (e != hipSuccess) return e;                                                        \
+        return hipFuncSetAttribute(reinterpret_cast<const void*>(&landing_kernel<n, kThreads, false>), \
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);     \
     }
     switch (M) {
@@ -761,20 +805,18 @@ hipError_t allow_dynamic_lds_landing(int M, size_t lds) {
 
 hipError_t allow_dynamic_lds(int L, size_t lds) {
     // Dynamic LDS beyond the default per-workgroup limit needs opting in per kernel.
-    const void* fns[] = {reinterpret_cast<const void*>(&place_kernel<kFatThreads>),
-                         reinterpret_cast<const void*>(&place_kernel<kThreads>),
-                         reinterpret_cast<const void*>(&stage_kernel<kFatThreads>),
-                         reinterpret_cast<const void*>(&stage_kernel<kThreads>)};
+    const void* fns[] = {reinterpret_cast<const void*>(&place_kernel<kFatThreads, false>),
+                         reinterpret_cast<const void*>(&place_kernel<kFatThreads, true>),
+                         reinterpret_cast<const void*>(&stage_kernel<kFatThreads, false>),
+                         reinterpret_cast<const void*>(&stage_kernel<kFatThreads, true>),
+                         reinterpret_cast<const void*>(&reduce_kernel<0, kFatThreads, true>)};
     for (const void* f : fns) {
         hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
 #define TIDE_LDS_CASE(n)                                                                      \
     case n: {                                                                                 \
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&reduce_kernel<n, kFatThreads>), \
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
-        if (e != hipSuccess) return e;                                                        \
-        return hipFuncSetAttribute(reinterpret_cast<const void*>(&reduce_kernel<n, kThreads>), \
+        return hipFuncSetAttribute(reinterpret_cast<const void*>(&reduce_kernel<n, kFatThreads, false>), \
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);     \
     }
     switch (L) {

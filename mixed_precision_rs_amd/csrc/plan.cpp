@@ -53,9 +53,6 @@ constexpr int kDefaultMaxLaunchUs = 300;
 // their CU's LDS, so no other kernel's workgroup (a GEMM's, typically) shares
 // the CU with them: the concurrent kernel's workgroups are placed on the many
 // idle CUs instead of running beside a streaming workgroup.
-#ifndef TIDE_BUDGET_THREADS
-#define TIDE_BUDGET_THREADS kFatThreads
-#endif
 #ifndef TIDE_BUDGET_LDS
 #define TIDE_BUDGET_LDS (128 * 1024)
 #endif
@@ -72,7 +69,7 @@ constexpr int kDefaultMaxLaunchUs = 300;
 #ifndef TIDE_WG_BYTES_PER_US_LANDING
 #define TIDE_WG_BYTES_PER_US_LANDING 35000
 #endif
-constexpr int kBudgetThreads = TIDE_BUDGET_THREADS;
+constexpr int kBudgetThreads = kFatThreads;
 constexpr size_t kBudgetLds = TIDE_BUDGET_LDS;
 constexpr int64_t kWgBytesPerUsRs = TIDE_WG_BYTES_PER_US_RS;
 constexpr int64_t kWgBytesPerUsAg = TIDE_WG_BYTES_PER_US_AG;       // placement and staging
@@ -172,6 +169,7 @@ tide_status resolve_launch(const tide_plan* plan, const tide_launch* in, tide_la
     if (l.reserved != 0 || (l.flags & ~kKnownFlags) != 0)
         return fail(TIDE_ERR_INVALID_ARG, "unknown launch flags 0x%x", l.flags);
     if (l.trace_capacity < 0) return fail(TIDE_ERR_INVALID_ARG, "negative trace_capacity");
+    if (l.write_counts_elems < 0) return fail(TIDE_ERR_INVALID_ARG, "negative write_counts_elems");
     if (l.reduce_blocks == 0) l.reduce_blocks = kDefaultReduceBlocks;
     if (l.place_blocks == 0) l.place_blocks = kDefaultPlaceBlocks;
     if (l.max_launch_us == 0) l.max_launch_us = kDefaultMaxLaunchUs;
@@ -475,6 +473,14 @@ int64_t launch_records(const tide_plan* plan, int op, const tide_launch& l, int6
     return n;
 }
 
+// A counted call needs `need` entries; checked before anything is enqueued.
+tide_status check_counts(const tide_launch& l, int64_t need) {
+    if (l.write_counts && l.write_counts_elems < need)
+        return fail(TIDE_ERR_INVALID_ARG, "write_counts holds %lld entries, the call needs %lld",
+                    (long long)l.write_counts_elems, (long long)need);
+    return TIDE_OK;
+}
+
 // A traced call must have room for every record before anything is enqueued.
 tide_status check_trace(const tide_launch& l, int64_t records) {
     if (l.trace && records > l.trace_capacity)
@@ -605,6 +611,8 @@ tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t*
         int64_t total;
         if (!mul_ok(out_stride, plan->N, &total) || !mul_ok(total, 4, &total))
             return fail(TIDE_ERR_OVERFLOW, "N * out_stride * 4 overflows int64");
+        st = check_counts(l, total / 4);
+        if (st != TIDE_OK) return st;
         const bool work = plan->S > 0 && l.rank_end > l.rank_begin;
         if (!work) return TIDE_OK;
         if (!out) return fail(TIDE_ERR_INVALID_ARG, "out is NULL");
@@ -664,7 +672,7 @@ tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t*
                                  int64_t tb) {
             return launch_reduce(L, grid, threads, lds, stream, tt->dev, lo, hi, l.rank_begin,
                                  l.rank_end, ds->params, dptrs, dflags, out, out_stride, l.trace,
-                                 tb);
+                                 tb, l.write_counts);
         });
         tide_status st2 = release_slot(ds, slot, stream);
         return st != TIDE_OK ? st : st2;
@@ -700,6 +708,10 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* sh
         if (engine == TIDE_ENGINE_SDMA)
             return fail(TIDE_ERR_UNSUPPORTED,
                         "the placement has no DMA-engine path (no compute-unit-free strided copy)");
+        if (l.write_counts && engine != TIDE_ENGINE_KERNEL)
+            return fail(TIDE_ERR_INVALID_ARG, "write counts need the kernel engine");
+        st = check_counts(l, (int64_t)plan->N * plan->S);
+        if (st != TIDE_OK) return st;
         const int32_t P = plan->P;
         if (shard_stride < plan->S)
             return fail(TIDE_ERR_INVALID_ARG, "shard_stride %lld < S %lld",
@@ -802,7 +814,7 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* sh
                                  int64_t tb) {
             return launch_place(grid, threads, lds, stream, tt->dev, lo, hi, l.rank_begin,
                                 l.rank_end, ds->params, dptrs, dflags, shards, shard_stride,
-                                shard_elems, first_rank, plan->N, l.trace, tb);
+                                shard_elems, first_rank, plan->N, l.trace, tb, l.write_counts);
         });
         tide_status st2 = release_slot(ds, slot, stream);
         return st != TIDE_OK ? st : st2;
@@ -827,6 +839,13 @@ tide_status tide_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* 
                         engine);
         const int32_t P = plan->P, L = plan->L;
         const int64_t slot_elems = (int64_t)plan->N * plan->S;   // fits: checked at plan creation
+        if (l.write_counts && engine != TIDE_ENGINE_KERNEL)
+            return fail(TIDE_ERR_INVALID_ARG, "write counts need the kernel engine");
+        int64_t counts_need;
+        if (!mul_ok(slot_elems, L, &counts_need))
+            return fail(TIDE_ERR_OVERFLOW, "L * N * S overflows int64");
+        st = check_counts(l, counts_need);
+        if (st != TIDE_OK) return st;
         if (plan->S == 0 || l.rank_end == l.rank_begin) return TIDE_OK;
         if (!slots) return fail(TIDE_ERR_INVALID_ARG, "slots is NULL");
         if (P > 0 && !grads) return fail(TIDE_ERR_INVALID_ARG, "grads is NULL");
@@ -917,7 +936,8 @@ tide_status tide_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* 
                              [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi,
                                  int64_t tb) {
             return launch_stage(grid, threads, lds, stream, tt->dev, ntiles, lo, hi, l.rank_begin,
-                                l.rank_end, ds->params, dsrc, ddst, dflags, L, l.trace, tb);
+                                l.rank_end, ds->params, dsrc, ddst, dflags, L, l.trace, tb,
+                                l.write_counts, slot_elems, plan->N);
         });
         tide_status st2 = release_slot(ds, slot, stream);
         return st != TIDE_OK ? st : st2;
@@ -992,6 +1012,7 @@ tide_status landing_launch(int32_t L, int32_t M, int64_t S, int32_t accumulate,
     if (l.reserved != 0 || (l.flags & ~kKnownFlags) != 0)
         return fail(TIDE_ERR_INVALID_ARG, "unknown launch flags 0x%x", l.flags);
     if (l.trace_capacity < 0) return fail(TIDE_ERR_INVALID_ARG, "negative trace_capacity");
+    if (l.write_counts_elems < 0) return fail(TIDE_ERR_INVALID_ARG, "negative write_counts_elems");
     if (l.place_blocks == 0) l.place_blocks = kDefaultPlaceBlocks;
     if (l.max_launch_us == 0) l.max_launch_us = kDefaultMaxLaunchUs;
     *out = l;
@@ -1059,6 +1080,8 @@ tide_status tide_landing_sum_fp32(int32_t L, int32_t M, int64_t S, const float* 
         });
         st = check_trace(l, records);
         if (st != TIDE_OK) return st;
+        st = check_counts(l, (int64_t)L * S);
+        if (st != TIDE_OK) return st;
         hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
         const int64_t tiles_per_shard = (S + kLandTile - 1) / kLandTile;
         const int32_t scalar = (l.flags & TIDE_FLAG_SCALAR_PATH) ? 1 : 0;
@@ -1077,7 +1100,7 @@ tide_status tide_landing_sum_fp32(int32_t L, int32_t M, int64_t S, const float* 
         TIDE_HIP_TRY(for_each_landing_launch(L, M, S, accumulate, l,
                      [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi, int64_t tb) {
             return launch_landing(M, grid, threads, lds, stream, ptrs, L, S, C, tiles_per_shard,
-                                  lo, hi, accumulate, scalar, l.trace, tb);
+                                  lo, hi, accumulate, scalar, l.trace, tb, l.write_counts);
         }));
         return TIDE_OK;
     } catch (const std::bad_alloc&) {

@@ -110,20 +110,22 @@ constexpr uint32_t kFlagVector = 1u;  // every pointer of this parameter allows 
 // Launch wrappers (kernels.hip). threads is kThreads or kFatThreads; lds is
 // dynamic LDS reserved per workgroup (unused by the kernels: it only keeps
 // other kernels' workgroups off the CU). trace, when not null, receives one
-// record per workgroup at trace[trace_base + blockIdx.x]. Return the launch's
-// hipError_t.
+// record per workgroup at trace[trace_base + blockIdx.x]; counts, when not
+// null, gets one added per element written (reduce: at the output offset;
+// placement: at N * o_p + f; staging: at c * N * S + N * o_p + f; landing: at
+// b * S + f). Return the launch's hipError_t.
 hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t stream,
                          const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                          int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
                          const uint32_t* flags, float* out, int64_t out_stride,
-                         tide_trace_rec* trace, int64_t trace_base);
+                         tide_trace_rec* trace, int64_t trace_base, uint32_t* counts);
 
 hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
                         const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                         int32_t re, const ParamDev* params, uint16_t* const* ptrs,
                         const uint32_t* flags, const uint16_t* shards, int64_t shard_stride,
                         int64_t shard_elems, int32_t first_rank, int32_t nranks,
-                        tide_trace_rec* trace, int64_t trace_base);
+                        tide_trace_rec* trace, int64_t trace_base, uint32_t* counts);
 
 // Slot-Reuse staging (kernels.hip): tiles [tile_lo, tile_hi) of L copies of
 // the staging tiling (ntiles tiles of kStageTile elements over each
@@ -133,7 +135,8 @@ hipError_t launch_stage(int grid, int threads, size_t lds, hipStream_t stream,
                         const TileRec* tiles, int64_t ntiles, int64_t tile_lo, int64_t tile_hi,
                         int32_t rb, int32_t re, const ParamDev* params,
                         const uint16_t* const* src, uint16_t* const* dst, const uint32_t* flags,
-                        int32_t L, tide_trace_rec* trace, int64_t trace_base);
+                        int32_t L, tide_trace_rec* trace, int64_t trace_base, uint32_t* counts,
+                        int64_t slot_elems, int32_t nranks);
 
 // Level-2 landing sum (kernels.hip). The node's inbox and shard pointers travel
 // in the kernel arguments (at most kMaxLanding GPUs per node).
@@ -147,7 +150,7 @@ hipError_t launch_landing(int M, int grid, int threads, size_t lds, hipStream_t 
                           const LandingPtrs& ptrs, int32_t L, int64_t S, int64_t C,
                           int64_t tiles_per_shard, int64_t tile_lo, int64_t tile_hi,
                           int32_t accumulate, int32_t scalar, tide_trace_rec* trace,
-                          int64_t trace_base);
+                          int64_t trace_base, uint32_t* counts);
 // Diagnostic occupant (tide_diag_occupy).
 hipError_t launch_occupy(int grid, int threads, size_t lds, hipStream_t stream, int64_t spin_ticks,
                          tide_trace_rec* trace);
