@@ -95,6 +95,13 @@ typedef struct tide_trace_rec {
     uint64_t t_end;          /* same, once all of its waves had finished their work */
 } tide_trace_rec;
 
+/* Graph capture. The reduce-scatter, and the placement and staging with the
+ * kernel engine, read a per-call pointer table from a small ring the library
+ * reuses; a captured graph would replay against whatever the ring holds by
+ * then. On a capturing stream these calls return TIDE_ERR_UNSUPPORTED before
+ * enqueuing anything. The runtime-copy engine, the landing sum and the
+ * diagnostic occupant pass everything by value and may be captured. */
+
 /* Launch options. A zero-filled struct (or a NULL pointer) means: full grid,
  * all ranks. Fields equal to 0 take their defaults. */
 typedef struct tide_launch {

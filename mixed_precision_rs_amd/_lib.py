@@ -316,6 +316,8 @@ def _record(tensors, stream_obj):
         return
     if stream_obj == torch.cuda.default_stream(stream_obj.device):
         return
+    if torch.cuda.is_current_stream_capturing():
+        return                      # a captured graph keeps its own references
     for t in tensors:
         if t is not None and not isinstance(t, int):
             t.record_stream(stream_obj)

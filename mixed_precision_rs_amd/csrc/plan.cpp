@@ -473,6 +473,19 @@ int64_t launch_records(const tide_plan* plan, int op, const tide_launch& l, int6
     return n;
 }
 
+// Calls that read a per-call pointer table from the ring cannot be captured
+// into a graph: a replay would read whatever table the slot holds by then.
+tide_status refuse_capture(hipStream_t stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    TIDE_HIP_TRY(hipStreamIsCapturing(stream, &cs));
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(TIDE_ERR_UNSUPPORTED,
+                    "the stream is capturing a graph; this call reads a per-call pointer table "
+                    "that a replay could not rely on (capture the runtime-copy engine or the "
+                    "landing sum instead)");
+    return TIDE_OK;
+}
+
 // A counted call needs `need` entries; checked before anything is enqueued.
 tide_status check_counts(const tide_launch& l, int64_t need) {
     if (l.write_counts && l.write_counts_elems < need)
@@ -645,6 +658,8 @@ tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t*
             fl[p] = f;
         }
         hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+        st = refuse_capture(stream);
+        if (st != TIDE_OK) return st;
         std::lock_guard<std::mutex> lock(plan->mu);
         int dev;
         st = stream_device(stream, &dev);
@@ -788,6 +803,8 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* sh
             }
             return TIDE_OK;
         }
+        st = refuse_capture(stream);
+        if (st != TIDE_OK) return st;
         std::lock_guard<std::mutex> lock(plan->mu);
         int dev;
         st = stream_device(stream, &dev);
@@ -909,6 +926,8 @@ tide_status tide_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* 
             }
             return TIDE_OK;
         }
+        st = refuse_capture(stream);
+        if (st != TIDE_OK) return st;
         std::lock_guard<std::mutex> lock(plan->mu);
         int dev;
         st = stream_device(stream, &dev);
