@@ -95,12 +95,13 @@ typedef struct tide_trace_rec {
     uint64_t t_end;          /* same, once all of its waves had finished their work */
 } tide_trace_rec;
 
-/* Graph capture. The reduce-scatter, and the placement and staging with the
- * kernel engine, read a per-call pointer table from a small ring the library
- * reuses; a captured graph would replay against whatever the ring holds by
- * then. On a capturing stream these calls return TIDE_ERR_UNSUPPORTED before
- * enqueuing anything. The runtime-copy engine, the landing sum and the
- * diagnostic occupant pass everything by value and may be captured. */
+/* Graph capture. The eager reduce-scatter, and the eager placement and
+ * staging with the kernel engine, read a per-call pointer table from a small
+ * ring the library reuses; a captured graph would replay against whatever the
+ * ring holds by then. On a capturing stream these calls return
+ * TIDE_ERR_UNSUPPORTED before enqueuing anything. Prepared calls
+ * (tide_call_enqueue), the runtime-copy engine, the landing sum and the
+ * diagnostic occupant keep everything they read fixed and may be captured. */
 
 /* Launch options. A zero-filled struct (or a NULL pointer) means: full grid,
  * all ranks. Fields equal to 0 take their defaults. */
@@ -259,6 +260,39 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* st
 tide_status tide_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* grads,
                                   uint16_t* const* slots, void* stream, int32_t engine,
                                   const tide_launch* launch);
+
+/*
+ * Prepared calls. A training step issues the same collectives on the same
+ * buffers every time; a prepared call validates those buffers once, copies
+ * its pointer table to a device allocation of its own, and is then enqueued
+ * with no host-side table work at all. Because its table never changes,
+ * tide_call_enqueue may be captured into a HIP graph and replayed.
+ *   - The tide_prepare_* calls take the same arguments as the eager calls
+ *     (kernel engine only), validate them the same way, and build the call on
+ *     the current HIP device. They allocate (device table, the plan's
+ *     per-device tables on first use) and copy synchronously.
+ *   - tide_call_enqueue(call, stream): stream must be on the call's device.
+ *     Launches the call's kernels, nothing else; allocates nothing; may be
+ *     captured. The buffers given at preparation must still be valid, and
+ *     their contents are read or written at the time the work runs.
+ *   - tide_call_destroy: frees the device table (NULL-safe). Destroy a call
+ *     after the work it enqueued has completed, and before its plan.
+ */
+typedef struct tide_call tide_call;
+
+tide_status tide_prepare_reduce_scatter_bf16_fp32(const tide_plan* plan,
+                                                  const uint16_t* const* grads, float* out,
+                                                  int64_t out_stride, const tide_launch* launch,
+                                                  tide_call** call);
+tide_status tide_prepare_allgather_place_stage(const tide_plan* plan, const uint16_t* shards,
+                                               int64_t shard_stride, int32_t first_rank,
+                                               uint16_t* const* params, const tide_launch* launch,
+                                               tide_call** call);
+tide_status tide_prepare_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* grads,
+                                          uint16_t* const* slots, const tide_launch* launch,
+                                          tide_call** call);
+tide_status tide_call_enqueue(const tide_call* call, void* stream);
+void tide_call_destroy(tide_call* call);
 
 /* One round of node n's recursive-doubling all-gather schedule. */
 typedef struct tide_rd_step {

@@ -4,6 +4,7 @@ placement into parameter storage (C ABI in include/tide.h, HIP kernels for
 gfx950 in csrc/). Importing this package loads libtide.so and fails loudly if
 it has not been built."""
 from ._lib import (  # noqa: F401
+    Call,
     ENGINE_KERNEL,
     ENGINE_RUNTIME,
     ENGINE_SDMA,
@@ -31,6 +32,9 @@ from ._lib import (  # noqa: F401
     lib,
     params_table,
     plan_create,
+    prepare_allgather_place,
+    prepare_reduce_scatter_bf16_fp32,
+    prepare_stage_grads_bf16,
     rd_schedule,
     reduce_scatter_bf16_fp32,
     slot_grads_table,

@@ -32,7 +32,9 @@ EXPORTS = ["tide_plan_create", "tide_plan_destroy", "tide_plan_dims", "tide_plan
            "tide_version", "tide_allgather_place_stage", "tide_rd_schedule",
            "tide_landing_sum_fp32", "tide_latin_square", "tide_stage_grads_bf16",
            "tide_plan_trace_records", "tide_landing_trace_records", "tide_diag_occupy",
-           "tide_plan_event_count"]
+           "tide_plan_event_count", "tide_prepare_reduce_scatter_bf16_fp32",
+           "tide_prepare_allgather_place_stage", "tide_prepare_stage_grads_bf16",
+           "tide_call_enqueue", "tide_call_destroy"]
 
 
 class TideError(RuntimeError):
@@ -160,6 +162,17 @@ def _load():
     lib.tide_landing_trace_records.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                                ctypes.c_int32, ctypes.POINTER(Launch), _I64P]
     lib.tide_plan_event_count.argtypes = [ctypes.c_void_p, _I64P]
+    lib.tide_prepare_reduce_scatter_bf16_fp32.argtypes = [
+        ctypes.c_void_p, _VPP, ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(Launch),
+        ctypes.POINTER(ctypes.c_void_p)]
+    lib.tide_prepare_allgather_place_stage.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, _VPP,
+        ctypes.POINTER(Launch), ctypes.POINTER(ctypes.c_void_p)]
+    lib.tide_prepare_stage_grads_bf16.argtypes = [
+        ctypes.c_void_p, _VPP, _VPP, ctypes.POINTER(Launch), ctypes.POINTER(ctypes.c_void_p)]
+    lib.tide_call_enqueue.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.tide_call_destroy.argtypes = [ctypes.c_void_p]
+    lib.tide_call_destroy.restype = None
     lib.tide_diag_occupy.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     lib.tide_status_string.argtypes = [ctypes.c_int]
@@ -172,7 +185,9 @@ def _load():
               "tide_reduce_scatter_bf16_fp32", "tide_allgather_place", "tide_plan_launch_count",
               "tide_allgather_place_stage", "tide_rd_schedule", "tide_landing_sum_fp32",
               "tide_latin_square", "tide_stage_grads_bf16", "tide_plan_trace_records",
-              "tide_landing_trace_records", "tide_diag_occupy", "tide_plan_event_count"):
+              "tide_landing_trace_records", "tide_diag_occupy", "tide_plan_event_count",
+              "tide_prepare_reduce_scatter_bf16_fp32", "tide_prepare_allgather_place_stage",
+              "tide_prepare_stage_grads_bf16", "tide_call_enqueue"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -413,6 +428,72 @@ def slot_grads_table(plan: Plan, slots: Sequence[object]) -> PointerTable:
     tab = PointerTable([_ptr(slots[c]) + offs[p] for c in range(plan.L) for p in range(plan.P)])
     tab.refs = list(slots)
     return tab
+
+
+class Call:
+    """A prepared call (tide_call): buffers validated once, its pointer table
+    on the device; enqueue() launches its kernels only, so it may be captured
+    into a graph. Holds the plan and the buffers alive."""
+
+    def __init__(self, plan: Plan, handle: int, refs):
+        self.plan = plan
+        self._h = handle
+        self.refs = refs
+
+    def enqueue(self, stream=None) -> None:
+        sh, sobj = _stream_handle(stream)
+        _check(_load().tide_call_enqueue(self._h, sh), "tide_call_enqueue")
+        _record(self.refs, sobj)
+
+    def close(self):
+        if self._h:
+            _load().tide_call_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass
+
+
+def _prepared(plan: Plan, fn, name: str, args, refs) -> Call:
+    h = ctypes.c_void_p()
+    _check(fn(*args, ctypes.byref(h)), name)
+    return Call(plan, h.value, refs)
+
+
+def prepare_reduce_scatter_bf16_fp32(plan: Plan, grads, out, out_stride: Optional[int] = None,
+                                     launch: Optional[Launch] = None) -> Call:
+    """Prepared form of reduce_scatter_bf16_fp32 (tide_prepare_reduce_scatter_bf16_fp32)."""
+    tab = grads if isinstance(grads, PointerTable) else grads_table(plan, grads)
+    stride = plan.S if out_stride is None else int(out_stride)
+    return _prepared(plan, _load().tide_prepare_reduce_scatter_bf16_fp32,
+                     "tide_prepare_reduce_scatter_bf16_fp32",
+                     (plan.handle, tab.arr, _ptr(out), stride,
+                      ctypes.byref(launch) if launch is not None else None), tab.refs + [out])
+
+
+def prepare_allgather_place(plan: Plan, shards, params, shard_stride: Optional[int] = None,
+                            first_rank: int = 0, launch: Optional[Launch] = None) -> Call:
+    """Prepared form of allgather_place_stage (kernel engine)."""
+    tab = params if isinstance(params, PointerTable) else params_table(plan, params)
+    stride = plan.S if shard_stride is None else int(shard_stride)
+    return _prepared(plan, _load().tide_prepare_allgather_place_stage,
+                     "tide_prepare_allgather_place_stage",
+                     (plan.handle, _ptr(shards), stride, int(first_rank), tab.arr,
+                      ctypes.byref(launch) if launch is not None else None), tab.refs + [shards])
+
+
+def prepare_stage_grads_bf16(plan: Plan, grads, slots, launch: Optional[Launch] = None) -> Call:
+    """Prepared form of stage_grads_bf16 (kernel engine)."""
+    tab = grads if isinstance(grads, PointerTable) else grads_table(plan, grads)
+    if len(slots) != plan.L:
+        raise ValueError("need L=%d slots" % plan.L)
+    sa = (ctypes.c_void_p * plan.L)(*[_ptr(t) for t in slots])
+    return _prepared(plan, _load().tide_prepare_stage_grads_bf16, "tide_prepare_stage_grads_bf16",
+                     (plan.handle, tab.arr, sa, ctypes.byref(launch) if launch is not None else None),
+                     tab.refs + list(slots))
 
 
 def rd_schedule(M: int, node: int, piece_bytes: int = 0, head_bytes: int = 0):

@@ -481,8 +481,8 @@ tide_status refuse_capture(hipStream_t stream) {
     if (cs != hipStreamCaptureStatusNone)
         return fail(TIDE_ERR_UNSUPPORTED,
                     "the stream is capturing a graph; this call reads a per-call pointer table "
-                    "that a replay could not rely on (capture the runtime-copy engine or the "
-                    "landing sum instead)");
+                    "that a replay could not rely on (capture a prepared call, the runtime-copy "
+                    "engine or the landing sum instead)");
     return TIDE_OK;
 }
 
@@ -609,88 +609,359 @@ tide_status tide_plan_launch_count(const tide_plan* plan, int32_t op, const tide
     }
 }
 
+}  // extern "C"
+
+namespace {
+
+// A validated call that reads a per-call pointer table (reduce-scatter, and
+// placement and staging with the kernel engine): everything but the stream.
+struct Prepared {
+    int op = 0;                       // 0 reduce-scatter, 1 placement, 2 staging
+    tide_launch l{};
+    bool empty = false;               // nothing to launch
+    std::vector<char> table;          // the per-call pointer table (and flag words)
+    float* out = nullptr;             // op 0
+    int64_t out_stride = 0;
+    const uint16_t* shards = nullptr; // op 1
+    int64_t shard_stride = 0, shard_elems = 0;
+    int32_t first_rank = 0;
+    int64_t slot_elems = 0;           // op 2
+};
+
+tide_status prep_reduce(const tide_plan* plan, const uint16_t* const* grads, float* out,
+                        int64_t out_stride, const tide_launch* launch, Prepared* pr) {
+    if (!plan) return fail(TIDE_ERR_INVALID_ARG, "plan is NULL");
+    pr->op = 0;
+    tide_launch& l = pr->l;
+    tide_status st = resolve_launch(plan, launch, &l);
+    if (st != TIDE_OK) return st;
+    const int32_t P = plan->P, L = plan->L;
+    if (out_stride < plan->S)
+        return fail(TIDE_ERR_INVALID_ARG, "out_stride %lld < S %lld", (long long)out_stride,
+                    (long long)plan->S);
+    int64_t total;
+    if (!mul_ok(out_stride, plan->N, &total) || !mul_ok(total, 4, &total))
+        return fail(TIDE_ERR_OVERFLOW, "N * out_stride * 4 overflows int64");
+    st = check_counts(l, total / 4);
+    if (st != TIDE_OK) return st;
+    pr->out = out;
+    pr->out_stride = out_stride;
+    if (plan->S == 0 || l.rank_end == l.rank_begin) {
+        pr->empty = true;
+        return TIDE_OK;
+    }
+    if (!out) return fail(TIDE_ERR_INVALID_ARG, "out is NULL");
+    if (reinterpret_cast<uintptr_t>(out) & 3)
+        return fail(TIDE_ERR_ALIGNMENT, "out is not 4-byte aligned");
+    if (P > 0 && !grads) return fail(TIDE_ERR_INVALID_ARG, "grads is NULL");
+    // Per-call table: P*L pointers (parameter-major) then P flag words.
+    pr->table.assign((size_t)P * L * sizeof(void*) + (size_t)P * sizeof(uint32_t), 0);
+    const uint16_t** tp = reinterpret_cast<const uint16_t**>(pr->table.data());
+    uint32_t* fl = reinterpret_cast<uint32_t*>(pr->table.data() + (size_t)P * L * sizeof(void*));
+    const Range w{reinterpret_cast<uintptr_t>(out) + (uintptr_t)l.rank_begin * out_stride * 4,
+                  reinterpret_cast<uintptr_t>(out) + (uintptr_t)(l.rank_end - 1) * out_stride * 4 +
+                      (uintptr_t)plan->S * 4,
+                  -1};
+    for (int32_t p = 0; p < P; ++p) {
+        const ParamInfo& q = plan->prm[p];
+        uint32_t f = (l.flags & TIDE_FLAG_SCALAR_PATH) ? 0u : kFlagVector;
+        for (int32_t c = 0; c < L; ++c) {
+            const uint16_t* g = grads[(size_t)c * P + p];
+            tp[(size_t)p * L + c] = g;
+            if (q.valid == 0) continue;
+            if (!g) return fail(TIDE_ERR_INVALID_ARG, "grads[%d] (c=%d, p=%d) is NULL", c * P + p, c, p);
+            const uintptr_t a = reinterpret_cast<uintptr_t>(g);
+            if (a & 1) return fail(TIDE_ERR_ALIGNMENT, "grads[%d] is not 2-byte aligned", c * P + p);
+            if (a & 15) f &= ~kFlagVector;
+            const Range in{a, a + (uintptr_t)q.valid * 2, c * P + p};
+            if (overlaps(in, w))
+                return fail(TIDE_ERR_INVALID_ARG, "grads[%d] overlaps the output", c * P + p);
+        }
+        fl[p] = f;
+    }
+    return TIDE_OK;
+}
+
+tide_status prep_place(const tide_plan* plan, const uint16_t* shards, int64_t shard_stride,
+                       int32_t first_rank, uint16_t* const* params, int32_t engine,
+                       const tide_launch* launch, Prepared* pr) {
+    if (!plan) return fail(TIDE_ERR_INVALID_ARG, "plan is NULL");
+    pr->op = 1;
+    if (first_rank < 0 || first_rank >= plan->N)
+        return fail(TIDE_ERR_INVALID_ARG, "first_rank %d outside [0, %d)", first_rank, plan->N);
+    tide_launch& l = pr->l;
+    tide_status st = resolve_launch(plan, launch, &l);
+    if (st != TIDE_OK) return st;
+    if (engine != TIDE_ENGINE_KERNEL && engine != TIDE_ENGINE_RUNTIME &&
+        engine != TIDE_ENGINE_SDMA)
+        return fail(TIDE_ERR_INVALID_ARG, "engine %d is not KERNEL (0), RUNTIME (1) or SDMA (2)",
+                    engine);
+    if (engine == TIDE_ENGINE_SDMA)
+        return fail(TIDE_ERR_UNSUPPORTED,
+                    "the placement has no DMA-engine path (no compute-unit-free strided copy)");
+    if (l.write_counts && engine != TIDE_ENGINE_KERNEL)
+        return fail(TIDE_ERR_INVALID_ARG, "write counts need the kernel engine");
+    st = check_counts(l, (int64_t)plan->N * plan->S);
+    if (st != TIDE_OK) return st;
+    const int32_t P = plan->P;
+    if (shard_stride < plan->S)
+        return fail(TIDE_ERR_INVALID_ARG, "shard_stride %lld < S %lld",
+                    (long long)shard_stride, (long long)plan->S);
+    int64_t shard_elems;
+    if (!mul_ok(shard_stride, plan->N, &shard_elems) || !mul_ok(shard_elems, 2, &shard_elems))
+        return fail(TIDE_ERR_OVERFLOW, "N * shard_stride * 2 overflows int64");
+    pr->shards = shards;
+    pr->shard_stride = shard_stride;
+    pr->shard_elems = shard_elems / 2;
+    pr->first_rank = first_rank;
+    if (plan->S == 0 || l.rank_end == l.rank_begin) {
+        pr->empty = true;
+        return TIDE_OK;
+    }
+    if (!shards) return fail(TIDE_ERR_INVALID_ARG, "shards is NULL");
+    if (reinterpret_cast<uintptr_t>(shards) & 1)
+        return fail(TIDE_ERR_ALIGNMENT, "shards is not 2-byte aligned");
+    if (P > 0 && !params) return fail(TIDE_ERR_INVALID_ARG, "params is NULL");
+    pr->table.assign((size_t)P * sizeof(void*) + (size_t)P * sizeof(uint32_t), 0);
+    uint16_t** tp = reinterpret_cast<uint16_t**>(pr->table.data());
+    uint32_t* fl = reinterpret_cast<uint32_t*>(pr->table.data() + (size_t)P * sizeof(void*));
+    const uintptr_t sb = reinterpret_cast<uintptr_t>(shards);
+    // Shards read: ranks [rank_begin, rank_end) in place, or the whole
+    // stage buffer when it is rotated.
+    const Range rd = first_rank == 0
+        ? Range{sb + (uintptr_t)l.rank_begin * shard_stride * 2,
+                sb + (uintptr_t)(l.rank_end - 1) * shard_stride * 2 + (uintptr_t)plan->S * 2, -1}
+        : Range{sb, sb + (uintptr_t)(plan->N - 1) * shard_stride * 2 + (uintptr_t)plan->S * 2, -1};
+    std::vector<Range> wr;
+    for (int32_t p = 0; p < P; ++p) {
+        const ParamInfo& q = plan->prm[p];
+        uint16_t* d = params[p];
+        tp[p] = d;
+        fl[p] = (l.flags & TIDE_FLAG_SCALAR_PATH) ? 0u : kFlagVector;
+        if (q.valid == 0) continue;
+        if (!d) return fail(TIDE_ERR_INVALID_ARG, "params[%d] is NULL", p);
+        const uintptr_t a = reinterpret_cast<uintptr_t>(d);
+        if (a & 1) return fail(TIDE_ERR_ALIGNMENT, "params[%d] is not 2-byte aligned", p);
+        if (a & 15) fl[p] = 0;
+        const Range r{a, a + (uintptr_t)q.valid * 2, p};
+        if (overlaps(r, rd)) return fail(TIDE_ERR_INVALID_ARG, "params[%d] overlaps the shards", p);
+        wr.push_back(r);
+    }
+    std::sort(wr.begin(), wr.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+    for (size_t i = 1; i < wr.size(); ++i)
+        if (wr[i].lo < wr[i - 1].hi)
+            return fail(TIDE_ERR_INVALID_ARG, "params[%d] and params[%d] overlap", wr[i - 1].who,
+                        wr[i].who);
+    return TIDE_OK;
+}
+
+tide_status prep_stage(const tide_plan* plan, const uint16_t* const* grads, uint16_t* const* slots,
+                       int32_t engine, const tide_launch* launch, Prepared* pr) {
+    if (!plan) return fail(TIDE_ERR_INVALID_ARG, "plan is NULL");
+    pr->op = 2;
+    tide_launch& l = pr->l;
+    tide_status st = resolve_launch(plan, launch, &l);
+    if (st != TIDE_OK) return st;
+    if (engine != TIDE_ENGINE_KERNEL && engine != TIDE_ENGINE_RUNTIME &&
+        engine != TIDE_ENGINE_SDMA)
+        return fail(TIDE_ERR_INVALID_ARG, "engine %d is not KERNEL (0), RUNTIME (1) or SDMA (2)",
+                    engine);
+    const int32_t P = plan->P, L = plan->L;
+    const int64_t slot_elems = (int64_t)plan->N * plan->S;   // fits: checked at plan creation
+    pr->slot_elems = slot_elems;
+    if (l.write_counts && engine != TIDE_ENGINE_KERNEL)
+        return fail(TIDE_ERR_INVALID_ARG, "write counts need the kernel engine");
+    int64_t counts_need;
+    if (!mul_ok(slot_elems, L, &counts_need))
+        return fail(TIDE_ERR_OVERFLOW, "L * N * S overflows int64");
+    st = check_counts(l, counts_need);
+    if (st != TIDE_OK) return st;
+    if (plan->S == 0 || l.rank_end == l.rank_begin) {
+        pr->empty = true;
+        return TIDE_OK;
+    }
+    if (!slots) return fail(TIDE_ERR_INVALID_ARG, "slots is NULL");
+    if (P > 0 && !grads) return fail(TIDE_ERR_INVALID_ARG, "grads is NULL");
+    std::vector<Range> sr;
+    for (int32_t c = 0; c < L; ++c) {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(slots[c]);
+        if (!a) return fail(TIDE_ERR_INVALID_ARG, "slots[%d] is NULL", c);
+        if (a & 1) return fail(TIDE_ERR_ALIGNMENT, "slots[%d] is not 2-byte aligned", c);
+        sr.push_back(Range{a, a + (uintptr_t)slot_elems * 2, c});
+    }
+    {
+        std::vector<Range> sorted = sr;
+        std::sort(sorted.begin(), sorted.end(),
+                  [](const Range& a, const Range& b) { return a.lo < b.lo; });
+        for (size_t i = 1; i < sorted.size(); ++i)
+            if (sorted[i].lo < sorted[i - 1].hi)
+                return fail(TIDE_ERR_INVALID_ARG, "slots[%d] and slots[%d] overlap",
+                            sorted[i - 1].who, sorted[i].who);
+    }
+    // Per-call table: P*L sources, P*L destinations (both parameter-major,
+    // p * L + c), then P flag words.
+    const size_t np = (size_t)P * L;
+    pr->table.assign(2 * np * sizeof(void*) + (size_t)P * sizeof(uint32_t), 0);
+    const uint16_t** ts = reinterpret_cast<const uint16_t**>(pr->table.data());
+    uint16_t** td = reinterpret_cast<uint16_t**>(pr->table.data() + np * sizeof(void*));
+    uint32_t* fl = reinterpret_cast<uint32_t*>(pr->table.data() + 2 * np * sizeof(void*));
+    for (int32_t p = 0; p < P; ++p) {
+        const ParamInfo& q = plan->prm[p];
+        uint32_t f = (l.flags & TIDE_FLAG_SCALAR_PATH) ? 0u : kFlagVector;
+        for (int32_t c = 0; c < L; ++c) {
+            const uint16_t* g = grads[(size_t)c * P + p];
+            uint16_t* d = slots[c] + (int64_t)plan->N * q.o;
+            ts[(size_t)p * L + c] = g;
+            td[(size_t)p * L + c] = d;
+            if (q.valid == 0) continue;
+            if (!g) return fail(TIDE_ERR_INVALID_ARG, "grads[%d] (c=%d, p=%d) is NULL", c * P + p, c, p);
+            const uintptr_t a = reinterpret_cast<uintptr_t>(g);
+            if (a & 1) return fail(TIDE_ERR_ALIGNMENT, "grads[%d] is not 2-byte aligned", c * P + p);
+            if ((a | reinterpret_cast<uintptr_t>(d)) & 3) f = 0;
+            const Range in{a, a + (uintptr_t)q.valid * 2, c * P + p};
+            for (const Range& r : sr)
+                if (overlaps(in, r))
+                    return fail(TIDE_ERR_INVALID_ARG, "grads[%d] overlaps slots[%d]", c * P + p, r.who);
+        }
+        fl[p] = f;
+    }
+    return TIDE_OK;
+}
+
+// Device state and tile table of a prepared call on `dev`, with its trace and
+// LDS checks done. Caller holds plan->mu.
+tide_status device_side(const tide_plan* plan, const Prepared& pr, int dev, DevState** ds,
+                        TileTable** tt) {
+    const tide_launch& l = pr.l;
+    tide_status st = get_dev_state(plan, dev, ds);
+    if (st != TIDE_OK) return st;
+    st = get_tiles(plan, *ds, pr.op, l.rank_begin, l.rank_end, l.mode == TIDE_LAUNCH_BUDGETED, tt);
+    if (st != TIDE_OK) return st;
+    const int64_t items = pr.op == 2 ? (*tt)->count * plan->L : (*tt)->count;
+    st = check_trace(l, launch_records(plan, pr.op, l, items));
+    if (st != TIDE_OK) return st;
+    return prepare_budget(*ds, plan->L, l);
+}
+
+// Enqueue the kernels of a prepared call, its pointer table at `dtab`.
+tide_status launch_prepared(const tide_plan* plan, const Prepared& pr, const DevState* ds,
+                            const TileTable* tt, const char* dtab, hipStream_t stream) {
+    const tide_launch& l = pr.l;
+    const int32_t P = plan->P, L = plan->L;
+    if (tt->count == 0) return TIDE_OK;
+    if (pr.op == 0) {
+        const uint16_t* const* dptrs = reinterpret_cast<const uint16_t* const*>(dtab);
+        const uint32_t* dflags = reinterpret_cast<const uint32_t*>(dtab + (size_t)P * L * sizeof(void*));
+        return for_each_launch(plan, 0, l, tt->count,
+                               [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi,
+                                   int64_t tb) {
+            return launch_reduce(L, grid, threads, lds, stream, tt->dev, lo, hi, l.rank_begin,
+                                 l.rank_end, ds->params, dptrs, dflags, pr.out, pr.out_stride,
+                                 l.trace, tb, l.write_counts);
+        });
+    }
+    if (pr.op == 1) {
+        uint16_t* const* dptrs = reinterpret_cast<uint16_t* const*>(const_cast<char*>(dtab));
+        const uint32_t* dflags = reinterpret_cast<const uint32_t*>(dtab + (size_t)P * sizeof(void*));
+        return for_each_launch(plan, 1, l, tt->count,
+                               [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi,
+                                   int64_t tb) {
+            return launch_place(grid, threads, lds, stream, tt->dev, lo, hi, l.rank_begin,
+                                l.rank_end, ds->params, dptrs, dflags, pr.shards, pr.shard_stride,
+                                pr.shard_elems, pr.first_rank, plan->N, l.trace, tb,
+                                l.write_counts);
+        });
+    }
+    const size_t np = (size_t)P * L;
+    const uint16_t* const* dsrc = reinterpret_cast<const uint16_t* const*>(dtab);
+    uint16_t* const* ddst =
+        reinterpret_cast<uint16_t* const*>(const_cast<char*>(dtab) + np * sizeof(void*));
+    const uint32_t* dflags = reinterpret_cast<const uint32_t*>(dtab + 2 * np * sizeof(void*));
+    const int64_t ntiles = tt->count;
+    return for_each_launch(plan, 2, l, ntiles * L,
+                           [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi,
+                               int64_t tb) {
+        return launch_stage(grid, threads, lds, stream, tt->dev, ntiles, lo, hi, l.rank_begin,
+                            l.rank_end, ds->params, dsrc, ddst, dflags, L, l.trace, tb,
+                            l.write_counts, pr.slot_elems, plan->N);
+    });
+}
+
+// An eager call: its table goes through the plan's ring.
+tide_status run_eager(const tide_plan* plan, const Prepared& pr, hipStream_t stream) {
+    if (pr.empty) return TIDE_OK;
+    tide_status st = refuse_capture(stream);
+    if (st != TIDE_OK) return st;
+    std::lock_guard<std::mutex> lock(plan->mu);
+    int dev;
+    st = stream_device(stream, &dev);
+    if (st != TIDE_OK) return st;
+    DevState* ds;
+    TileTable* tt;
+    st = device_side(plan, pr, dev, &ds, &tt);
+    if (st != TIDE_OK) return st;
+    if (tt->count == 0) return TIDE_OK;
+    int slot;
+    st = stage_table(ds, pr.table.data(), pr.table.size(), stream, &slot);
+    if (st != TIDE_OK) return st;
+    st = launch_prepared(plan, pr, ds, tt, static_cast<const char*>(ds->slots[slot].dev), stream);
+    tide_status st2 = release_slot(ds, slot, stream);
+    return st != TIDE_OK ? st : st2;
+}
+
+}  // namespace
+
+// A prepared call: fixed buffers, its own device copy of the pointer table.
+struct tide_call {
+    const tide_plan* plan = nullptr;
+    Prepared pr;
+    int device = -1;
+    const DevState* ds = nullptr;
+    const TileTable* tt = nullptr;
+    void* dtab = nullptr;
+};
+
+namespace {
+
+tide_status make_call(const tide_plan* plan, Prepared&& pr, tide_call** out) {
+    std::unique_ptr<tide_call> call(new tide_call());
+    call->plan = plan;
+    call->pr = std::move(pr);
+    TIDE_HIP_TRY(hipGetDevice(&call->device));
+    if (!call->pr.empty) {
+        std::lock_guard<std::mutex> lock(plan->mu);
+        DevState* ds;
+        TileTable* tt;
+        tide_status st = device_side(plan, call->pr, call->device, &ds, &tt);
+        if (st != TIDE_OK) return st;
+        call->ds = ds;
+        call->tt = tt;
+        if (tt->count > 0) {
+            TIDE_HIP_TRY(hipMalloc(&call->dtab, call->pr.table.size()));
+            hipError_t e = hipMemcpy(call->dtab, call->pr.table.data(), call->pr.table.size(),
+                                     hipMemcpyHostToDevice);
+            if (e != hipSuccess) {
+                (void)hipFree(call->dtab);
+                return hip_fail(e, "hipMemcpy(call table)");
+            }
+        }
+    }
+    *out = call.release();
+    return TIDE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t* const* grads,
                                           float* out, int64_t out_stride, void* stream_v,
                                           const tide_launch* launch) {
     try {
-        if (!plan) return fail(TIDE_ERR_INVALID_ARG, "plan is NULL");
-        tide_launch l;
-        tide_status st = resolve_launch(plan, launch, &l);
+        Prepared pr;
+        tide_status st = prep_reduce(plan, grads, out, out_stride, launch, &pr);
         if (st != TIDE_OK) return st;
-        const int32_t P = plan->P, L = plan->L;
-        if (out_stride < plan->S)
-            return fail(TIDE_ERR_INVALID_ARG, "out_stride %lld < S %lld", (long long)out_stride,
-                        (long long)plan->S);
-        int64_t total;
-        if (!mul_ok(out_stride, plan->N, &total) || !mul_ok(total, 4, &total))
-            return fail(TIDE_ERR_OVERFLOW, "N * out_stride * 4 overflows int64");
-        st = check_counts(l, total / 4);
-        if (st != TIDE_OK) return st;
-        const bool work = plan->S > 0 && l.rank_end > l.rank_begin;
-        if (!work) return TIDE_OK;
-        if (!out) return fail(TIDE_ERR_INVALID_ARG, "out is NULL");
-        if (reinterpret_cast<uintptr_t>(out) & 3)
-            return fail(TIDE_ERR_ALIGNMENT, "out is not 4-byte aligned");
-        if (P > 0 && !grads) return fail(TIDE_ERR_INVALID_ARG, "grads is NULL");
-        // Per-call table: P*L pointers (parameter-major) then P flag words.
-        std::vector<char> table((size_t)P * L * sizeof(void*) + (size_t)P * sizeof(uint32_t));
-        const uint16_t** tp = reinterpret_cast<const uint16_t**>(table.data());
-        uint32_t* fl = reinterpret_cast<uint32_t*>(table.data() + (size_t)P * L * sizeof(void*));
-        const Range w{reinterpret_cast<uintptr_t>(out) + (uintptr_t)l.rank_begin * out_stride * 4,
-                      reinterpret_cast<uintptr_t>(out) + (uintptr_t)(l.rank_end - 1) * out_stride * 4 +
-                          (uintptr_t)plan->S * 4,
-                      -1};
-        for (int32_t p = 0; p < P; ++p) {
-            const ParamInfo& q = plan->prm[p];
-            uint32_t f = (l.flags & TIDE_FLAG_SCALAR_PATH) ? 0u : kFlagVector;
-            for (int32_t c = 0; c < L; ++c) {
-                const uint16_t* g = grads[(size_t)c * P + p];
-                tp[(size_t)p * L + c] = g;
-                if (q.valid == 0) continue;
-                if (!g) return fail(TIDE_ERR_INVALID_ARG, "grads[%d] (c=%d, p=%d) is NULL", c * P + p, c, p);
-                const uintptr_t a = reinterpret_cast<uintptr_t>(g);
-                if (a & 1) return fail(TIDE_ERR_ALIGNMENT, "grads[%d] is not 2-byte aligned", c * P + p);
-                if (a & 15) f &= ~kFlagVector;
-                const Range in{a, a + (uintptr_t)q.valid * 2, c * P + p};
-                if (overlaps(in, w))
-                    return fail(TIDE_ERR_INVALID_ARG, "grads[%d] overlaps the output", c * P + p);
-            }
-            fl[p] = f;
-        }
-        hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
-        st = refuse_capture(stream);
-        if (st != TIDE_OK) return st;
-        std::lock_guard<std::mutex> lock(plan->mu);
-        int dev;
-        st = stream_device(stream, &dev);
-        if (st != TIDE_OK) return st;
-        DevState* ds;
-        st = get_dev_state(plan, dev, &ds);
-        if (st != TIDE_OK) return st;
-        TileTable* tt;
-        st = get_tiles(plan, ds, 0, l.rank_begin, l.rank_end, l.mode == TIDE_LAUNCH_BUDGETED, &tt);
-        if (st != TIDE_OK) return st;
-        if (tt->count == 0) return TIDE_OK;
-        st = check_trace(l, launch_records(plan, 0, l, tt->count));
-        if (st != TIDE_OK) return st;
-        int slot;
-        st = stage_table(ds, table.data(), table.size(), stream, &slot);
-        if (st != TIDE_OK) return st;
-        const char* base = static_cast<const char*>(ds->slots[slot].dev);
-        const uint16_t* const* dptrs = reinterpret_cast<const uint16_t* const*>(base);
-        const uint32_t* dflags =
-            reinterpret_cast<const uint32_t*>(base + (size_t)P * L * sizeof(void*));
-        st = prepare_budget(ds, L, l);
-        if (st != TIDE_OK) return st;
-        st = for_each_launch(plan, 0, l, tt->count,
-                             [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi,
-                                 int64_t tb) {
-            return launch_reduce(L, grid, threads, lds, stream, tt->dev, lo, hi, l.rank_begin,
-                                 l.rank_end, ds->params, dptrs, dflags, out, out_stride, l.trace,
-                                 tb, l.write_counts);
-        });
-        tide_status st2 = release_slot(ds, slot, stream);
-        return st != TIDE_OK ? st : st2;
+        return run_eager(plan, pr, reinterpret_cast<hipStream_t>(stream_v));
     } catch (const std::bad_alloc&) {
         return fail(TIDE_ERR_NO_MEMORY, "host allocation failed");
     } catch (...) {
@@ -710,75 +981,20 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* sh
                                        uint16_t* const* params, void* stream_v, int32_t engine,
                                        const tide_launch* launch) {
     try {
-        if (!plan) return fail(TIDE_ERR_INVALID_ARG, "plan is NULL");
-        if (first_rank < 0 || first_rank >= plan->N)
-            return fail(TIDE_ERR_INVALID_ARG, "first_rank %d outside [0, %d)", first_rank, plan->N);
-        tide_launch l;
-        tide_status st = resolve_launch(plan, launch, &l);
-        if (st != TIDE_OK) return st;
-        if (engine != TIDE_ENGINE_KERNEL && engine != TIDE_ENGINE_RUNTIME &&
-            engine != TIDE_ENGINE_SDMA)
-            return fail(TIDE_ERR_INVALID_ARG, "engine %d is not KERNEL (0), RUNTIME (1) or SDMA (2)",
-                        engine);
-        if (engine == TIDE_ENGINE_SDMA)
-            return fail(TIDE_ERR_UNSUPPORTED,
-                        "the placement has no DMA-engine path (no compute-unit-free strided copy)");
-        if (l.write_counts && engine != TIDE_ENGINE_KERNEL)
-            return fail(TIDE_ERR_INVALID_ARG, "write counts need the kernel engine");
-        st = check_counts(l, (int64_t)plan->N * plan->S);
-        if (st != TIDE_OK) return st;
-        const int32_t P = plan->P;
-        if (shard_stride < plan->S)
-            return fail(TIDE_ERR_INVALID_ARG, "shard_stride %lld < S %lld",
-                        (long long)shard_stride, (long long)plan->S);
-        int64_t shard_elems;
-        if (!mul_ok(shard_stride, plan->N, &shard_elems) || !mul_ok(shard_elems, 2, &shard_elems))
-            return fail(TIDE_ERR_OVERFLOW, "N * shard_stride * 2 overflows int64");
-        shard_elems /= 2;
-        if (plan->S == 0 || l.rank_end == l.rank_begin) return TIDE_OK;
-        if (!shards) return fail(TIDE_ERR_INVALID_ARG, "shards is NULL");
-        if (reinterpret_cast<uintptr_t>(shards) & 1)
-            return fail(TIDE_ERR_ALIGNMENT, "shards is not 2-byte aligned");
-        if (P > 0 && !params) return fail(TIDE_ERR_INVALID_ARG, "params is NULL");
-        std::vector<char> table((size_t)P * sizeof(void*) + (size_t)P * sizeof(uint32_t));
-        uint16_t** tp = reinterpret_cast<uint16_t**>(table.data());
-        uint32_t* fl = reinterpret_cast<uint32_t*>(table.data() + (size_t)P * sizeof(void*));
-        const uintptr_t sb = reinterpret_cast<uintptr_t>(shards);
-        // Shards read: ranks [rank_begin, rank_end) in place, or the whole
-        // stage buffer when it is rotated.
-        const Range rd = first_rank == 0
-            ? Range{sb + (uintptr_t)l.rank_begin * shard_stride * 2,
-                    sb + (uintptr_t)(l.rank_end - 1) * shard_stride * 2 + (uintptr_t)plan->S * 2, -1}
-            : Range{sb, sb + (uintptr_t)(plan->N - 1) * shard_stride * 2 + (uintptr_t)plan->S * 2, -1};
-        std::vector<Range> wr;
-        for (int32_t p = 0; p < P; ++p) {
-            const ParamInfo& q = plan->prm[p];
-            uint16_t* d = params[p];
-            tp[p] = d;
-            fl[p] = (l.flags & TIDE_FLAG_SCALAR_PATH) ? 0u : kFlagVector;
-            if (q.valid == 0) continue;
-            if (!d) return fail(TIDE_ERR_INVALID_ARG, "params[%d] is NULL", p);
-            const uintptr_t a = reinterpret_cast<uintptr_t>(d);
-            if (a & 1) return fail(TIDE_ERR_ALIGNMENT, "params[%d] is not 2-byte aligned", p);
-            if (a & 15) fl[p] = 0;
-            const Range r{a, a + (uintptr_t)q.valid * 2, p};
-            if (overlaps(r, rd)) return fail(TIDE_ERR_INVALID_ARG, "params[%d] overlaps the shards", p);
-            wr.push_back(r);
-        }
-        std::sort(wr.begin(), wr.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
-        for (size_t i = 1; i < wr.size(); ++i)
-            if (wr[i].lo < wr[i - 1].hi)
-                return fail(TIDE_ERR_INVALID_ARG, "params[%d] and params[%d] overlap", wr[i - 1].who,
-                            wr[i].who);
+        Prepared pr;
+        tide_status st = prep_place(plan, shards, shard_stride, first_rank, params, engine, launch,
+                                    &pr);
+        if (st != TIDE_OK || pr.empty) return st;
         hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
         if (engine == TIDE_ENGINE_RUNTIME) {
             // One 2-D copy per parameter for its full pieces (rows of s_p
             // elements, source pitch = shard stride, destination contiguous),
             // split in two where a rotated stage wraps, plus one 1-D copy for
             // a partial last piece.
+            const tide_launch& l = pr.l;
             const int64_t N = plan->N;
             auto pos = [&](int64_t r) { return (r - first_rank + N) % N; };
-            for (int32_t p = 0; p < P; ++p) {
+            for (int32_t p = 0; p < plan->P; ++p) {
                 const ParamInfo& q = plan->prm[p];
                 if (q.valid == 0) continue;
                 const int64_t full = q.valid / q.s;                   // ranks with a whole piece
@@ -803,38 +1019,7 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* sh
             }
             return TIDE_OK;
         }
-        st = refuse_capture(stream);
-        if (st != TIDE_OK) return st;
-        std::lock_guard<std::mutex> lock(plan->mu);
-        int dev;
-        st = stream_device(stream, &dev);
-        if (st != TIDE_OK) return st;
-        DevState* ds;
-        st = get_dev_state(plan, dev, &ds);
-        if (st != TIDE_OK) return st;
-        TileTable* tt;
-        st = get_tiles(plan, ds, 1, l.rank_begin, l.rank_end, l.mode == TIDE_LAUNCH_BUDGETED, &tt);
-        if (st != TIDE_OK) return st;
-        if (tt->count == 0) return TIDE_OK;
-        st = check_trace(l, launch_records(plan, 1, l, tt->count));
-        if (st != TIDE_OK) return st;
-        int slot;
-        st = stage_table(ds, table.data(), table.size(), stream, &slot);
-        if (st != TIDE_OK) return st;
-        char* base = static_cast<char*>(ds->slots[slot].dev);
-        uint16_t* const* dptrs = reinterpret_cast<uint16_t* const*>(base);
-        const uint32_t* dflags = reinterpret_cast<const uint32_t*>(base + (size_t)P * sizeof(void*));
-        st = prepare_budget(ds, plan->L, l);
-        if (st != TIDE_OK) return st;
-        st = for_each_launch(plan, 1, l, tt->count,
-                             [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi,
-                                 int64_t tb) {
-            return launch_place(grid, threads, lds, stream, tt->dev, lo, hi, l.rank_begin,
-                                l.rank_end, ds->params, dptrs, dflags, shards, shard_stride,
-                                shard_elems, first_rank, plan->N, l.trace, tb, l.write_counts);
-        });
-        tide_status st2 = release_slot(ds, slot, stream);
-        return st != TIDE_OK ? st : st2;
+        return run_eager(plan, pr, stream);
     } catch (const std::bad_alloc&) {
         return fail(TIDE_ERR_NO_MEMORY, "host allocation failed");
     } catch (...) {
@@ -846,79 +1031,24 @@ tide_status tide_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* 
                                   uint16_t* const* slots, void* stream_v, int32_t engine,
                                   const tide_launch* launch) {
     try {
-        if (!plan) return fail(TIDE_ERR_INVALID_ARG, "plan is NULL");
-        tide_launch l;
-        tide_status st = resolve_launch(plan, launch, &l);
-        if (st != TIDE_OK) return st;
-        if (engine != TIDE_ENGINE_KERNEL && engine != TIDE_ENGINE_RUNTIME &&
-            engine != TIDE_ENGINE_SDMA)
-            return fail(TIDE_ERR_INVALID_ARG, "engine %d is not KERNEL (0), RUNTIME (1) or SDMA (2)",
-                        engine);
-        const int32_t P = plan->P, L = plan->L;
-        const int64_t slot_elems = (int64_t)plan->N * plan->S;   // fits: checked at plan creation
-        if (l.write_counts && engine != TIDE_ENGINE_KERNEL)
-            return fail(TIDE_ERR_INVALID_ARG, "write counts need the kernel engine");
-        int64_t counts_need;
-        if (!mul_ok(slot_elems, L, &counts_need))
-            return fail(TIDE_ERR_OVERFLOW, "L * N * S overflows int64");
-        st = check_counts(l, counts_need);
-        if (st != TIDE_OK) return st;
-        if (plan->S == 0 || l.rank_end == l.rank_begin) return TIDE_OK;
-        if (!slots) return fail(TIDE_ERR_INVALID_ARG, "slots is NULL");
-        if (P > 0 && !grads) return fail(TIDE_ERR_INVALID_ARG, "grads is NULL");
-        std::vector<Range> sr;
-        for (int32_t c = 0; c < L; ++c) {
-            const uintptr_t a = reinterpret_cast<uintptr_t>(slots[c]);
-            if (!a) return fail(TIDE_ERR_INVALID_ARG, "slots[%d] is NULL", c);
-            if (a & 1) return fail(TIDE_ERR_ALIGNMENT, "slots[%d] is not 2-byte aligned", c);
-            sr.push_back(Range{a, a + (uintptr_t)slot_elems * 2, c});
-        }
-        {
-            std::vector<Range> sorted = sr;
-            std::sort(sorted.begin(), sorted.end(),
-                      [](const Range& a, const Range& b) { return a.lo < b.lo; });
-            for (size_t i = 1; i < sorted.size(); ++i)
-                if (sorted[i].lo < sorted[i - 1].hi)
-                    return fail(TIDE_ERR_INVALID_ARG, "slots[%d] and slots[%d] overlap",
-                                sorted[i - 1].who, sorted[i].who);
-        }
-        // Per-call table: P*L sources, P*L destinations (both parameter-major,
-        // p * L + c), then P flag words.
-        const size_t np = (size_t)P * L;
-        std::vector<char> table(2 * np * sizeof(void*) + (size_t)P * sizeof(uint32_t));
-        const uint16_t** ts = reinterpret_cast<const uint16_t**>(table.data());
-        uint16_t** td = reinterpret_cast<uint16_t**>(table.data() + np * sizeof(void*));
-        uint32_t* fl = reinterpret_cast<uint32_t*>(table.data() + 2 * np * sizeof(void*));
-        for (int32_t p = 0; p < P; ++p) {
-            const ParamInfo& q = plan->prm[p];
-            uint32_t f = (l.flags & TIDE_FLAG_SCALAR_PATH) ? 0u : kFlagVector;
-            for (int32_t c = 0; c < L; ++c) {
-                const uint16_t* g = grads[(size_t)c * P + p];
-                uint16_t* d = slots[c] + (int64_t)plan->N * q.o;
-                ts[(size_t)p * L + c] = g;
-                td[(size_t)p * L + c] = d;
-                if (q.valid == 0) continue;
-                if (!g) return fail(TIDE_ERR_INVALID_ARG, "grads[%d] (c=%d, p=%d) is NULL", c * P + p, c, p);
-                const uintptr_t a = reinterpret_cast<uintptr_t>(g);
-                if (a & 1) return fail(TIDE_ERR_ALIGNMENT, "grads[%d] is not 2-byte aligned", c * P + p);
-                if ((a | reinterpret_cast<uintptr_t>(d)) & 3) f = 0;
-                const Range in{a, a + (uintptr_t)q.valid * 2, c * P + p};
-                for (const Range& r : sr)
-                    if (overlaps(in, r))
-                        return fail(TIDE_ERR_INVALID_ARG, "grads[%d] overlaps slots[%d]", c * P + p, r.who);
-            }
-            fl[p] = f;
-        }
+        Prepared pr;
+        tide_status st = prep_stage(plan, grads, slots, engine, launch, &pr);
+        if (st != TIDE_OK || pr.empty) return st;
         hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
         if (engine != TIDE_ENGINE_KERNEL) {
             // One contiguous copy per (contributor, parameter): the rows of
             // ranks [rank_begin, rank_end) are one run on both sides.
             const hipMemcpyKind kind = engine == TIDE_ENGINE_SDMA ? hipMemcpyDeviceToDeviceNoCU
                                                                    : hipMemcpyDeviceToDevice;
+            const int32_t P = plan->P, L = plan->L;
+            const size_t np = (size_t)P * L;
+            const uint16_t* const* ts = reinterpret_cast<const uint16_t* const*>(pr.table.data());
+            uint16_t* const* td =
+                reinterpret_cast<uint16_t* const*>(pr.table.data() + np * sizeof(void*));
             for (int32_t p = 0; p < P; ++p) {
                 const ParamInfo& q = plan->prm[p];
-                const int64_t lo = (int64_t)l.rank_begin * q.s;
-                const int64_t hi = std::min((int64_t)l.rank_end * q.s, q.valid);
+                const int64_t lo = (int64_t)pr.l.rank_begin * q.s;
+                const int64_t hi = std::min((int64_t)pr.l.rank_end * q.s, q.valid);
                 if (hi <= lo) continue;
                 for (int32_t c = 0; c < L; ++c)
                     TIDE_HIP_TRY(hipMemcpyAsync(td[(size_t)p * L + c] + lo, ts[(size_t)p * L + c] + lo,
@@ -926,45 +1056,92 @@ tide_status tide_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* 
             }
             return TIDE_OK;
         }
-        st = refuse_capture(stream);
-        if (st != TIDE_OK) return st;
-        std::lock_guard<std::mutex> lock(plan->mu);
-        int dev;
-        st = stream_device(stream, &dev);
-        if (st != TIDE_OK) return st;
-        DevState* ds;
-        st = get_dev_state(plan, dev, &ds);
-        if (st != TIDE_OK) return st;
-        TileTable* tt;
-        st = get_tiles(plan, ds, 2, l.rank_begin, l.rank_end, l.mode == TIDE_LAUNCH_BUDGETED, &tt);
-        if (st != TIDE_OK) return st;
-        if (tt->count == 0) return TIDE_OK;
-        st = check_trace(l, launch_records(plan, 2, l, tt->count * L));
-        if (st != TIDE_OK) return st;
-        int slot;
-        st = stage_table(ds, table.data(), table.size(), stream, &slot);
-        if (st != TIDE_OK) return st;
-        char* base = static_cast<char*>(ds->slots[slot].dev);
-        const uint16_t* const* dsrc = reinterpret_cast<const uint16_t* const*>(base);
-        uint16_t* const* ddst = reinterpret_cast<uint16_t* const*>(base + np * sizeof(void*));
-        const uint32_t* dflags = reinterpret_cast<const uint32_t*>(base + 2 * np * sizeof(void*));
-        st = prepare_budget(ds, L, l);
-        if (st != TIDE_OK) return st;
-        const int64_t ntiles = tt->count;
-        st = for_each_launch(plan, 2, l, ntiles * L,
-                             [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi,
-                                 int64_t tb) {
-            return launch_stage(grid, threads, lds, stream, tt->dev, ntiles, lo, hi, l.rank_begin,
-                                l.rank_end, ds->params, dsrc, ddst, dflags, L, l.trace, tb,
-                                l.write_counts, slot_elems, plan->N);
-        });
-        tide_status st2 = release_slot(ds, slot, stream);
-        return st != TIDE_OK ? st : st2;
+        return run_eager(plan, pr, stream);
     } catch (const std::bad_alloc&) {
         return fail(TIDE_ERR_NO_MEMORY, "host allocation failed");
     } catch (...) {
         return fail(TIDE_ERR_INVALID_ARG, "unexpected exception");
     }
+}
+
+tide_status tide_prepare_reduce_scatter_bf16_fp32(const tide_plan* plan,
+                                                  const uint16_t* const* grads, float* out,
+                                                  int64_t out_stride, const tide_launch* launch,
+                                                  tide_call** call) {
+    try {
+        if (!call) return fail(TIDE_ERR_INVALID_ARG, "call is NULL");
+        *call = nullptr;
+        Prepared pr;
+        tide_status st = prep_reduce(plan, grads, out, out_stride, launch, &pr);
+        if (st != TIDE_OK) return st;
+        return make_call(plan, std::move(pr), call);
+    } catch (const std::bad_alloc&) {
+        return fail(TIDE_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return fail(TIDE_ERR_INVALID_ARG, "unexpected exception");
+    }
+}
+
+tide_status tide_prepare_allgather_place_stage(const tide_plan* plan, const uint16_t* shards,
+                                               int64_t shard_stride, int32_t first_rank,
+                                               uint16_t* const* params, const tide_launch* launch,
+                                               tide_call** call) {
+    try {
+        if (!call) return fail(TIDE_ERR_INVALID_ARG, "call is NULL");
+        *call = nullptr;
+        Prepared pr;
+        tide_status st = prep_place(plan, shards, shard_stride, first_rank, params,
+                                    TIDE_ENGINE_KERNEL, launch, &pr);
+        if (st != TIDE_OK) return st;
+        return make_call(plan, std::move(pr), call);
+    } catch (const std::bad_alloc&) {
+        return fail(TIDE_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return fail(TIDE_ERR_INVALID_ARG, "unexpected exception");
+    }
+}
+
+tide_status tide_prepare_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* grads,
+                                          uint16_t* const* slots, const tide_launch* launch,
+                                          tide_call** call) {
+    try {
+        if (!call) return fail(TIDE_ERR_INVALID_ARG, "call is NULL");
+        *call = nullptr;
+        Prepared pr;
+        tide_status st = prep_stage(plan, grads, slots, TIDE_ENGINE_KERNEL, launch, &pr);
+        if (st != TIDE_OK) return st;
+        return make_call(plan, std::move(pr), call);
+    } catch (const std::bad_alloc&) {
+        return fail(TIDE_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return fail(TIDE_ERR_INVALID_ARG, "unexpected exception");
+    }
+}
+
+tide_status tide_call_enqueue(const tide_call* call, void* stream_v) {
+    if (!call) return fail(TIDE_ERR_INVALID_ARG, "call is NULL");
+    if (call->pr.empty || !call->tt || call->tt->count == 0) return TIDE_OK;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+    int dev;
+    tide_status st = stream_device(stream, &dev);
+    if (st != TIDE_OK) return st;
+    if (dev != call->device)
+        return fail(TIDE_ERR_INVALID_ARG, "stream is on device %d, the call was prepared on %d", dev,
+                    call->device);
+    return launch_prepared(call->plan, call->pr, call->ds, call->tt,
+                           static_cast<const char*>(call->dtab), stream);
+}
+
+void tide_call_destroy(tide_call* call) {
+    if (!call) return;
+    if (call->dtab) {
+        int prev = -1;
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        (void)hipSetDevice(call->device);
+        (void)hipFree(call->dtab);
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+    delete call;
 }
 
 tide_status tide_latin_square(int32_t M, int32_t L, int32_t dst_node, int32_t src_node, int32_t* c,

@@ -238,3 +238,29 @@ def test_diag_occupy_validates(tide):
     assert _status(lambda: occ(4, 256, 200 * 1024, 10, FAKE, stream=0)) == "TIDE_ERR_INVALID_ARG"
     assert _status(lambda: occ(4, 256, 0, 10 ** 9, FAKE, stream=0)) == "TIDE_ERR_INVALID_ARG"
     assert _status(lambda: occ(4, 256, 0, 10, 0, stream=0)) == "TIDE_ERR_INVALID_ARG"
+
+
+def test_prepared_calls_validate_before_allocating(tide):
+    shapes = [(8, 4), (4, 4), (12, 4)]
+    plan = tide.plan_create(shapes, 4, 2)
+    S = plan.S
+    grads = [[FAKE + 0x100000 * (c * 3 + p) for p in range(3)] for c in range(2)]
+    out = FAKE + 0x10000000
+    pr = tide.prepare_reduce_scatter_bf16_fp32
+    assert _status(lambda: pr(plan, grads, out, out_stride=S - 1)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: pr(plan, grads, out + 2)) == "TIDE_ERR_ALIGNMENT"
+    bad = [list(g) for g in grads]
+    bad[0][0] = out + 4
+    assert _status(lambda: pr(plan, bad, out)) == "TIDE_ERR_INVALID_ARG"
+    shards = FAKE + 0x20000000
+    params = [FAKE + 0x30000000 + 0x100000 * p for p in range(3)]
+    pa = tide.prepare_allgather_place
+    assert _status(lambda: pa(plan, shards, params, first_rank=4)) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: pa(plan, shards + 1, params)) == "TIDE_ERR_ALIGNMENT"
+    slots = [FAKE + 0x40000000, FAKE + 0x40000000 + 2 * 4 * S]
+    ps = tide.prepare_stage_grads_bf16
+    assert _status(lambda: ps(plan, grads, [slots[0], slots[0]])) == "TIDE_ERR_INVALID_ARG"
+    # A NULL call handle is refused by every call entry point.
+    lib = tide.lib()
+    assert lib.tide_call_enqueue(None, None) == 1
+    lib.tide_call_destroy(None)
