@@ -12,7 +12,7 @@ value = algorithmic bytes per step / time per step:
 Prints ONE JSON line on stdout; progress goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--parts] [--victim] [--stock] [--slot-reuse] [--occupancy]
+                  [--parts] [--victim] [--stock] [--slot-reuse] [--occupancy] [--graph]
                   [--no-cpu-baseline]
 """
 import argparse
@@ -330,6 +330,57 @@ def occupancy_probe(torch, tide, plan, grads, out, shards, params, gs, cs, probe
     return res
 
 
+def graph_parts(torch, tide, plan, g_tab, out, shards, p_tab, rs_bytes, ag_bytes, iters=10):
+    """The step (reduce-scatter + placement) as prepared calls: enqueued eagerly,
+    and captured once into a HIP graph and replayed; full grid and budgeted.
+    Host time per step (enqueue only) and GPU time per step."""
+    res = {}
+    for name, launch in (("full_grid", tide.Launch()), ("budgeted_16_4", tide.budgeted())):
+        rs = tide.prepare_reduce_scatter_bf16_fp32(plan, g_tab, out, launch=launch)
+        ag = tide.prepare_allgather_place(plan, shards, p_tab, launch=launch)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            rs.enqueue()
+            ag.enqueue()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        h0 = time.perf_counter()
+        e0.record()
+        for _ in range(iters):
+            rs.enqueue()
+            ag.enqueue()
+        e1.record()
+        h_eager = (time.perf_counter() - h0) / iters
+        torch.cuda.synchronize()
+        t_eager = e0.elapsed_time(e1) / iters
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            rs.enqueue()
+            ag.enqueue()
+        g.replay()
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        e0.record()
+        for _ in range(iters):
+            g.replay()
+        e1.record()
+        h_graph = (time.perf_counter() - h0) / iters
+        torch.cuda.synchronize()
+        t_graph = e0.elapsed_time(e1) / iters
+        res[name] = {"launches_per_step": plan.launch_count(0, launch) + plan.launch_count(1, launch),
+                     "prepared_eager_ms": round(t_eager, 4),
+                     "prepared_eager_host_ms": round(h_eager * 1e3, 4),
+                     "graph_replay_ms": round(t_graph, 4),
+                     "graph_replay_host_ms": round(h_graph * 1e3, 4),
+                     "graph_GBps": round((rs_bytes + ag_bytes) / (t_graph / 1e3) / 1e9, 1)}
+        del g
+        rs.close()
+        ag.close()
+    return res
+
+
 def stock_fsdp2(torch, tide, plan, cfg, grads, shards, out, p_tab, iters=3):
     """The stock FSDP2 path on one GPU, for comparison: every contributor's
     gradients packed with torch._chunk_cat into an fp32 rank-major buffer (the
@@ -455,6 +506,8 @@ def main():
                     help="also time the Slot-Reuse staging and the reduce reading the slots")
     ap.add_argument("--occupancy", action="store_true",
                     help="trace where budgeted workgroups run, beside GEMM-shaped occupants")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step as prepared calls, eager and replayed from a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-ranks", type=int, default=0, help="ranks in the CPU sample (0: all)")
     args = ap.parse_args()
@@ -586,6 +639,12 @@ def main():
     gs = cs = None
     if args.occupancy or args.victim:
         gs, cs = torch.cuda.Stream(), torch.cuda.Stream()
+    graph = None
+    if args.graph:
+        log("bench: prepared calls and graph replay")
+        graph = graph_parts(torch, tide, plan, g_tab, out, shards, p_tab, rs_bytes, ag_bytes)
+        log("bench: graph %s" % json.dumps(graph))
+
     occ = None
     if args.occupancy:
         log("bench: occupancy probe")
@@ -662,6 +721,8 @@ def main():
         line["slot_reuse"] = slot
     if occ is not None:
         line["occupancy_probe"] = occ
+    if graph is not None:
+        line["prepared_and_graph"] = graph
     print(json.dumps(line), flush=True)
 
 
