@@ -264,3 +264,28 @@ def test_prepared_calls_validate_before_allocating(tide):
     lib = tide.lib()
     assert lib.tide_call_enqueue(None, None) == 1
     lib.tide_call_destroy(None)
+
+
+def test_struct_layouts_match_the_header(tide, tmp_path):
+    """The ctypes mirrors of tide_launch, tide_rd_step and tide_trace_rec have
+    the C header's sizes and field offsets (compiled with the host C compiler)."""
+    import subprocess
+    specs = {"tide_launch": tide.Launch, "tide_rd_step": tide._lib.RdStep}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "tide.h"', 'int main(void) {']
+    for cname, cls in specs.items():
+        lines.append('printf("%s size %%zu\\n", sizeof(%s));' % (cname, cname))
+        for f, _ in cls._fields_:
+            lines.append('printf("%s.%s %%zu\\n", offsetof(%s, %s));' % (cname, f, cname, f))
+    lines.append('printf("tide_trace_rec size %zu\\n", sizeof(tide_trace_rec));')
+    lines.append('return 0; }')
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.check_call(["gcc", "-std=c11", "-Wall", "-Werror", "-I", inc, str(src), "-o", str(exe)])
+    got = dict(line.rsplit(" ", 1) for line in subprocess.check_output([str(exe)]).decode().splitlines())
+    for cname, cls in specs.items():
+        assert int(got["%s size" % cname]) == ctypes.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert int(got["%s.%s" % (cname, f)]) == getattr(cls, f).offset, (cname, f)
+    assert int(got["tide_trace_rec size"]) == tide._lib.TRACE_REC_BYTES
