@@ -77,8 +77,12 @@ def traced(launch: Launch, buf, records: Optional[int] = None) -> Launch:
     """Copy of `launch` that writes its workgroup records into `buf`."""
     out = Launch()
     ctypes.pointer(out)[0] = launch
+    cap = buf.numel() // 3
+    if records is not None and int(records) > cap:
+        raise ValueError("trace buffer holds %d records, %d requested" % (cap, int(records)))
+    _tensor_arg(buf, "int64", "trace buffer")
     out.trace = _ptr(buf)
-    out.trace_capacity = buf.numel() // 3 if records is None else int(records)
+    out.trace_capacity = cap if records is None else int(records)
     return out
 
 
@@ -87,6 +91,7 @@ def counted(launch: Launch, counts) -> Launch:
     zeroed int32 device tensor; see tide_launch.write_counts for the indices)."""
     out = Launch()
     ctypes.pointer(out)[0] = launch
+    _tensor_arg(counts, "int32", "write counts")
     out.write_counts = _ptr(counts)
     out.write_counts_elems = counts.numel()
     return out
@@ -212,6 +217,33 @@ def _ptr(x) -> int:
     return int(x.data_ptr())
 
 
+def _tensor_arg(t, dtype_name: str, what: str, numel: Optional[int] = None,
+                min_numel: Optional[int] = None) -> None:
+    """Check a tensor argument before its address goes to the library, which
+    sees only pointers: dtype, contiguity, size, and that it is on the GPU.
+    Raw integer addresses are the caller's responsibility and pass unchecked."""
+    if t is None or isinstance(t, int):
+        return
+    import torch
+    dtype = getattr(torch, dtype_name)
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (what, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s is not contiguous" % what)
+    n = t.numel()
+    if numel is not None and n != numel:
+        raise ValueError("%s holds %d elements, expected %d" % (what, n, numel))
+    if min_numel is not None and n < min_numel:
+        raise ValueError("%s holds %d elements, at least %d needed" % (what, n, min_numel))
+    if not t.is_cuda:
+        raise ValueError("%s is not a GPU tensor" % what)
+
+
+def _shards_elems(plan: "Plan", stride: int) -> int:
+    """Elements N shards of S, `stride` apart, span."""
+    return 0 if plan.S == 0 else (plan.N - 1) * stride + plan.S
+
+
 def _stream_handle(stream) -> Tuple[int, object]:
     import torch
     if stream is None:
@@ -311,12 +343,17 @@ def grads_table(plan: Plan, grads: Sequence[Sequence[object]]) -> PointerTable:
     """grads[c][p] -> the L*P table tide_reduce_scatter_bf16_fp32 reads (c-major)."""
     if len(grads) != plan.L or any(len(g) != plan.P for g in grads):
         raise ValueError("grads must be L=%d lists of P=%d tensors" % (plan.L, plan.P))
+    for c in range(plan.L):
+        for p, (t, k) in enumerate(plan.shapes):
+            _tensor_arg(grads[c][p], "bfloat16", "grads[%d][%d]" % (c, p), numel=t * k)
     return PointerTable([grads[c][p] for c in range(plan.L) for p in range(plan.P)])
 
 
 def params_table(plan: Plan, params: Sequence[object]) -> PointerTable:
     if len(params) != plan.P:
         raise ValueError("params must hold P=%d tensors" % plan.P)
+    for p, (t, k) in enumerate(plan.shapes):
+        _tensor_arg(params[p], "bfloat16", "params[%d]" % p, numel=t * k)
     return PointerTable(params)
 
 
@@ -331,8 +368,9 @@ def _record(tensors, stream_obj):
         return
     if stream_obj == torch.cuda.default_stream(stream_obj.device):
         return
-    if torch.cuda.is_current_stream_capturing():
-        return                      # a captured graph keeps its own references
+    with torch.cuda.stream(stream_obj):
+        if torch.cuda.is_current_stream_capturing():
+            return                  # a captured graph keeps its own references
     for t in tensors:
         if t is not None and not isinstance(t, int):
             t.record_stream(stream_obj)
@@ -349,6 +387,7 @@ def reduce_scatter_bf16_fp32(plan: Plan, grads: Sequence[Sequence[object]], out,
         raise ValueError("pointer table holds %d entries, expected L*P=%d" % (tab.n, plan.L * plan.P))
     flat, arr = tab.refs, tab.arr
     stride = plan.S if out_stride is None else int(out_stride)
+    _tensor_arg(out, "float32", "out", min_numel=_shards_elems(plan, stride))
     sh, sobj = _stream_handle(stream)
     st = _load().tide_reduce_scatter_bf16_fp32(
         plan.handle, arr, _ptr(out), stride, sh,
@@ -371,6 +410,7 @@ def allgather_place(plan: Plan, shards, params: Sequence[object],
         engine = ENGINES[engine]
     arr = tab.arr
     stride = plan.S if shard_stride is None else int(shard_stride)
+    _tensor_arg(shards, "bfloat16", "shards", min_numel=_shards_elems(plan, stride))
     sh, sobj = _stream_handle(stream)
     st = _load().tide_allgather_place(plan.handle, _ptr(shards), stride, arr, sh, int(engine),
                                       ctypes.byref(launch) if launch is not None else None)
@@ -390,6 +430,7 @@ def allgather_place_stage(plan: Plan, stage, first_rank: int, params: Sequence[o
     if isinstance(engine, str):
         engine = ENGINES[engine]
     stride = plan.S if shard_stride is None else int(shard_stride)
+    _tensor_arg(stage, "bfloat16", "stage", min_numel=_shards_elems(plan, stride))
     sh, sobj = _stream_handle(stream)
     st = _load().tide_allgather_place_stage(plan.handle, _ptr(stage), stride, int(first_rank),
                                             tab.arr, sh, int(engine),
@@ -407,8 +448,7 @@ def stage_grads_bf16(plan: Plan, grads: Sequence[Sequence[object]], slots: Seque
     tab = grads if isinstance(grads, PointerTable) else grads_table(plan, grads)
     if tab.n != plan.L * plan.P:
         raise ValueError("pointer table holds %d entries, expected L*P=%d" % (tab.n, plan.L * plan.P))
-    if len(slots) != plan.L:
-        raise ValueError("need L=%d slots" % plan.L)
+    _slots_arg(plan, slots)
     if isinstance(engine, str):
         engine = ENGINES[engine]
     sa = (ctypes.c_void_p * plan.L)(*[_ptr(t) for t in slots])
@@ -419,11 +459,17 @@ def stage_grads_bf16(plan: Plan, grads: Sequence[Sequence[object]], slots: Seque
     _record(tab.refs + list(slots), sobj)
 
 
+def _slots_arg(plan: Plan, slots: Sequence[object]) -> None:
+    if len(slots) != plan.L:
+        raise ValueError("need L=%d slots" % plan.L)
+    for c, t in enumerate(slots):
+        _tensor_arg(t, "bfloat16", "slots[%d]" % c, min_numel=plan.N * plan.S)
+
+
 def slot_grads_table(plan: Plan, slots: Sequence[object]) -> PointerTable:
     """The reduce's L*P gradient table reading the staged slots: entry c*P + p
     is slots[c] + N * o_p (addresses; keeps the slot tensors alive)."""
-    if len(slots) != plan.L:
-        raise ValueError("need L=%d slots" % plan.L)
+    _slots_arg(plan, slots)
     offs = [plan.N * plan.param(p)[4] * 2 for p in range(plan.P)]
     tab = PointerTable([_ptr(slots[c]) + offs[p] for c in range(plan.L) for p in range(plan.P)])
     tab.refs = list(slots)
@@ -468,6 +514,7 @@ def prepare_reduce_scatter_bf16_fp32(plan: Plan, grads, out, out_stride: Optiona
     """Prepared form of reduce_scatter_bf16_fp32 (tide_prepare_reduce_scatter_bf16_fp32)."""
     tab = grads if isinstance(grads, PointerTable) else grads_table(plan, grads)
     stride = plan.S if out_stride is None else int(out_stride)
+    _tensor_arg(out, "float32", "out", min_numel=_shards_elems(plan, stride))
     return _prepared(plan, _load().tide_prepare_reduce_scatter_bf16_fp32,
                      "tide_prepare_reduce_scatter_bf16_fp32",
                      (plan.handle, tab.arr, _ptr(out), stride,
@@ -479,6 +526,7 @@ def prepare_allgather_place(plan: Plan, shards, params, shard_stride: Optional[i
     """Prepared form of allgather_place_stage (kernel engine)."""
     tab = params if isinstance(params, PointerTable) else params_table(plan, params)
     stride = plan.S if shard_stride is None else int(shard_stride)
+    _tensor_arg(shards, "bfloat16", "shards", min_numel=_shards_elems(plan, stride))
     return _prepared(plan, _load().tide_prepare_allgather_place_stage,
                      "tide_prepare_allgather_place_stage",
                      (plan.handle, _ptr(shards), stride, int(first_rank), tab.arr,
@@ -488,8 +536,7 @@ def prepare_allgather_place(plan: Plan, shards, params, shard_stride: Optional[i
 def prepare_stage_grads_bf16(plan: Plan, grads, slots, launch: Optional[Launch] = None) -> Call:
     """Prepared form of stage_grads_bf16 (kernel engine)."""
     tab = grads if isinstance(grads, PointerTable) else grads_table(plan, grads)
-    if len(slots) != plan.L:
-        raise ValueError("need L=%d slots" % plan.L)
+    _slots_arg(plan, slots)
     sa = (ctypes.c_void_p * plan.L)(*[_ptr(t) for t in slots])
     return _prepared(plan, _load().tide_prepare_stage_grads_bf16, "tide_prepare_stage_grads_bf16",
                      (plan.handle, tab.arr, sa, ctypes.byref(launch) if launch is not None else None),
@@ -513,6 +560,10 @@ def landing_sum_fp32(L: int, M: int, S: int, inboxes: Sequence[object], shards: 
     inboxes[g]: fp32 device tensors of L*L*ceil(S/L); shards[b]: fp32 of S."""
     if len(inboxes) != L or len(shards) != L:
         raise ValueError("need L=%d inboxes and L shards" % L)
+    C = -(-int(S) // L) if L > 0 else 0
+    for g in range(L):
+        _tensor_arg(inboxes[g], "float32", "inboxes[%d]" % g, min_numel=L * L * C)
+        _tensor_arg(shards[g], "float32", "shards[%d]" % g, min_numel=int(S))
     ia = (ctypes.c_void_p * L)(*[_ptr(t) for t in inboxes])
     sa = (ctypes.c_void_p * L)(*[_ptr(t) for t in shards])
     sh, sobj = _stream_handle(stream)
@@ -534,6 +585,7 @@ def landing_trace_records(L: int, M: int, S: int, accumulate: bool = False,
 def diag_occupy(workgroups: int, threads: int, lds_bytes: int, spin_ticks: int, trace,
                 stream=None) -> None:
     """tide_diag_occupy: a GEMM-shaped occupant that records where it ran."""
+    _tensor_arg(trace, "int64", "trace", min_numel=3 * max(int(workgroups), 0))
     sh, sobj = _stream_handle(stream)
     _check(_load().tide_diag_occupy(workgroups, threads, lds_bytes, spin_ticks, _ptr(trace), sh),
            "tide_diag_occupy")

@@ -43,6 +43,31 @@ tide_status hip_fail(hipError_t e, const char* what) {
         if (e_ != hipSuccess) return hip_fail(e_, #expr);       \
     } while (0)
 
+// Makes `dev` the current device for the guard's lifetime. Allocations,
+// events and kernel attributes belong to the current device, and a caller's
+// stream may sit on another one.
+class DeviceGuard {
+  public:
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev_) != hipSuccess) prev_ = -1;
+        if (prev_ != dev) {
+            status_ = hipSetDevice(dev);
+            changed_ = status_ == hipSuccess && prev_ >= 0;
+        }
+    }
+    ~DeviceGuard() {
+        if (changed_) (void)hipSetDevice(prev_);
+    }
+    DeviceGuard(const DeviceGuard&) = delete;
+    DeviceGuard& operator=(const DeviceGuard&) = delete;
+    hipError_t status() const { return status_; }
+
+  private:
+    int prev_ = -1;
+    bool changed_ = false;
+    hipError_t status_ = hipSuccess;
+};
+
 // Defaults of the CU-budgeted mode: 16 summing + 4 landing blocks living
 // 0.2-0.4 ms each (page 1 "Why does a communication kernel slow a matrix
 // multiply by 69%?"; page 3 Table 4 "TIDE, training 16+4").
@@ -121,9 +146,7 @@ struct DevState {
     bool lds_allowed[65] = {};             // allow_dynamic_lds done for this L
 
     ~DevState() {
-        int prev = -1;
-        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
-        (void)hipSetDevice(device);
+        DeviceGuard guard(device);
         for (auto& kv : tiles) (void)hipFree(kv.second.dev);
         (void)hipFree(params);
         (void)hipFree(ring_dev);
@@ -136,7 +159,6 @@ struct DevState {
             if (s.upload_done) (void)hipEventDestroy(s.upload_done);
         }
         for (hipEvent_t e : event_pool) (void)hipEventDestroy(e);
-        if (prev >= 0) (void)hipSetDevice(prev);
     }
 };
 
@@ -896,6 +918,8 @@ tide_status run_eager(const tide_plan* plan, const Prepared& pr, hipStream_t str
     int dev;
     st = stream_device(stream, &dev);
     if (st != TIDE_OK) return st;
+    DeviceGuard guard(dev);
+    if (guard.status() != hipSuccess) return hip_fail(guard.status(), "hipSetDevice");
     DevState* ds;
     TileTable* tt;
     st = device_side(plan, pr, dev, &ds, &tt);
@@ -1135,11 +1159,8 @@ tide_status tide_call_enqueue(const tide_call* call, void* stream_v) {
 void tide_call_destroy(tide_call* call) {
     if (!call) return;
     if (call->dtab) {
-        int prev = -1;
-        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
-        (void)hipSetDevice(call->device);
+        DeviceGuard guard(call->device);
         (void)hipFree(call->dtab);
-        if (prev >= 0) (void)hipSetDevice(prev);
     }
     delete call;
 }
@@ -1286,6 +1307,8 @@ tide_status tide_landing_sum_fp32(int32_t L, int32_t M, int64_t S, const float* 
             int dev = 0;
             st = stream_device(stream, &dev);
             if (st != TIDE_OK) return st;
+            DeviceGuard guard(dev);
+            if (guard.status() != hipSuccess) return hip_fail(guard.status(), "hipSetDevice");
             const int key = M <= 8 ? M : 0;
             const uint64_t bit = (uint64_t)1 << key;
             if (dev < 64 && !(g_landing_lds_done[dev] & bit)) {

@@ -289,3 +289,58 @@ def test_struct_layouts_match_the_header(tide, tmp_path):
         for f, _ in cls._fields_:
             assert int(got["%s.%s" % (cname, f)]) == getattr(cls, f).offset, (cname, f)
     assert int(got["tide_trace_rec size"]) == tide._lib.TRACE_REC_BYTES
+
+
+def test_binding_checks_tensor_arguments(tide):
+    """The library sees only pointers, so the binding checks each tensor's
+    dtype, contiguity, size and device before passing its address (raw
+    integer addresses are the caller's and pass unchecked)."""
+    import torch
+    shapes = [(8, 4), (4, 4), (12, 4)]
+    plan = tide.plan_create(shapes, 4, 2)
+    N, S = plan.N, plan.S
+    out = torch.zeros(N * S, dtype=torch.float32)
+
+    def grads_with(c, p, t):
+        """Raw addresses everywhere but (c, p), which holds tensor t."""
+        g = [[FAKE + 0x100000 * (i * 3 + j) for j in range(3)] for i in range(2)]
+        g[c][p] = t
+        return g
+
+    with pytest.raises(TypeError):
+        tide.grads_table(plan, grads_with(1, 2, torch.zeros((12, 4), dtype=torch.float16)))
+    with pytest.raises(ValueError, match="not contiguous"):
+        tide.grads_table(plan, grads_with(0, 1, torch.zeros((4, 8), dtype=torch.bfloat16)[:, ::2]))
+    with pytest.raises(ValueError, match="not contiguous"):   # a broadcast view spans one row
+        tide.grads_table(plan, grads_with(0, 0, torch.zeros(4, dtype=torch.bfloat16).expand(8, 4)))
+    with pytest.raises(ValueError, match="expected 48"):
+        tide.grads_table(plan, grads_with(1, 2, torch.zeros((11, 4), dtype=torch.bfloat16)))
+    with pytest.raises(ValueError, match="not a GPU tensor"):
+        tide.grads_table(plan, grads_with(1, 0, torch.zeros((8, 4), dtype=torch.bfloat16)))
+    with pytest.raises(ValueError, match="params\\[1\\]"):
+        tide.params_table(plan, [FAKE, torch.zeros((4, 5), dtype=torch.bfloat16), FAKE + 4096])
+    tab = tide.PointerTable([FAKE] * (2 * 3))
+    with pytest.raises(ValueError, match="at least %d" % (N * S)):
+        tide.reduce_scatter_bf16_fp32(plan, tab, out[1:], stream=0)
+    with pytest.raises(ValueError, match="at least %d" % (3 * S + S + 5 * 3)):
+        tide.reduce_scatter_bf16_fp32(plan, tab, out, out_stride=S + 5, stream=0)
+    with pytest.raises(TypeError):
+        tide.reduce_scatter_bf16_fp32(plan, tab, out.view(torch.int32), stream=0)
+    ptab = tide.PointerTable([FAKE] * 3)
+    with pytest.raises(ValueError, match="shards"):
+        tide.allgather_place(plan, torch.zeros(N * S - 1, dtype=torch.bfloat16), ptab, stream=0)
+    with pytest.raises(ValueError, match="slots\\[1\\]"):
+        tide.stage_grads_bf16(plan, tab, [FAKE, torch.zeros(N * S - 1, dtype=torch.bfloat16)],
+                              stream=0)
+    with pytest.raises(ValueError, match="inboxes\\[0\\]"):
+        tide.landing_sum_fp32(2, 2, 7, [torch.zeros(15), FAKE], [FAKE, FAKE + 4096], stream=0)
+    # Trace and count buffers: dtype, and no capacity beyond the buffer.
+    buf = torch.zeros(3 * 10, dtype=torch.int64)
+    with pytest.raises(ValueError, match="holds 10 records"):
+        tide.traced(tide.Launch(), buf, records=11)
+    with pytest.raises(TypeError):
+        tide.traced(tide.Launch(), buf.view(torch.float64))
+    with pytest.raises(TypeError):
+        tide.counted(tide.Launch(), torch.zeros(8, dtype=torch.int64))
+    with pytest.raises(ValueError, match="at least 33"):
+        tide.diag_occupy(11, 64, 0, 10, buf, stream=0)
