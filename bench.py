@@ -155,9 +155,19 @@ def host_info():
     return {"cpu_model": model, "cores_available": len(os.sched_getaffinity(0))}
 
 
+def under_profiler() -> bool:
+    """True when rocprofv3 launched this process (its tool library is preloaded)."""
+    return "rocprof" in os.environ.get("LD_PRELOAD", "") or any(
+        k.startswith("ROCPROF_") for k in os.environ)
+
+
 def gpu_clocks():
-    """Current GPU clock state as rocm-smi reports it (None if it cannot be read)."""
+    """Current GPU clock state as rocm-smi reports it (None if it cannot be read).
+    Skipped under the profiler: there the child process would carry the
+    profiler's preloaded GPU state into rocm-smi's interpreter."""
     import subprocess
+    if under_profiler():
+        return None
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
                            timeout=20)
@@ -529,7 +539,8 @@ def main():
     plan = tide.plan_create(cfg.shapes, cfg.N, cfg.L)
     S = plan.S
     grads = device_grads(cfg.shapes, cfg.L, seed=cfg.seed, sigma=cfg.sigma,
-                         outlier_frac=cfg.outlier_frac)
+                         outlier_frac=cfg.outlier_frac,
+                         progress=lambda c: log("bench: contributor %d of %d drawn" % (c + 1, cfg.L)))
     out = torch.empty(cfg.N * S, dtype=torch.float32, device="cuda")
     shards = device_rank_major_bits(cfg.N * S, seed=1)
     params = [torch.empty((t, k), dtype=torch.bfloat16, device="cuda") for t, k in cfg.shapes]

@@ -89,10 +89,12 @@ def host_rank_major_bits(count: int, seed: int) -> np.ndarray:
 
 
 def device_grads(shapes: Sequence[Tuple[int, int]], L: int, seed: int,
-                 sigma: float = 1.0, outlier_frac: float = 0.0, device="cuda"):
+                 sigma: float = 1.0, outlier_frac: float = 0.0, device="cuda",
+                 progress=None):
     """grads[c][p] = a separately allocated bf16 (T_p, K_p) tensor on `device`.
 
     Drawn on the device from one seeded torch.Generator, contributor-major.
+    `progress(c)`, if given, is called once contributor c's tensors are drawn.
     """
     import torch
     g = torch.Generator(device=device)
@@ -113,6 +115,8 @@ def device_grads(shapes: Sequence[Tuple[int, int]], L: int, seed: int,
             row.append(x.to(torch.bfloat16))
             del x
         out.append(row)
+        if progress is not None:
+            progress(len(out) - 1)
     return out
 
 
