@@ -178,7 +178,8 @@ tide_status tide_plan_map(const tide_plan* plan, int32_t r, int32_t p, int64_t* 
  *       p, T_p x K_p contiguous, 2-byte aligned (may be NULL when T_p * K_p == 0).
  *       Read only; gradients are read in place, with no packed copy.
  *   out: device pointer to N fp32 shards; shard r starts at out + r * out_stride
- *       (out_stride >= S), 4-byte aligned.
+ *       (out_stride >= S), 4-byte aligned; the buffer must span
+ *       (N - 1) * out_stride + S elements.
  * For every rank r in [rank_begin, rank_end), every element of out[r][0..S) is
  * written exactly once: the fp32 sum over c = 0..L-1, in that order (a left
  * fold, binary32 round-to-nearest-even, subnormals kept), of the widened bf16
@@ -195,7 +196,9 @@ tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t*
 /*
  * All-gather placement, bf16.
  *   shards: device pointer to N rank-major bf16 shards, shard r at
- *       shards + r * shard_stride (shard_stride >= S), 2-byte aligned. Read only.
+ *       shards + r * shard_stride (shard_stride >= S), 2-byte aligned. Read only;
+ *       the buffer must span (N - 1) * shard_stride + S elements, and nothing
+ *       outside the pieces read is accessed.
  *   params[p]: device pointer to parameter p's storage, T_p x K_p contiguous,
  *       2-byte aligned (may be NULL when T_p * K_p == 0).
  * For every rank r in [rank_begin, rank_end), the true rows of rank r's piece

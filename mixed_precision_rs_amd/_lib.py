@@ -357,23 +357,25 @@ def params_table(plan: Plan, params: Sequence[object]) -> PointerTable:
     return PointerTable(params)
 
 
-def _record(tensors, stream_obj):
+def _record(tensors, stream_obj) -> bool:
     """Tell torch's caching allocator that the tensors are used on a
     non-default stream, so their memory is not handed out again before that
     stream's work on them has run (tensors are assumed to be allocated on the
     default stream; a caller that allocates on other streams records them
-    itself)."""
+    itself). Returns False when nothing could be recorded because the stream
+    is capturing a graph (the graph keeps its own references)."""
     import torch
     if stream_obj is None:
-        return
+        return True
     if stream_obj == torch.cuda.default_stream(stream_obj.device):
-        return
+        return True
     with torch.cuda.stream(stream_obj):
         if torch.cuda.is_current_stream_capturing():
-            return                  # a captured graph keeps its own references
+            return False
     for t in tensors:
         if t is not None and not isinstance(t, int):
             t.record_stream(stream_obj)
+    return True
 
 
 def reduce_scatter_bf16_fp32(plan: Plan, grads: Sequence[Sequence[object]], out,
@@ -485,11 +487,16 @@ class Call:
         self.plan = plan
         self._h = handle
         self.refs = refs
+        self._recorded = set()      # streams the buffers are already recorded on
 
     def enqueue(self, stream=None) -> None:
         sh, sobj = _stream_handle(stream)
         _check(_load().tide_call_enqueue(self._h, sh), "tide_call_enqueue")
-        _record(self.refs, sobj)
+        # The call holds its buffers for its whole life, so one record per
+        # stream covers every later enqueue on it (a gradient table of
+        # thousands of tensors would otherwise cost milliseconds per enqueue).
+        if sh not in self._recorded and _record(self.refs, sobj):
+            self._recorded.add(sh)
 
     def close(self):
         if self._h:

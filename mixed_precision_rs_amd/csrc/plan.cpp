@@ -734,7 +734,9 @@ tide_status prep_place(const tide_plan* plan, const uint16_t* shards, int64_t sh
         return fail(TIDE_ERR_OVERFLOW, "N * shard_stride * 2 overflows int64");
     pr->shards = shards;
     pr->shard_stride = shard_stride;
-    pr->shard_elems = shard_elems / 2;
+    // The extent the caller guarantees: the last shard ends at S, not at the
+    // stride. The kernel's realigning loads stay inside it.
+    pr->shard_elems = (int64_t)(plan->N - 1) * shard_stride + plan->S;
     pr->first_rank = first_rank;
     if (plan->S == 0 || l.rank_end == l.rank_begin) {
         pr->empty = true;

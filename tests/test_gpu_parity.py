@@ -151,6 +151,31 @@ def test_misaligned_destinations(tide, orc, out_off):
                  check_ag=False)
 
 
+@pytest.mark.parametrize("off", [0, 1])
+def test_tight_shard_buffer(tide, orc, off):
+    """A shards buffer that ends where the last shard's S elements end (a
+    stride above S), at a 4-byte or a 2-mod-4 base: the realigning 16-byte
+    loads near its end must stay inside it, and the result must still be the
+    oracle's."""
+    shapes = [(37, 24), (5, 3), (16, 9), (61, 2)]
+    N = 4
+    plan = tide.plan_create(shapes, N, 2)
+    S = plan.S
+    for stride in (S + 1, S + 6):
+        n = (N - 1) * stride + S
+        bits = host_rank_major_bits(N * stride, seed=stride)
+        sh = to_dev_bf16(bits[:n], (n,), off)
+        params = [to_dev_bf16(np.full(t * k, SENTINEL_BF16, np.uint16), (t, k)) for t, k in shapes]
+        say("tight shards: stride S+%d, base offset %d" % (stride - S, off))
+        tide.allgather_place(plan, sh, params, shard_stride=stride)
+        torch.cuda.synchronize()
+        want = orc.allgather_place(shapes, N, bits, shard_stride=stride)
+        for p in range(len(shapes)):
+            same_u16(bits_of(params[p]), want[p], "tight placement param %d" % p)
+        with pytest.raises(ValueError):
+            tide.allgather_place(plan, sh[:n - 1], params, shard_stride=stride)
+
+
 def test_runtime_contributor_count(tide, orc):
     """L above 8 takes the runtime-L kernel."""
     shapes = [(300, 64), (17, 1), (1000, 40)]
