@@ -258,6 +258,24 @@ std::vector<TileRec> build_tiles(const tide_plan* plan, int op, int rb, int re, 
     return out;
 }
 
+// The number of tiles build_tiles makes, in O(P): what the host-only
+// queries (launch and trace-record counts) need, without building the table.
+int64_t count_tiles(const tide_plan* plan, int op, int rb, int re, bool fat) {
+    const int64_t tile = tile_elems(op, fat);
+    int64_t n = 0;
+    for (int32_t p = 0; p < plan->P; ++p) {
+        const ParamInfo& q = plan->prm[p];
+        if (q.s == 0) continue;
+        const int64_t lo = (int64_t)rb * q.s;
+        int64_t hi = (int64_t)re * q.s;
+        if (op != 0) hi = std::min(hi, q.valid);
+        if (hi <= lo) continue;
+        const int64_t a = lo - lo % kVec;
+        n += (hi - a + tile - 1) / tile;
+    }
+    return n;
+}
+
 // Bytes a budgeted tile moves.
 int64_t tile_bytes(const tide_plan* plan, int op) {
     return op == 0 ? tile_elems(0, true) * (2 * (int64_t)plan->L + 4) : tile_elems(op, true) * 4;
@@ -620,7 +638,7 @@ tide_status tide_plan_launch_count(const tide_plan* plan, int32_t op, const tide
         tide_status st = resolve_launch(plan, launch, &l);
         if (st != TIDE_OK) return st;
         // The staging walks its tiling once per contributor.
-        int64_t n = (int64_t)build_tiles(plan, op, l.rank_begin, l.rank_end, l.mode == TIDE_LAUNCH_BUDGETED).size();
+        int64_t n = count_tiles(plan, op, l.rank_begin, l.rank_end, l.mode == TIDE_LAUNCH_BUDGETED);
         if (op == 2) n *= plan->L;
         *launches = count_launches(plan, op, l, n);
         return TIDE_OK;
@@ -861,6 +879,10 @@ tide_status device_side(const tide_plan* plan, const Prepared& pr, int dev, DevS
     if (st != TIDE_OK) return st;
     st = get_tiles(plan, *ds, pr.op, l.rank_begin, l.rank_end, l.mode == TIDE_LAUNCH_BUDGETED, tt);
     if (st != TIDE_OK) return st;
+    // The host-only counts must describe the table the kernels walk.
+    if ((*tt)->count != count_tiles(plan, pr.op, l.rank_begin, l.rank_end,
+                                    l.mode == TIDE_LAUNCH_BUDGETED))
+        return fail(TIDE_ERR_INVALID_ARG, "internal: tile table and tile count disagree");
     const int64_t items = pr.op == 2 ? (*tt)->count * plan->L : (*tt)->count;
     st = check_trace(l, launch_records(plan, pr.op, l, items));
     if (st != TIDE_OK) return st;
@@ -1400,7 +1422,7 @@ tide_status tide_plan_trace_records(const tide_plan* plan, int32_t op, const tid
         tide_launch l;
         tide_status st = resolve_launch(plan, launch, &l);
         if (st != TIDE_OK) return st;
-        int64_t n = (int64_t)build_tiles(plan, op, l.rank_begin, l.rank_end, l.mode == TIDE_LAUNCH_BUDGETED).size();
+        int64_t n = count_tiles(plan, op, l.rank_begin, l.rank_end, l.mode == TIDE_LAUNCH_BUDGETED);
         if (op == 2) n *= plan->L;
         *records = launch_records(plan, op, l, n);
         return TIDE_OK;
