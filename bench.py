@@ -39,11 +39,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_text(src: str) -> str:
+    """C++ source without its comments and blank-line or trailing-space noise:
+    what the compiler sees (the kernel sources hold no string literals with
+    comment markers)."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+
+
 def kernel_source_hash() -> str:
+    """sha256 of the kernel sources' code (comments excluded): counter
+    summaries taken on other kernel code are not used."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()
 
 

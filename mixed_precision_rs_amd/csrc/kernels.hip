@@ -1,11 +1,15 @@
 // HIP kernels for gfx950 (CDNA4): the level-1 bf16 -> fp32 reduce of TIDE's
-// reduce-scatter and the all-gather placement step.
+// reduce-scatter, the all-gather placement step, the Slot-Reuse staging copy
+// and the level-2 landing sum.
 //
-// Both are HBM streams with no reuse, so the design is about bytes in flight
+// All are HBM streams with no reuse, so the design is about bytes in flight
 // and access width, not arithmetic:
-//   * each thread owns kVec = 8 consecutive elements of a parameter's flat
-//     index space, so a wave64 touches 1 KiB of contiguous bf16 per
-//     contributor per instruction (global_load_dwordx4);
+//   * the placement and the staging give each thread kVec = 8 consecutive
+//     elements of a parameter's flat index space, so a wave64 touches 1 KiB
+//     of contiguous bf16 per instruction (16-byte accesses); the reduce lays
+//     a wave's 512 elements out as two runs of 256, 4 elements per lane, so
+//     its 8-byte bf16 loads and 16-byte fp32 stores are both contiguous
+//     across the wave;
 //   * the reduce keeps kRsUnroll steps x L contributors of loads in flight
 //     before it adds, the placement kAgUnroll steps of gathers;
 //   * the fp32 sum is a left fold over contributors in registers: no LDS;
