@@ -239,6 +239,19 @@ def _tensor_arg(t, dtype_name: str, what: str, numel: Optional[int] = None,
         raise ValueError("%s is not a GPU tensor" % what)
 
 
+def _check_many(tensors, dtype_name: str, numels, what) -> None:
+    """_tensor_arg over many tensors of exact sizes, with the common case (a
+    contiguous GPU tensor of the right dtype and size) tested in one pass;
+    `what(i)` names tensor i in an error."""
+    import torch
+    dtype = getattr(torch, dtype_name)
+    for i, (t, n) in enumerate(zip(tensors, numels)):
+        if t is None or isinstance(t, int):
+            continue
+        if t.dtype is not dtype or not t.is_cuda or t.numel() != n or not t.is_contiguous():
+            _tensor_arg(t, dtype_name, what(i), numel=n)
+
+
 def _shards_elems(plan: "Plan", stride: int) -> int:
     """Elements N shards of S, `stride` apart, span."""
     return 0 if plan.S == 0 else (plan.N - 1) * stride + plan.S
@@ -343,17 +356,16 @@ def grads_table(plan: Plan, grads: Sequence[Sequence[object]]) -> PointerTable:
     """grads[c][p] -> the L*P table tide_reduce_scatter_bf16_fp32 reads (c-major)."""
     if len(grads) != plan.L or any(len(g) != plan.P for g in grads):
         raise ValueError("grads must be L=%d lists of P=%d tensors" % (plan.L, plan.P))
-    for c in range(plan.L):
-        for p, (t, k) in enumerate(plan.shapes):
-            _tensor_arg(grads[c][p], "bfloat16", "grads[%d][%d]" % (c, p), numel=t * k)
-    return PointerTable([grads[c][p] for c in range(plan.L) for p in range(plan.P)])
+    flat = [grads[c][p] for c in range(plan.L) for p in range(plan.P)]
+    _check_many(flat, "bfloat16", [t * k for t, k in plan.shapes] * plan.L,
+                lambda i: "grads[%d][%d]" % divmod(i, plan.P))
+    return PointerTable(flat)
 
 
 def params_table(plan: Plan, params: Sequence[object]) -> PointerTable:
     if len(params) != plan.P:
         raise ValueError("params must hold P=%d tensors" % plan.P)
-    for p, (t, k) in enumerate(plan.shapes):
-        _tensor_arg(params[p], "bfloat16", "params[%d]" % p, numel=t * k)
+    _check_many(params, "bfloat16", [t * k for t, k in plan.shapes], lambda i: "params[%d]" % i)
     return PointerTable(params)
 
 
