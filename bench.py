@@ -535,7 +535,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only (the path is one GPU's share of "
+        print("bench.py: the benchmark runs on one GPU only (it measures one GPU's share of "
               "the collective); --gpus %d is not supported." % args.gpus, file=sys.stderr)
         sys.exit(2)
 
