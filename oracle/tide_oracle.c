@@ -33,7 +33,8 @@
  *   takes a left fold in contributor order: acc = f32(g_0), then
  *   acc = acc + f32(g_c) for c = 1..L-1, each add binary32 round-to-nearest-
  *   even, subnormals kept. bf16 -> fp32 is the exact widening (bits << 16).
- *   At L = 1 this is the stock "slice, zero-pad, upcast, pack" of page 1.
+ *   At L = 1 this is the stock path's result: each rank's rows sliced out,
+ *   zero-padded, widened to fp32 and packed (page 1).
  *
  *   All-gather placement. Rank r's piece of parameter p, read from the
  *   rank-major buffer at r * stride + o_p, lands at the parameter's own
