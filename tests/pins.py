@@ -12,9 +12,9 @@ Sources the pins use, none of which is the oracle's code:
   * torch._chunk_cat, the routine FSDP2 packs reduce-scatter inputs with
     (slice along dim 0 into N chunks, zero-pad each to the first chunk's
     rows, concatenate rank-major, optionally into an fp32 `out`): the stock
-    pack that page 1 describes as "slices, zero-pads and upcasts";
+    pack page 1 describes (slicing, zero padding and the fp32 upcast);
   * torch.split_with_sizes, FSDP2's all-gather copy-out (page 1; page 3
-    Table 7 "+ Copy-out" adds split_with_sizes_copy);
+    Table 7: its copy-out rows add split_with_sizes_copy);
   * closed forms: sums that are exact in binary32 regardless of order;
   * the error bound of recursive binary32 summation against the exact sum;
   * hand-derived results of crafted inputs whose value depends on the order.
