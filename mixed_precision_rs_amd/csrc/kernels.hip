@@ -12,7 +12,9 @@
 //     across the wave;
 //   * the reduce keeps kRsUnroll steps x L contributors of loads in flight
 //     before it adds, the placement kAgUnroll steps of gathers;
-//   * the fp32 sum is a left fold over contributors in registers: no LDS;
+//   * the fp32 sum is a left fold over contributors in registers; LDS only
+//     stages a reduce step whose destination starts mid-line, so that its
+//     stores cover whole lines;
 //   * the destination of the reduce and the source of the placement are
 //     only guaranteed 4-byte (fp32) or 2-byte (bf16) aligned: dword-aligned
 //     16-byte accesses are native on CDNA, and a bf16 run that starts
@@ -219,6 +221,11 @@ __device__ __forceinline__ void trace_end(tide_trace_rec* trace, int64_t base, u
     }
 }
 
+// Misaligned destinations through LDS (see the reduce's interior path).
+#ifndef TIDE_RS_LDS_ALIGN
+#define TIDE_RS_LDS_ALIGN 1
+#endif
+
 // Reduce: out[rank piece] = fold_c widen(g[c][f]) for f < valid, +0 past it.
 // LT > 0: L known at compile time (fully unrolled); LT == 0: runtime L.
 // A workgroup of NT threads is NT / kThreads independent quarters of kThreads
@@ -238,6 +245,12 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
     const int L = LT > 0 ? LT : Lrt;
     const int sub = (int)threadIdx.x / kThreads;          // wave-uniform
     const int tid = (int)threadIdx.x % kThreads;
+#if TIDE_RS_LDS_ALIGN
+    // Staging of one step for whole-line stores (full grid only; budgeted
+    // workgroups keep their LDS reservation for the fence).
+    __shared__ __attribute__((aligned(16))) float lds_stage[NT == kThreads ? kStep : 4];
+    const int64_t out_e0 = (int64_t)(reinterpret_cast<uintptr_t>(out) >> 2);
+#endif
     // One tile per workgroup (the full grid): XCD-aware order.
     const bool one_each = kSubs == 1 && (int64_t)gridDim.x == tile_hi - tile_lo;
     for (int64_t t = tile_lo + (int64_t)blockIdx.x * kSubs + sub; t < tile_hi;
@@ -287,6 +300,51 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
                                 }
                             }
                         }
+                    }
+                }
+                if constexpr (NT == kThreads && kUR == 1 && TIDE_RS_LDS_ALIGN) {
+                    // A step inside one rank's piece whose destination starts
+                    // mid-line (a prefix offset or shard stride not a multiple
+                    // of 32 elements): its sums go through LDS, so that each
+                    // wave-wide store covers whole 128-byte lines and only the
+                    // two lines at the step's ends are partly written, element
+                    // by element. Storing the runs in place leaves every run's
+                    // two end lines partly written by different waves, and
+                    // those partial lines cost 4-5% of the reduce's bandwidth
+                    // on MI355X (the counters show them as extra writes); the
+                    // LDS round trip costs nothing measurable.
+                    int64_t r, j;
+                    locate<kTileR>(tr, pd.s, g0, r, j);
+                    const int64_t d0 = r * out_stride + pd.o + j;   // destination of g0
+                    const int m = (int)((out_e0 + d0) & 31);
+                    if (m != 0 && j + kStep <= pd.s) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            float* at = lds_stage + (fw - g0) + h * kHalf + 4 * lane;
+                            *reinterpret_cast<float4*>(at) =
+                                make_float4(a[0][h][0], a[0][h][1], a[0][h][2], a[0][h][3]);
+                        }
+                        __syncthreads();
+                        const int a0 = 32 - m;                      // first element on a line start
+                        float* dst = out + d0;
+#pragma unroll
+                        for (int k = 0; k < 2; ++k) {
+                            const int q = tid + k * kThreads;       // quad of the whole lines
+                            if (q < (kStep - 32) / 4) {
+                                const int e = a0 + 4 * q;
+                                const f32x4_a4 x = {lds_stage[e], lds_stage[e + 1], lds_stage[e + 2],
+                                                    lds_stage[e + 3]};
+                                TIDE_ST(x, reinterpret_cast<f32x4_a4*>(dst + e));
+                                count_writes<CNT>(counts, d0 + e, 4);
+                            }
+                        }
+                        if (tid < 32) {                             // the two partial lines
+                            const int e = tid < a0 ? tid : kStep - 32 + tid;
+                            dst[e] = lds_stage[e];
+                            count_writes<CNT>(counts, d0 + e, 1);
+                        }
+                        __syncthreads();                            // lds_stage is reused by the next tile
+                        continue;
                     }
                 }
 #pragma unroll
