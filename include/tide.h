@@ -107,8 +107,9 @@ typedef struct tide_trace_rec {
  * all ranks. Fields equal to 0 take their defaults. */
 typedef struct tide_launch {
     int32_t mode;            /* tide_launch_mode */
-    int32_t reduce_blocks;   /* BUDGETED: workgroups of each reduce launch (0 -> 16) */
-    int32_t place_blocks;    /* BUDGETED: workgroups of each placement or landing launch (0 -> 4) */
+    int32_t reduce_blocks;   /* BUDGETED: workgroups of each reduce launch (0 -> 16; at most 65536) */
+    int32_t place_blocks;    /* BUDGETED: workgroups of each placement or landing launch (0 -> 4;
+                                at most 65536) */
     int32_t max_launch_us;   /* BUDGETED: work per launch sized so a workgroup lives about
                                 this long (0 -> 300). Each launch is a separate kernel; no
                                 workgroup ever waits on another. */

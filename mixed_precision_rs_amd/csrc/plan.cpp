@@ -100,10 +100,16 @@ constexpr int64_t kWgBytesPerUsRs = TIDE_WG_BYTES_PER_US_RS;
 constexpr int64_t kWgBytesPerUsAg = TIDE_WG_BYTES_PER_US_AG;       // placement and staging
 constexpr int64_t kWgBytesPerUsLanding = TIDE_WG_BYTES_PER_US_LANDING;
 // Full mode: at most this many workgroups per launch (they loop over tiles).
+// A dispatch holds at most 2^32 - 1 work-items; 2^24 workgroups of 128
+// threads stay well below that (a group of up to 16 G reduce elements still
+// gets one workgroup per tile).
 #ifndef TIDE_FULL_GRID_CAP
-#define TIDE_FULL_GRID_CAP (1 << 30)
+#define TIDE_FULL_GRID_CAP (1 << 24)
 #endif
 constexpr int kFullGridCap = TIDE_FULL_GRID_CAP;
+static_assert((int64_t)kFullGridCap * kThreads < (int64_t(1) << 32), "dispatch size");
+// Budgeted mode: at most this many workgroups per launch (of kFatThreads).
+constexpr int32_t kMaxBudgetBlocks = 65536;
 #ifndef TIDE_RS_GROUP_ELEMS
 #define TIDE_RS_GROUP_ELEMS (1 << 20)
 #endif
@@ -188,6 +194,9 @@ tide_status resolve_launch(const tide_plan* plan, const tide_launch* in, tide_la
         return fail(TIDE_ERR_INVALID_ARG, "launch.mode %d is not FULL (0) or BUDGETED (1)", l.mode);
     if (l.reduce_blocks < 0 || l.place_blocks < 0 || l.max_launch_us < 0)
         return fail(TIDE_ERR_INVALID_ARG, "negative launch budget");
+    if (l.reduce_blocks > kMaxBudgetBlocks || l.place_blocks > kMaxBudgetBlocks)
+        return fail(TIDE_ERR_INVALID_ARG, "reduce_blocks %d / place_blocks %d above %d",
+                    l.reduce_blocks, l.place_blocks, kMaxBudgetBlocks);
     if (l.reserved != 0 || (l.flags & ~kKnownFlags) != 0)
         return fail(TIDE_ERR_INVALID_ARG, "unknown launch flags 0x%x", l.flags);
     if (l.trace_capacity < 0) return fail(TIDE_ERR_INVALID_ARG, "negative trace_capacity");
@@ -403,6 +412,10 @@ tide_status stage_table(DevState* ds, const void* bytes, size_t n, hipStream_t s
         ds->event_pool.push_back(r.ev);
     }
     s.readers.clear();
+    // The slot's previous upload reads the pinned host copy when its stream
+    // reaches it; every upload is followed by a reader event, but a call that
+    // failed to record one must not let the copy be overwritten early.
+    if (s.loaded) TIDE_HIP_TRY(hipEventSynchronize(s.upload_done));
     s.loaded = false;
     std::memcpy(s.host, bytes, n);
     TIDE_HIP_TRY(hipMemcpyAsync(s.dev, s.host, n, hipMemcpyHostToDevice, stream));
@@ -1250,6 +1263,9 @@ tide_status landing_launch(int32_t L, int32_t M, int64_t S, int32_t accumulate,
         return fail(TIDE_ERR_INVALID_ARG, "launch.mode %d is not FULL (0) or BUDGETED (1)", l.mode);
     if (l.reduce_blocks < 0 || l.place_blocks < 0 || l.max_launch_us < 0)
         return fail(TIDE_ERR_INVALID_ARG, "negative launch budget");
+    if (l.reduce_blocks > kMaxBudgetBlocks || l.place_blocks > kMaxBudgetBlocks)
+        return fail(TIDE_ERR_INVALID_ARG, "reduce_blocks %d / place_blocks %d above %d",
+                    l.reduce_blocks, l.place_blocks, kMaxBudgetBlocks);
     if (l.reserved != 0 || (l.flags & ~kKnownFlags) != 0)
         return fail(TIDE_ERR_INVALID_ARG, "unknown launch flags 0x%x", l.flags);
     if (l.trace_capacity < 0) return fail(TIDE_ERR_INVALID_ARG, "negative trace_capacity");

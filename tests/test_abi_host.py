@@ -230,6 +230,21 @@ def test_trace_record_counts_and_flags(tide):
     assert _status(lambda: tide.landing_trace_records(8, 9, S)) == "TIDE_ERR_INVALID_ARG"
 
 
+def test_grid_stays_within_one_dispatch(tide):
+    """A dispatch holds fewer than 2^32 work-items: a group with more tiles
+    than the full grid's cap gets the capped grid (its workgroups loop over
+    the rest), and budgeted block counts are bounded."""
+    plan = tide.plan_create([(1 << 22, 8192)], 64, 1)      # 2^35 elements, 2^25 reduce tiles
+    cap = plan.trace_records(0)
+    assert cap == 1 << 24 and cap * 128 < 1 << 32
+    assert plan.launch_count(0) == 1
+    assert plan.trace_records(1) == 1 << 24
+    b = tide.budgeted(reduce_blocks=65536, place_blocks=65536)
+    assert plan.trace_records(0, b) <= plan.launch_count(0, b) * 65536
+    for bad in (tide.budgeted(reduce_blocks=65537), tide.budgeted(place_blocks=1 << 30)):
+        assert _status(lambda: plan.launch_count(0, bad)) == "TIDE_ERR_INVALID_ARG"
+
+
 def test_diag_occupy_validates(tide):
     occ = tide.diag_occupy
     assert _status(lambda: occ(0, 256, 0, 10, FAKE, stream=0)) == "TIDE_ERR_INVALID_ARG"
