@@ -97,3 +97,46 @@ def test_beyond_int32(tide, orc):
     del sh, params, v
     _free()
     say("large: ok")
+
+
+# 2,097,160 x 8192 = 17,179,934,720 elements (> 2^34): 16,777,280 reduce
+# tiles, 64 more than the full grid's 2^24 workgroups, so the last tiles are
+# reached through the workgroups' loop. N = 8 divides T: no padding.
+HUGE = [(2_097_160, 8192)]
+
+
+def test_full_grid_cap_and_beyond_2_34(tide):
+    """One reduce over more tiles than the full grid has workgroups, with
+    element offsets beyond 2^34 (byte offsets beyond 2^36). Two identical
+    contributors give the closed form out = 2 * f32(g) in every element
+    (doubling is exact in binary32; a bf16 near its maximum doubles to inf on
+    both sides). About 103 GB of device memory."""
+    (t, k), = HUGE
+    n = t * k
+    plan = tide.plan_create(HUGE, 8, 2)
+    assert plan.S * 8 == n and n > 2 ** 34
+    tiles = plan.trace_records(0)
+    assert tiles == 1 << 24 and n // 1024 > tiles
+    say("huge: drawing %d bf16 values (%.1f GB)" % (n, 2 * n / 1e9))
+    g = torch.empty((t, k), dtype=torch.bfloat16, device=dev())
+    flat = g.view(-1)
+    gen = torch.Generator(device=dev())
+    gen.manual_seed(11)
+    chunk = 1 << 30
+    for a in range(0, n, chunk):
+        b = min(n, a + chunk)
+        flat[a:b] = torch.randn(b - a, generator=gen, device=dev(), dtype=torch.float32).to(torch.bfloat16)
+    out = torch.empty(n, dtype=torch.float32, device=dev())
+    out.view(torch.int32).fill_(0x7FC0DEAD)
+    say("huge: reduce-scatter")
+    tide.reduce_scatter_bf16_fp32(plan, [[g], [g]], out)
+    torch.cuda.synchronize()
+    say("huge: checking every element in %d chunks" % ((n + chunk - 1) // chunk))
+    for a in range(0, n, chunk):
+        b = min(n, a + chunk)
+        want = flat[a:b].float().mul_(2.0)
+        assert torch.equal(out[a:b].view(torch.int32), want.view(torch.int32)), (a, b)
+        del want
+    del g, flat, out
+    _free()
+    say("huge: ok")
