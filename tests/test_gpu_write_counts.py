@@ -22,6 +22,10 @@ GROUPS = [
     ([(3, 5)], 8, 2),
     ([(300, 1000), (17, 4096), (1, 1), (5000, 64)], 64, 8),
     (padding_stress_shapes(5, count=24, max_rows=400, ks=(1, 3, 64, 4096)), 48, 4),
+    # Reduce tile order: 50 small pieces (24,576 elements each, 1.2 M per rank)
+    # form one long group walked rank by rank; a 131,072-element piece closes
+    # it; 50 more small pieces and a tiny one follow.
+    ([(768, 256)] * 50 + [(2048, 512)] + [(768, 256)] * 50 + [(7, 3)], 8, 2),
 ]
 
 
