@@ -472,6 +472,94 @@ __device__ __forceinline__ u32x4 gather8(const Span& t, const ParamDev& pd, int6
     return w;
 }
 
+// gather8 for a step in which every lane of the wave takes part (the
+// placement's interior steps). A source at 2 mod 4 needs the dword after its
+// 16-byte load: when the next lane reads on in the same piece, that dword is
+// the next lane's first one and comes over the lane crossbar instead of from
+// a second load (measured on MI355X: the second load cost the placement 10%
+// whenever half its sources sat at 2 mod 4).
+#ifndef TIDE_AG_NEIGHBOUR
+#define TIDE_AG_NEIGHBOUR 1
+#endif
+template <int64_t kTile, int U>
+__device__ __forceinline__ void gather8_wave(const Span& t, const ParamDev& pd, int64_t f0, int lane,
+                                             const uint16_t* __restrict__ shards, int64_t stride,
+                                             int64_t shard_elems, int32_t first, int32_t n,
+                                             u32x4 (&w)[U]) {
+    int64_t r[U], j[U], e[U];
+    bool direct[U], shift[U], from_next[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        locate<kTile>(t, pd.s, f0 + (int64_t)u * kStep, r[u], j[u]);
+        e[u] = stage_pos(r[u], first, n) * stride + pd.o + j[u];
+        const bool inside = j[u] + kVec <= pd.s;
+        const bool odd = (reinterpret_cast<uintptr_t>(shards + e[u]) & 3) != 0;
+        direct[u] = inside && !odd;
+        shift[u] = inside && odd && e[u] >= 1 && e[u] + 9 <= shard_elems;
+        // Lane l+1 then holds elements e+8.. of the same piece, at the same
+        // alignment and inside the buffer: it takes the shifted load too, and
+        // its first dword holds elements e+7, e+8.
+        from_next[u] = shift[u] && lane != kWave - 1 && j[u] + 2 * kVec <= pd.s &&
+                       e[u] + 17 <= shard_elems;
+    }
+    bool all_direct = true;
+#pragma unroll
+    for (int u = 0; u < U; ++u) all_direct = all_direct && direct[u];
+    if (__builtin_amdgcn_ballot_w64(!all_direct) == 0) {   // wave-uniform: every source dword-aligned
+#pragma unroll
+        for (int u = 0; u < U; ++u) w[u] = TIDE_LD(reinterpret_cast<const u32x4_a4*>(shards + e[u]));
+        return;
+    }
+    // All loads are issued before any result is used, the ninth pair of a
+    // lane without a neighbour included.
+    u32x4 x[U];
+    uint32_t y[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        x[u] = u32x4{0u, 0u, 0u, 0u};
+        y[u] = 0u;
+        if (direct[u])
+            x[u] = TIDE_LD(reinterpret_cast<const u32x4_a4*>(shards + e[u]));
+        else if (shift[u])
+            x[u] = TIDE_LD(reinterpret_cast<const u32x4_a4*>(shards + e[u] - 1));
+        if (shift[u] && !from_next[u]) y[u] = TIDE_LD(reinterpret_cast<const uint32_t*>(shards + e[u] - 1) + 4);
+    }
+    bool any_shift = false;
+#pragma unroll
+    for (int u = 0; u < U; ++u) any_shift = any_shift || shift[u];
+    if (__builtin_amdgcn_ballot_w64(any_shift) != 0) {     // wave-uniform
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // Every lane of the wave runs this: lane l receives lane l+1's first dword.
+            const uint32_t next =
+                (uint32_t)__builtin_amdgcn_ds_bpermute(((lane + 1) & (kWave - 1)) << 2, (int)x[u][0]);
+            if (from_next[u]) y[u] = next;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (direct[u]) {
+            w[u] = x[u];
+        } else if (shift[u]) {
+            w[u][0] = __builtin_amdgcn_alignbit(x[u][1], x[u][0], 16);
+            w[u][1] = __builtin_amdgcn_alignbit(x[u][2], x[u][1], 16);
+            w[u][2] = __builtin_amdgcn_alignbit(x[u][3], x[u][2], 16);
+            w[u][3] = __builtin_amdgcn_alignbit(y[u], x[u][3], 16);
+        } else {
+            // Straddles two ranks' pieces, or sits at the very ends of the buffer.
+            int64_t rr = r[u], jj = j[u];
+            uint32_t h[kVec];
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                h[k] = shards[stage_pos(rr, first, n) * stride + pd.o + jj];
+                step(pd.s, rr, jj);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) w[u][m] = h[2 * m] | (h[2 * m + 1] << 16);
+        }
+    }
+}
+
 // Placement: param[f] = shards[rank(f) * stride + o_p + offset(f)] for true f.
 template <int NT, bool CNT>
 __global__ __launch_bounds__(NT) void place_kernel(
@@ -504,10 +592,15 @@ __global__ __launch_bounds__(NT) void place_kernel(
             const int64_t f0 = g0 + (int64_t)tid * kVec;
             if (vec && g0 >= tr.lo && g1 <= end) {
                 u32x4 w[kUA];
+#if TIDE_AG_NEIGHBOUR
+                gather8_wave<kTileA, kUA>(tr, pd, f0, tid % kWave, shards, stride, shard_elems, first,
+                                          nranks, w);
+#else
 #pragma unroll
                 for (int u = 0; u < kUA; ++u)
                     w[u] = gather8<kTileA>(tr, pd, f0 + (int64_t)u * kStep, shards, stride, shard_elems,
                                    first, nranks);
+#endif
                 TIDE_GLOBAL u32x4* d4 = gbl_mut<u32x4>(dst + f0);
 #pragma unroll
                 for (int u = 0; u < kUA; ++u) {
