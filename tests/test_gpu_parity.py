@@ -152,6 +152,35 @@ def test_misaligned_destinations(tide, orc, out_off):
 
 
 @pytest.mark.parametrize("off", [0, 1])
+def test_placement_sources_at_every_lane_boundary(tide, orc, off):
+    """Placement sources at 2 mod 4 take the dword after their 16-byte load
+    from the next lane when it reads on in the same piece. Pieces here end at
+    many different lanes of a wave (s_p mod 512 varies), prefix offsets are odd
+    and even, and the shard buffer starts at a 4-byte or a 2-mod-4 address,
+    at strides S and S+1, over all ranks and a rank subset."""
+    shapes = [(4 * 513, 1), (4 * 131, 3), (4 * 700, 1), (4 * 64, 5), (4 * 1031, 1), (4 * 9, 7),
+              (4 * 2047, 1), (4 * 257, 2), (4 * 100, 41), (4 * 3, 1)]
+    N = 4
+    plan = tide.plan_create(shapes, N, 1)
+    S = plan.S
+    for extra in (0, 1):
+        stride = S + extra
+        n = (N - 1) * stride + S
+        bits = host_rank_major_bits(N * stride, seed=100 + extra)
+        sh = to_dev_bf16(bits[:n], (n,), off)
+        for rr in ((0, N), (1, 3)):
+            params = [to_dev_bf16(np.full(t * k, SENTINEL_BF16, np.uint16), (t, k)) for t, k in shapes]
+            say("lane exchange: stride S+%d, base offset %d, ranks %s" % (extra, off, rr))
+            tide.allgather_place(plan, sh, params, shard_stride=stride,
+                                 launch=tide.Launch(rank_begin=rr[0], rank_end=rr[1]))
+            torch.cuda.synchronize()
+            want = [np.full(t * k, SENTINEL_BF16, np.uint16) for t, k in shapes]
+            orc.allgather_place(shapes, N, bits, shard_stride=stride, rank_range=rr, params=want)
+            for p in range(len(shapes)):
+                same_u16(bits_of(params[p]), want[p], "placement param %d" % p)
+
+
+@pytest.mark.parametrize("off", [0, 1])
 def test_tight_shard_buffer(tide, orc, off):
     """A shards buffer that ends where the last shard's S elements end (a
     stride above S), at a 4-byte or a 2-mod-4 base: the realigning 16-byte
