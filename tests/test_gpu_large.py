@@ -1,6 +1,7 @@
 """Offsets beyond 2^31 elements: one parameter larger than 2^31 elements and a
 second whose rank-major pieces start beyond 2^31 in the output, through the
-reduce-scatter, the placement, and the Slot-Reuse staging.
+reduce-scatter, the placement, and the Slot-Reuse staging; and one reduce of
+more than 2^34 elements, whose tiles outnumber the full grid's workgroups.
 
 Checks: sampled pieces against the oracle (bit for bit), the identical-
 contributor whole-output closed form (2 * f32(g) in every true element, +0
