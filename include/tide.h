@@ -177,7 +177,10 @@ tide_status tide_plan_map(const tide_plan* plan, int32_t r, int32_t p, int64_t* 
  * Level-1 reduce-scatter, bf16 in, fp32 out.
  *   grads[c * P + p]: device pointer to contributor c's bf16 gradient of parameter
  *       p, T_p x K_p contiguous, 2-byte aligned (may be NULL when T_p * K_p == 0).
- *       Read only; gradients are read in place, with no packed copy.
+ *       Read only; gradients are read in place, with no packed copy. Speed: a
+ *       parameter is read with vector loads only when all L of its gradients
+ *       are 16-byte aligned (separate device allocations are); otherwise it is
+ *       summed element by element, with the same result.
  *   out: device pointer to N fp32 shards; shard r starts at out + r * out_stride
  *       (out_stride >= S), 4-byte aligned; the buffer must span
  *       (N - 1) * out_stride + S elements.
@@ -201,7 +204,9 @@ tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t*
  *       the buffer must span (N - 1) * shard_stride + S elements, and nothing
  *       outside the pieces read is accessed.
  *   params[p]: device pointer to parameter p's storage, T_p x K_p contiguous,
- *       2-byte aligned (may be NULL when T_p * K_p == 0).
+ *       2-byte aligned (may be NULL when T_p * K_p == 0). Speed: a parameter
+ *       is written with 16-byte stores only when params[p] is 16-byte aligned;
+ *       otherwise element by element, with the same bytes.
  * For every rank r in [rank_begin, rank_end), the true rows of rank r's piece
  * of every parameter are copied bit for bit to rows r * R_p.. of params[p];
  * padded rows are not written, and nothing else in params is touched.
