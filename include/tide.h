@@ -178,8 +178,8 @@ tide_status tide_plan_map(const tide_plan* plan, int32_t r, int32_t p, int64_t* 
  *   grads[c * P + p]: device pointer to contributor c's bf16 gradient of parameter
  *       p, T_p x K_p contiguous, 2-byte aligned (may be NULL when T_p * K_p == 0).
  *       Read only; gradients are read in place, with no packed copy. Speed: a
- *       parameter is read with vector loads only when all L of its gradients
- *       are 16-byte aligned (separate device allocations are); otherwise it is
+ *       parameter is read with vector loads when all L of its gradients are
+ *       4-byte aligned (separate device allocations are); otherwise it is
  *       summed element by element, with the same result.
  *   out: device pointer to N fp32 shards; shard r starts at out + r * out_stride
  *       (out_stride >= S), 4-byte aligned; the buffer must span

@@ -33,6 +33,7 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 // Pointers read from the per-call table are generic pointers to the compiler;
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
                 constexpr int kCUnroll = LT > 0 ? LT : 1;
 #pragma unroll kCUnroll
                 for (int c = 0; c < L; ++c) {
-                    const TIDE_GLOBAL u32x2* gc = gbl<u32x2>(g[c] + fh);
+                    const TIDE_GLOBAL u32x2_a4* gc = gbl<u32x2_a4>(g[c] + fh);
                     u32x2 v[kUR][2];
 #pragma unroll
                     for (int u = 0; u < kUR; ++u)
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
             } else {
                 // Ragged step: it crosses an end of the launch's range or of
                 // the tile, or the valid end, or the parameter has pointers
-                // that are not 16-byte aligned. A thread's group of 8
+                // that are not 4-byte aligned. A thread's group of 8
                 // elements that lies wholly inside the step's bounds and on
                 // one side of the valid end still goes as one vector; only
                 // a group that straddles a bound goes element by element.
@@ -377,7 +378,7 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
                         constexpr int kCUnroll = LT > 0 ? LT : 1;
 #pragma unroll kCUnroll
                         for (int c = 0; c < L; ++c) {
-                            const u32x4 v = TIDE_LD(gbl<u32x4>(g[c] + fu));
+                            const u32x4 v = TIDE_LD(gbl<u32x4_a4>(g[c] + fu));
 #pragma unroll
                             for (int m = 0; m < 4; ++m) {
                                 const float lo = lo_bf16(v[m]), hi = hi_bf16(v[m]);

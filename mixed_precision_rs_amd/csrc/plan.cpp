@@ -747,7 +747,7 @@ tide_status prep_reduce(const tide_plan* plan, const uint16_t* const* grads, flo
             if (!g) return fail(TIDE_ERR_INVALID_ARG, "grads[%d] (c=%d, p=%d) is NULL", c * P + p, c, p);
             const uintptr_t a = reinterpret_cast<uintptr_t>(g);
             if (a & 1) return fail(TIDE_ERR_ALIGNMENT, "grads[%d] is not 2-byte aligned", c * P + p);
-            if (a & 15) f &= ~kFlagVector;
+            if (a & 3) f &= ~kFlagVector;        // multi-dword loads need dword alignment only
             const Range in{a, a + (uintptr_t)q.valid * 2, c * P + p};
             if (overlaps(in, w))
                 return fail(TIDE_ERR_INVALID_ARG, "grads[%d] overlaps the output", c * P + p);

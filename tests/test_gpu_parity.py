@@ -151,6 +151,22 @@ def test_misaligned_destinations(tide, orc, out_off):
                  check_ag=False)
 
 
+def test_gradients_at_dword_offsets(tide, orc):
+    """Gradients 4-byte aligned but not 16-byte aligned (offsets of 2, 4 and 6
+    elements, mixed per contributor and parameter) still take the vector loads;
+    2-byte offsets take the element path. Both must give the oracle's bits, at
+    aligned and misaligned output strides and over a rank subset."""
+    shapes = [(512, 1024), (300, 520), (70, 1), (1000, 3), (9, 4096)]
+    N, L = 8, 8
+    grads = host_grads(shapes, L, seed=77)
+    for name, offs in (("dword", [[2 * ((c + p) % 4) for p in range(len(shapes))] for c in range(L)]),
+                       ("mixed", [[(c * 3 + p) % 8 for p in range(len(shapes))] for c in range(L)])):
+        for stride_extra, rr in ((0, None), (1, (2, 7))):
+            say("gradient offsets %s, stride S+%d, ranks %s" % (name, stride_extra, rr))
+            run_case(tide, orc, shapes, N, L, grads, stride_extra=stride_extra, grad_offs=offs,
+                     rank_range=rr, check_ag=False)
+
+
 @pytest.mark.parametrize("off", [0, 1])
 def test_placement_sources_at_every_lane_boundary(tide, orc, off):
     """Placement sources at 2 mod 4 take the dword after their 16-byte load
