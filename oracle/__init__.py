@@ -147,6 +147,78 @@ class Oracle:
             return out2, counts.reshape(N, stride)
         return out2
 
+    def reduce_scatter_rows(self, shapes, N, L, grads_rows: List[List[np.ndarray]],
+                            rank_range: Tuple[int, int], out_rows: np.ndarray):
+        """reduce_scatter over ranks [rb, re) from inputs that hold only those
+        ranks' rows, so a very large group can be checked range by range with
+        bounded host memory. grads_rows[c][p] holds rows
+        [rb * R_p, min(T_p, re * R_p)) of contributor c's gradient (flat uint16);
+        out_rows (float32, (re - rb) * S elements) receives shards rb .. re - 1.
+        The unchanged C routine is called with every base pointer moved back by
+        the rows (and shards) the arrays leave out, so its own indexing, which
+        only touches rows and shards of the range, lands inside them."""
+        rows, rlen = self._shape_arrays(shapes)
+        P = len(shapes)
+        lay = self.layout(shapes, N)
+        S = lay["S"]
+        rb, re = rank_range
+        if not (0 <= rb <= re <= N) or out_rows.dtype != np.float32 or \
+                out_rows.size < (re - rb) * S or not out_rows.flags.c_contiguous:
+            raise ValueError("reduce_scatter_rows: bad range or output")
+        keep, ptrs = [], []
+        for c in range(L):
+            for p in range(P):
+                t, k = shapes[p]
+                first = min(t, rb * int(lay["R"][p]))
+                a = np.ascontiguousarray(grads_rows[c][p], dtype=np.uint16)
+                if a.size != (min(t, re * int(lay["R"][p])) - first) * k:
+                    raise ValueError("grads_rows[%d][%d] holds %d elements" % (c, p, a.size))
+                keep.append(a)
+                ptrs.append(a.ctypes.data - first * k * 2 if a.size else 0)
+        parr = (_U16P * max(len(ptrs), 1))(*[ctypes.cast(ctypes.c_void_p(x), _U16P)
+                                              for x in ptrs])
+        out_base = ctypes.cast(ctypes.c_void_p(out_rows.ctypes.data - rb * S * 4), _F32P)
+        t0 = time.perf_counter()
+        rc = self.lib.oracle_reduce_scatter(P, self._p(rows, _I64P), self._p(rlen, _I64P), N, L,
+                                            parr, out_base, S, rb, re, None)
+        self.last_call_s = time.perf_counter() - t0
+        if rc != 0:
+            raise ValueError("oracle_reduce_scatter rejected its arguments")
+        return out_rows
+
+    def allgather_place_rows(self, shapes, N, shards_rows: np.ndarray,
+                             rank_range: Tuple[int, int], params_rows: List[np.ndarray]):
+        """allgather_place over ranks [rb, re) with only those ranks' data in
+        memory: shards_rows holds shards rb .. re - 1 ((re - rb) * S uint16,
+        stride S); params_rows[p] receives rows [rb * R_p, min(T_p, re * R_p))
+        of parameter p. Base pointers are moved back as in reduce_scatter_rows."""
+        rows, rlen = self._shape_arrays(shapes)
+        P = len(shapes)
+        lay = self.layout(shapes, N)
+        S = lay["S"]
+        rb, re = rank_range
+        shards_rows = np.ascontiguousarray(shards_rows, dtype=np.uint16)
+        if not (0 <= rb <= re <= N) or shards_rows.size < (re - rb) * S:
+            raise ValueError("allgather_place_rows: bad range or shards")
+        ptrs = []
+        for p in range(P):
+            t, k = shapes[p]
+            first = min(t, rb * int(lay["R"][p]))
+            a = params_rows[p]
+            if a.dtype != np.uint16 or not a.flags.c_contiguous or \
+                    a.size != (min(t, re * int(lay["R"][p])) - first) * k:
+                raise ValueError("params_rows[%d] has the wrong size or type" % p)
+            ptrs.append(a.ctypes.data - first * k * 2 if a.size else 0)
+        parr = (_U16P * max(P, 1))(*[ctypes.cast(ctypes.c_void_p(x), _U16P) for x in ptrs])
+        sh_base = ctypes.cast(ctypes.c_void_p(shards_rows.ctypes.data - rb * S * 2), _U16P)
+        t0 = time.perf_counter()
+        rc = self.lib.oracle_allgather_place(P, self._p(rows, _I64P), self._p(rlen, _I64P), N,
+                                             sh_base, S, parr, rb, re, None)
+        self.last_call_s = time.perf_counter() - t0
+        if rc != 0:
+            raise ValueError("oracle_allgather_place rejected its arguments")
+        return params_rows
+
     def reduce_piece(self, shapes, N, L, r, p, rank_rows: List[np.ndarray]) -> np.ndarray:
         rows, rlen = self._shape_arrays(shapes)
         lay = self.layout(shapes, N)
