@@ -4,16 +4,19 @@ on MI355X: the level-1 bf16 -> fp32 reduce-scatter into padded rank-major
 shards, then the all-gather placement into parameter storage.
 
 One step = one reduce-scatter + one placement (HIP kernel engine) of one
-parameter group, back to back on one stream, inputs already in HBM.
-value = algorithmic bytes per step / time per step:
+parameter group, back to back on one stream, inputs already in HBM. The
+default group is the padding-stress group (the largest); the Llama, Qwen and
+Wan groups follow in a per_config block, with the Wan GEMM-victim protocol.
+value = algorithmic bytes per step / median time per step:
     reduce-scatter: 2 * L * valid (bf16 reads) + 4 * N * S (fp32 writes,
                     padding included), placement: 2 * valid + 2 * valid.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--parts] [--victim] [--stock] [--slot-reuse] [--occupancy] [--graph]
-                  [--no-cpu-baseline]
+                  [--placement-engine kernel|sdma|runtime] [--parts] [--victim] [--stock]
+                  [--slot-reuse] [--occupancy] [--graph] [--no-cpu-baseline]
+                  [--no-per-config]
 """
 import argparse
 import hashlib
@@ -79,75 +82,112 @@ def group_bytes(cfg, S):
     return rs, ag, valid
 
 
-def cpu_baseline(orc, cfg, plan, grads, shards, out, ranks, reps=3):
-    """Time the CPU oracle on ranks [0, ranks) of the same group, with the same
-    bits copied from the GPU (median of `reps` runs of each leg): once on one
-    thread, and once with one host thread per available core, each calling the
-    unchanged oracle on its own slice of the ranks (the oracle's C calls release
-    the interpreter lock, and the slices write disjoint output). Checks the
-    GPU's shards on the sample."""
+def _run_threads(fn, a, b, nthreads):
+    """fn(x, y) on up to `nthreads` host threads over disjoint rank slices of
+    [a, b) (the oracle's C calls release the interpreter lock); wall seconds."""
     import threading
+    cuts = [a + round(i * (b - a) / nthreads) for i in range(nthreads + 1)]
+    slices = [(x, y) for x, y in zip(cuts, cuts[1:]) if y > x]
+    th = [threading.Thread(target=fn, args=sl) for sl in slices]
+    t0 = time.perf_counter()
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    return time.perf_counter() - t0, len(slices)
 
+
+def oracle_check(orc, cfg, plan, grads, out, shards, params, one_thread_reps=0):
+    """The whole output of one step against the CPU oracle, bit for bit: every
+    shard of the reduce-scatter and every parameter the placement wrote, from
+    the same bits copied from the GPU. Streamed by rank range (as many ranks
+    at a time as host threads), so host memory stays bounded by one range's
+    gradients. The oracle runs unchanged, one host thread per rank slice.
+    With one_thread_reps > 0, the first range is also timed on one thread
+    (median of that many runs)."""
     import numpy as np
     import torch
-    N, L, S = cfg.N, cfg.L, plan.S
-    lay = orc.layout(cfg.shapes, N)
-    h_grads, valid = [], 0
-    for c in range(L):
-        row = []
-        for p, (t, k) in enumerate(cfg.shapes):
-            nrows = min(t, ranks * int(lay["R"][p]))
-            row.append(grads[c][p][:nrows].reshape(-1).view(torch.int16).cpu().numpy()
-                       .view(np.uint16))
-            if c == 0:
-                valid += nrows * k
-        h_grads.append(row)
-    h_out = np.empty(N * S, np.float32)
-    h_sh = np.zeros(N * S, np.uint16)
-    h_sh[: ranks * S] = shards[: ranks * S].view(torch.int16).cpu().numpy().view(np.uint16)
-    h_params = [np.zeros(min(t, ranks * int(lay["R"][p])) * k, np.uint16)
-                for p, (t, k) in enumerate(cfg.shapes)]
-
-    def legs(nthreads):
-        cuts = [round(i * ranks / nthreads) for i in range(nthreads + 1)]
-        slices = [(a, b) for a, b in zip(cuts, cuts[1:]) if b > a]
-
-        def run(fn):
-            ts = []
-            for _ in range(reps):
-                th = [threading.Thread(target=fn, args=sl) for sl in slices]
-                t0 = time.perf_counter()
-                for t in th:
-                    t.start()
-                for t in th:
-                    t.join()
-                ts.append(time.perf_counter() - t0)
-            return statistics.median(ts)
-        t_rs = run(lambda a, b: orc.reduce_scatter(cfg.shapes, N, L, h_grads, rank_range=(a, b),
-                                                   out=h_out))
-        t_ag = run(lambda a, b: orc.allgather_place(cfg.shapes, N, h_sh, rank_range=(a, b),
-                                                    params=h_params))
-        return t_rs, t_ag, len(slices)
-
-    t_rs1, t_ag1, _ = legs(1)
-    gpu_part = out[: ranks * S].cpu().numpy()
-    exact = bool(np.array_equal(gpu_part.view(np.uint32), h_out[: ranks * S].view(np.uint32)))
+    N, L, S, shapes = cfg.N, cfg.L, plan.S, list(cfg.shapes)
+    R = [int(x) for x in orc.layout(shapes, N)["R"]]
     cores = len(os.sched_getaffinity(0))
-    t_rsn, t_agn, used = legs(min(cores, ranks))
-    nbytes = 2 * L * valid + 4 * ranks * S + 4 * valid
-    one = nbytes / (t_rs1 + t_ag1) / 1e9
+    chunk = max(8, min(cores, N))
+    t_rs = t_ag = 0.0
+    used = 1
+    ok_rs = ok_ag = True
+    first_bad = None
+    one = None
+    nbytes = 0
+    for a in range(0, N, chunk):
+        b = min(N, a + chunk)
+        lo = [min(t, a * R[p]) for p, (t, _) in enumerate(shapes)]
+        hi = [min(t, b * R[p]) for p, (t, _) in enumerate(shapes)]
+        h_g = [[grads[c][p].view(-1)[lo[p] * k: hi[p] * k].view(torch.int16).cpu().numpy()
+                .view(np.uint16) for p, (_, k) in enumerate(shapes)] for c in range(L)]
+        h_sh = shards[a * S: b * S].view(torch.int16).cpu().numpy().view(np.uint16)
+        h_out = np.empty((b - a) * S, np.float32)
+        h_par = [np.empty((hi[p] - lo[p]) * k, np.uint16) for p, (_, k) in enumerate(shapes)]
+        valid = sum((hi[p] - lo[p]) * k for p, (_, k) in enumerate(shapes))
+        cbytes = 2 * L * valid + 4 * (b - a) * S + 4 * valid
+        nbytes += cbytes
+
+        def rows_of(arrs, x, y):
+            return [arr[(min(t, x * R[p]) - lo[p]) * k: (min(t, y * R[p]) - lo[p]) * k]
+                    for p, ((t, k), arr) in enumerate(zip(shapes, arrs))]
+
+        def rs(x, y):
+            orc.reduce_scatter_rows(shapes, N, L, [rows_of(h_g[c], x, y) for c in range(L)],
+                                    (x, y), h_out[(x - a) * S: (y - a) * S])
+
+        def ag(x, y):
+            orc.allgather_place_rows(shapes, N, h_sh[(x - a) * S: (y - a) * S], (x, y),
+                                     rows_of(h_par, x, y))
+        if one_thread_reps and a == 0:
+            t1 = [(_run_threads(rs, a, b, 1)[0], _run_threads(ag, a, b, 1)[0])
+                  for _ in range(one_thread_reps)]
+            t1r = statistics.median(x for x, _ in t1)
+            t1a = statistics.median(y for _, y in t1)
+            one = {"ranks": "0-%d" % (b - 1), "reps": one_thread_reps, "reduce_s": round(t1r, 3),
+                   "placement_s": round(t1a, 3), "GBps": round(cbytes / (t1r + t1a) / 1e9, 4)}
+        dt, n = _run_threads(rs, a, b, cores)
+        used = max(used, n)
+        t_rs += dt
+        dt, _ = _run_threads(ag, a, b, cores)
+        t_ag += dt
+        g_out = out[a * S: b * S].cpu().numpy()
+        if not np.array_equal(g_out.view(np.uint32), h_out.view(np.uint32)):
+            ok_rs = False
+            first_bad = first_bad or "reduce-scatter, ranks %d-%d" % (a, b - 1)
+        for p, (_, k) in enumerate(shapes):
+            g_p = params[p].view(-1)[lo[p] * k: hi[p] * k].view(torch.int16).cpu().numpy()
+            if not np.array_equal(g_p.view(np.uint16), h_par[p]):
+                ok_ag = False
+                first_bad = first_bad or "placement, parameter %d, ranks %d-%d" % (p, a, b - 1)
+        del h_g, h_sh, h_out, h_par
+    return {"reduce_scatter_bit_exact": ok_rs, "placement_bit_exact": ok_ag,
+            "first_mismatch": first_bad, "bytes": nbytes, "reduce_s": t_rs, "placement_s": t_ag,
+            "threads": used, "ranks_per_range": chunk, "one_thread": one}
+
+
+def cpu_baseline(chk, cfg):
+    """The oracle timed on the host cores, from an oracle_check run over the
+    whole group (the same bits the GPU used)."""
+    one = chk["one_thread"]
     return {
-        "value": round(nbytes / (t_rsn + t_agn) / 1e9, 4),
+        "value": round(chk["bytes"] / (chk["reduce_s"] + chk["placement_s"]) / 1e9, 4),
         "unit": "GB/s",
-        "cores": used,
+        "cores": chk["threads"],
         "kind": "oracle",
-        "sample": "ranks 0-%d of %d of the same group (all %d params), reduce-scatter + "
-                  "placement, same bits copied from the GPU; median of %d runs: %.2f s reduce + "
-                  "%.2f s placement on %d threads (each calling the unchanged oracle on a slice of "
-                  "the ranks); on one thread %.2f s + %.2f s = %.2f GB/s"
-                  % (ranks - 1, N, len(cfg.shapes), reps, t_rsn, t_agn, used, t_rs1, t_ag1, one),
-        "value_one_thread": round(one, 4),
-        "gpu_shards_bit_exact_on_sample": exact,
+        "sample": "the whole %s group (all %d ranks, %d params): reduce-scatter + placement by the "
+                  "unchanged oracle on %d host threads, one rank slice each, %d ranks at a time, "
+                  "from the same bits the GPU used: %.2f s + %.2f s; one thread on ranks %s: "
+                  "%.2f s + %.2f s = %.2f GB/s (median of %d runs)"
+                  % (cfg.name, cfg.N, len(cfg.shapes), chk["threads"], chk["ranks_per_range"],
+                     chk["reduce_s"], chk["placement_s"], one["ranks"], one["reduce_s"],
+                     one["placement_s"], one["GBps"], one["reps"]),
+        "value_one_thread": one["GBps"],
+        "gpu_shards_bit_exact_on_sample": chk["reduce_scatter_bit_exact"] and chk["placement_bit_exact"],
+        "gpu_reduce_scatter_bit_exact": chk["reduce_scatter_bit_exact"],
+        "gpu_placement_bit_exact": chk["placement_bit_exact"],
         "host": host_info(),
     }
 
@@ -508,19 +548,146 @@ def slot_reuse_parts(torch, tide, plan, cfg, g_tab, out, valid, in_place_ms, ite
             "slot_reuse_over_in_place": round(tot / in_place_ms, 3)}
 
 
+class Group:
+    """One parameter group's inputs and outputs on the GPU, the pointer tables
+    marshalled once (the buffers persist across steps, as FSDP's do)."""
+
+    def __init__(self, torch, tide, cfg):
+        from workloads import device_grads, device_rank_major_bits
+        self.cfg = cfg
+        self.plan = tide.plan_create(cfg.shapes, cfg.N, cfg.L)
+        S = self.plan.S
+        self.grads = device_grads(cfg.shapes, cfg.L, seed=cfg.seed, sigma=cfg.sigma,
+                                  outlier_frac=cfg.outlier_frac,
+                                  progress=lambda c: log("bench: %s: contributor %d of %d drawn"
+                                                         % (cfg.name, c + 1, cfg.L)))
+        self.out = torch.empty(cfg.N * S, dtype=torch.float32, device="cuda")
+        self.shards = device_rank_major_bits(cfg.N * S, seed=1)
+        self.params = [torch.empty((t, k), dtype=torch.bfloat16, device="cuda")
+                       for t, k in cfg.shapes]
+        self.rs_bytes, self.ag_bytes, self.valid = group_bytes(cfg, S)
+        self.g_tab = tide.grads_table(self.plan, self.grads)
+        self.p_tab = tide.params_table(self.plan, self.params)
+        torch.cuda.synchronize()
+
+    def free(self, torch):
+        for name in ("grads", "out", "shards", "params", "g_tab", "p_tab"):
+            setattr(self, name, None)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def time_steps(torch, tide, grp, launch, steps, warmup, engine="kernel"):
+    """`warmup` untimed steps, then `steps` timed ones; one step = reduce-scatter
+    then placement on the current stream. HIP events on that stream bracket
+    each part of each step; the wall clock brackets all timed steps."""
+    stream = torch.cuda.current_stream()
+    plan = grp.plan
+
+    def step(ev):
+        ev[0].record(stream)
+        tide.reduce_scatter_bf16_fp32(plan, grp.g_tab, grp.out, stream=stream, launch=launch)
+        ev[1].record(stream)
+        tide.allgather_place(plan, grp.shards, grp.p_tab, stream=stream, launch=launch,
+                             engine=engine)
+        ev[2].record(stream)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(warmup + steps)]
+    for i in range(warmup):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[warmup + i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    timed = evs[warmup:]
+    rs = [a.elapsed_time(b) for a, b, _ in timed]
+    ag = [b.elapsed_time(c) for _, b, c in timed]
+    st = [a.elapsed_time(c) for a, _, c in timed]
+    tot = grp.rs_bytes + grp.ag_bytes
+    return {
+        "step_ms_median": statistics.median(st), "step_ms_wall_mean": wall,
+        "reduce_ms_mean": statistics.mean(rs), "reduce_ms_median": statistics.median(rs),
+        "reduce_ms_min": min(rs), "placement_ms_mean": statistics.mean(ag),
+        "placement_ms_median": statistics.median(ag),
+        "GBps": tot / (statistics.median(st) / 1e3) / 1e9,
+        "reduce_GBps": grp.rs_bytes / (statistics.median(rs) / 1e3) / 1e9,
+        "reduce_GBps_mean": grp.rs_bytes / (statistics.mean(rs) / 1e3) / 1e9,
+        "placement_GBps": grp.ag_bytes / (statistics.median(ag) / 1e3) / 1e9,
+    }
+
+
+def sdma_placement(torch, tide, grp, reps=3):
+    """Host wall time of the placement on the DMA engines (the call returns
+    once its copies are done; median of `reps` calls)."""
+    tide.allgather_place(grp.plan, grp.shards, grp.p_tab, engine="sdma")
+    ts = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        tide.allgather_place(grp.plan, grp.shards, grp.p_tab, engine="sdma")
+        ts.append(time.perf_counter() - t0)
+    ms = statistics.median(ts) * 1e3
+    return {"ms": round(ms, 3), "GBps": round(grp.ag_bytes / (ms / 1e3) / 1e9, 1),
+            "engines": tide.dma_engine_count(torch.cuda.current_device())}
+
+
+def per_config_line(torch, tide, orc, name, args, gs, cs):
+    """Full-grid step, SDMA placement and the whole-output oracle check of one
+    more group; for the Wan2.2 block also the budgeted GEMM-victim protocol."""
+    from workloads.configs import CONFIGS
+    cfg = CONFIGS[name]
+    log("bench: per-config %s: generating inputs" % name)
+    grp = Group(torch, tide, cfg)
+    t = time_steps(torch, tide, grp, tide.Launch(), args.steps, args.warmup)
+    res = {"GBps": round(t["GBps"], 1), "pct_of_8TBps": round(100.0 * t["GBps"] / HBM_PEAK_GBPS, 2),
+           "step_ms_median": round(t["step_ms_median"], 4),
+           "reduce_GBps": round(t["reduce_GBps"], 1),
+           "reduce_frac_by_mean": round(t["reduce_GBps_mean"] / HBM_PEAK_GBPS, 4),
+           "placement_GBps": round(t["placement_GBps"], 1),
+           "bytes_per_step": grp.rs_bytes + grp.ag_bytes}
+    log("bench: per-config %s: %.1f GB/s fused, reduce %.1f, placement %.1f"
+        % (name, t["GBps"], t["reduce_GBps"], t["placement_GBps"]))
+    res["placement_sdma"] = sdma_placement(torch, tide, grp)
+    if name == "wan22_dit_block":
+        log("bench: per-config %s: GEMM victim" % name)
+        res["victim_gemm_256x8192x8192"] = {
+            "budgeted_16_4": victim_slowdown(torch, tide, grp.plan, grp.grads, grp.out, grp.shards,
+                                             grp.params, tide.budgeted(), gs, cs),
+            "full_grid": victim_slowdown(torch, tide, grp.plan, grp.grads, grp.out, grp.shards,
+                                         grp.params, tide.Launch(), gs, cs)}
+    if orc is not None:
+        # The step's outputs are re-made with the kernel engine before the check.
+        tide.reduce_scatter_bf16_fp32(grp.plan, grp.g_tab, grp.out)
+        tide.allgather_place(grp.plan, grp.shards, grp.p_tab)
+        torch.cuda.synchronize()
+        log("bench: per-config %s: whole output vs the oracle" % name)
+        chk = oracle_check(orc, cfg, grp.plan, grp.grads, grp.out, grp.shards, grp.params)
+        res["oracle_bit_exact"] = chk["reduce_scatter_bit_exact"] and chk["placement_bit_exact"]
+        if chk["first_mismatch"]:
+            res["first_mismatch"] = chk["first_mismatch"]
+    grp.free(torch)
+    log("bench: per-config %s: %s" % (name, json.dumps(res)))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama70b_layer",
+    ap.add_argument("--workload", default="padding_stress",
                     choices=["llama70b_layer", "qwen3_moe_layer", "padding_stress", "wan22_dit_block"])
     ap.add_argument("--mode", default="full", choices=["full", "budgeted"])
+    ap.add_argument("--placement-engine", default="kernel", choices=["kernel", "sdma", "runtime"],
+                    help="engine of the placement in the timed step (default: the kernel)")
     ap.add_argument("--parts", action="store_true",
                     help="also time the runtime-copy placement, the stage placement, the "
                          "landing sum and a plain copy")
     ap.add_argument("--victim", action="store_true",
-                    help="GEMM-victim slowdown, budgeted and full grid")
+                    help="GEMM-victim slowdown of this workload, budgeted and full grid")
     ap.add_argument("--stock", action="store_true",
                     help="also time the stock FSDP2 path (chunk_cat pack + sum, split_with_sizes_copy)")
     ap.add_argument("--slot-reuse", action="store_true",
@@ -529,8 +696,10 @@ def main():
                     help="trace where budgeted workgroups run, beside GEMM-shaped occupants")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step as prepared calls, eager and replayed from a HIP graph")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-ranks", type=int, default=0, help="ranks in the CPU sample (0: all)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle (timing and whole-output checks)")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the other large groups (Llama, Qwen, Wan and the Wan GEMM victim)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -541,71 +710,44 @@ def main():
 
     import torch
     import mixed_precision_rs_amd as tide
-    from workloads import device_grads, device_rank_major_bits
     from workloads.configs import CONFIGS
 
     cfg = CONFIGS[args.workload]
     torch.cuda.set_device(0)
     log("bench: %s, generating inputs" % cfg.name)
-    plan = tide.plan_create(cfg.shapes, cfg.N, cfg.L)
+    grp = Group(torch, tide, cfg)
+    plan, grads, out, shards, params = grp.plan, grp.grads, grp.out, grp.shards, grp.params
+    g_tab, p_tab = grp.g_tab, grp.p_tab
+    rs_bytes, ag_bytes, valid = grp.rs_bytes, grp.ag_bytes, grp.valid
     S = plan.S
-    grads = device_grads(cfg.shapes, cfg.L, seed=cfg.seed, sigma=cfg.sigma,
-                         outlier_frac=cfg.outlier_frac,
-                         progress=lambda c: log("bench: contributor %d of %d drawn" % (c + 1, cfg.L)))
-    out = torch.empty(cfg.N * S, dtype=torch.float32, device="cuda")
-    shards = device_rank_major_bits(cfg.N * S, seed=1)
-    params = [torch.empty((t, k), dtype=torch.bfloat16, device="cuda") for t, k in cfg.shapes]
-    rs_bytes, ag_bytes, valid = group_bytes(cfg, S)
     launch = tide.Launch() if args.mode == "full" else tide.budgeted()
-    stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
 
-    # Device addresses are marshalled once: the gradient and parameter
-    # buffers persist across steps, as FSDP's do.
-    g_tab = tide.grads_table(plan, grads)
-    p_tab = tide.params_table(plan, params)
-
-    def step(ev):
-        ev[0].record(stream)
-        tide.reduce_scatter_bf16_fp32(plan, g_tab, out, stream=stream, launch=launch)
-        ev[1].record(stream)
-        tide.allgather_place(plan, shards, p_tab, stream=stream, launch=launch)
-        ev[2].record(stream)
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-           for _ in range(args.warmup + args.steps)]
-    log("bench: %d warmup steps" % args.warmup)
-    for i in range(args.warmup):
-        step(evs[i])
-    torch.cuda.synchronize()
-    log("bench: %d timed steps" % args.steps)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[args.warmup + i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    timed = evs[args.warmup:]
-    rs_ms = [a.elapsed_time(b) for a, b, _ in timed]
-    ag_ms = [b.elapsed_time(c) for _, b, c in timed]
-    rs_avg, ag_avg = statistics.mean(rs_ms), statistics.mean(ag_ms)
-    value = (rs_bytes + ag_bytes) / (ms_per_step / 1e3) / 1e9
-    achieved = rs_bytes / (rs_avg / 1e3) / 1e9
-    log("bench: %.3f ms/step, %.1f GB/s; reduce %.3f ms (%.1f GB/s), placement %.3f ms (%.1f GB/s)"
-        % (ms_per_step, value, rs_avg, achieved, ag_avg, ag_bytes / (ag_avg / 1e3) / 1e9))
+    log("bench: %d warmup + %d timed steps" % (args.warmup, args.steps))
+    t = time_steps(torch, tide, grp, launch, args.steps, args.warmup, engine=args.placement_engine)
+    value = t["GBps"]
+    achieved = t["reduce_GBps_mean"]
+    rs_avg, ag_avg = t["reduce_ms_mean"], t["placement_ms_mean"]
+    log("bench: %.3f ms/step (median), %.1f GB/s; reduce %.3f ms mean (%.1f GB/s), placement "
+        "%.3f ms mean; wall %.3f ms/step"
+        % (t["step_ms_median"], value, rs_avg, achieved, ag_avg, t["step_ms_wall_mean"]))
 
     parts = {
-        "reduce_ms_mean": round(rs_avg, 4), "reduce_ms_median": round(statistics.median(rs_ms), 4),
-        "reduce_ms_min": round(min(rs_ms), 4),
+        "step_ms_wall_mean": round(t["step_ms_wall_mean"], 4),
+        "GBps_by_wall_mean": round((rs_bytes + ag_bytes) / (t["step_ms_wall_mean"] / 1e3) / 1e9, 1),
+        "reduce_ms_mean": round(rs_avg, 4), "reduce_ms_median": round(t["reduce_ms_median"], 4),
+        "reduce_ms_min": round(t["reduce_ms_min"], 4),
         "placement_ms_mean": round(ag_avg, 4),
-        "placement_ms_median": round(statistics.median(ag_ms), 4),
-        "reduce_GBps": round(achieved, 1),
-        "placement_GBps": round(ag_bytes / (ag_avg / 1e3) / 1e9, 1),
+        "placement_ms_median": round(t["placement_ms_median"], 4),
+        "reduce_GBps": round(t["reduce_GBps"], 1),
+        "placement_GBps": round(t["placement_GBps"], 1),
         "reduce_bytes": rs_bytes, "placement_bytes": ag_bytes,
         "pct_of_8TBps": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "reduce_launches_per_call": plan.launch_count(0, launch),
         "placement_launches_per_call": plan.launch_count(1, launch),
     }
+    if args.placement_engine != "sdma":
+        parts["placement_sdma"] = sdma_placement(torch, tide, grp)
+        log("bench: SDMA placement %s" % json.dumps(parts["placement_sdma"]))
     if args.parts:
         e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         tide.allgather_place(plan, shards, params, engine="runtime")
@@ -650,17 +792,15 @@ def main():
         parts["placement_runtime_copy_ms"] = round(sd, 4)
         parts["placement_runtime_copy_GBps"] = round(ag_bytes / (sd / 1e3) / 1e9, 1)
         log("bench: runtime-copy placement %.3f ms" % sd)
-    # The practical ceiling: a plain 4 GiB device-to-device copy in the same run.
-    parts["plain_copy_GBps"] = round(copy_ceiling_gbps(torch), 1)
-    log("bench: plain copy %.1f GB/s" % parts["plain_copy_GBps"])
+        # The practical ceiling of a plain 4 GiB device-to-device copy.
+        parts["plain_copy_GBps"] = round(copy_ceiling_gbps(torch), 1)
+        log("bench: plain copy %.1f GB/s" % parts["plain_copy_GBps"])
 
     # Two side streams, created once: a GEMM (or occupant) stream and a
     # collective stream. Reusing them keeps every measurement on the same pair
     # of hardware queues (streams created later may share a queue with an
     # earlier one, which would serialise the two).
-    gs = cs = None
-    if args.occupancy or args.victim:
-        gs, cs = torch.cuda.Stream(), torch.cuda.Stream()
+    gs, cs = torch.cuda.Stream(), torch.cuda.Stream()
     graph = None
     if args.graph:
         log("bench: prepared calls and graph replay")
@@ -700,12 +840,38 @@ def main():
         log("bench: victim %s" % json.dumps(victim))
 
     cpu = None
+    orc = None
     if not args.no_cpu_baseline:
         import oracle
-        ranks = args.cpu_ranks if args.cpu_ranks > 0 else cfg.N
-        log("bench: CPU oracle baseline on ranks 0-%d" % (ranks - 1))
-        cpu = cpu_baseline(oracle.load(), cfg, plan, grads, shards, out, ranks)
+        orc = oracle.load()
+        # The outputs of one full-grid step with the kernel engine are checked.
+        tide.reduce_scatter_bf16_fp32(plan, g_tab, out)
+        tide.allgather_place(plan, shards, p_tab)
+        torch.cuda.synchronize()
+        log("bench: whole output vs the CPU oracle, all %d ranks" % cfg.N)
+        chk = oracle_check(orc, cfg, plan, grads, out, shards, params, one_thread_reps=3)
+        cpu = cpu_baseline(chk, cfg)
+        if chk["first_mismatch"]:
+            cpu["first_mismatch"] = chk["first_mismatch"]
         log("bench: cpu %s" % json.dumps(cpu))
+    del grads, out, shards, params, g_tab, p_tab
+    grp.free(torch)
+
+    per_config = None
+    if not args.no_per_config:
+        per_config = {}
+        for name in ("llama70b_layer", "qwen3_moe_layer", "wan22_dit_block"):
+            if name != cfg.name:
+                per_config[name] = per_config_line(torch, tide, orc, name, args, gs, cs)
+        per_config["all_at_least_70pct"] = all(
+            v["pct_of_8TBps"] >= 70.0 for v in per_config.values() if isinstance(v, dict)) and \
+            100.0 * value / HBM_PEAK_GBPS >= 70.0
+        wv = per_config.get("wan22_dit_block", {}).get("victim_gemm_256x8192x8192")
+        if wv and "slowdown_pct" in wv["budgeted_16_4"]:
+            per_config["wan22_budgeted_gemm_slowdown_pct"] = wv["budgeted_16_4"]["slowdown_pct"]
+        if orc is not None:
+            per_config["all_oracle_bit_exact"] = all(
+                v.get("oracle_bit_exact", False) for v in per_config.values() if isinstance(v, dict))
 
     traffic = counter_traffic(cfg.name)
     clocks = gpu_clocks()
@@ -716,7 +882,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(t["step_ms_median"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -724,7 +890,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "params": len(cfg.shapes), "N": cfg.N, "L": cfg.L,
                    "S": S, "valid_elements": valid, "bytes_per_step": rs_bytes + ag_bytes,
-                   "launch": args.mode, "placement_engine": "kernel",
+                   "launch": args.mode, "placement_engine": args.placement_engine,
+                   "statistic": "median of the per-step times (HIP events on the stream)",
                    "inputs": "bf16 grads %s, seeded on device" % (
                        "N(0,%g)" % cfg.sigma + (" + %g outliers" % cfg.outlier_frac
                                                 if cfg.outlier_frac else ""))},
@@ -733,6 +900,7 @@ def main():
                      "traffic": traffic, "kernel": "reduce_kernel<%d>" % cfg.L},
         "cpu_baseline": cpu,
         "parts": parts,
+        "per_config": per_config,
         "gpu_clocks_after_run": clocks,
     }
     if victim is not None:

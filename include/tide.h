@@ -72,10 +72,18 @@ typedef enum tide_engine {
                                    staging: one hipMemcpyAsync per contributor and
                                    parameter). The runtime runs these as its own blit
                                    kernels, so they occupy compute units too. */
-    TIDE_ENGINE_SDMA = 2        /* the GPU's DMA engines, no compute units
-                                   (hipMemcpyDeviceToDeviceNoCU, one copy per contributor
-                                   and parameter). Staging only: the runtime has no
-                                   compute-unit-free strided copy for the placement. */
+    TIDE_ENGINE_SDMA = 2        /* the GPU's DMA (SDMA) engines through the HSA runtime,
+                                   no compute units: one linear copy per piece (placement:
+                                   per parameter and rank; staging: per contributor and
+                                   parameter), spread over every engine the device offers
+                                   for copies inside its memory (14 on MI355X, about
+                                   60 GB/s each). Host-synchronous: the call waits for the
+                                   work already enqueued on `stream`, runs the copies and
+                                   returns once all have completed; it fails with
+                                   TIDE_ERR_HIP if they have not completed within
+                                   10 s + 1 s per GB copied, and with TIDE_ERR_UNSUPPORTED
+                                   on a capturing stream or a device without such engines.
+                                   Only launch.rank_begin / rank_end apply. */
 } tide_engine;
 
 typedef enum tide_launch_mode {
@@ -201,8 +209,10 @@ tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t*
  * All-gather placement, bf16.
  *   shards: device pointer to N rank-major bf16 shards, shard r at
  *       shards + r * shard_stride (shard_stride >= S), 2-byte aligned. Read only;
- *       the buffer must span (N - 1) * shard_stride + S elements, and nothing
- *       outside the pieces read is accessed.
+ *       the buffer must span (N - 1) * shard_stride + S elements. The kernel
+ *       engine's realigning loads of a piece at 2 mod 4 bytes may also read,
+ *       and discard, the one element before and the one after the piece, always
+ *       inside that span; nothing else outside the pieces is read.
  *   params[p]: device pointer to parameter p's storage, T_p x K_p contiguous,
  *       2-byte aligned (may be NULL when T_p * K_p == 0). Speed: a parameter
  *       is written with 16-byte stores only when params[p] is 16-byte aligned;
@@ -210,9 +220,11 @@ tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t*
  * For every rank r in [rank_begin, rank_end), the true rows of rank r's piece
  * of every parameter are copied bit for bit to rows r * R_p.. of params[p];
  * padded rows are not written, and nothing else in params is touched.
- * engine: TIDE_ENGINE_KERNEL or TIDE_ENGINE_RUNTIME; both write the same bytes
- * (TIDE_ENGINE_SDMA returns UNSUPPORTED). The parameters must not overlap
- * each other or the shards read.
+ * engine: TIDE_ENGINE_KERNEL (this library's kernel; asynchronous on `stream`),
+ * TIDE_ENGINE_RUNTIME (one hipMemcpy2DAsync per parameter; asynchronous) or
+ * TIDE_ENGINE_SDMA (one DMA-engine copy per piece, no compute units;
+ * host-synchronous, see tide_engine). All three write the same bytes. The
+ * parameters must not overlap each other or the shards read.
  */
 tide_status tide_allgather_place(const tide_plan* plan, const uint16_t* shards,
                                  int64_t shard_stride, uint16_t* const* params, void* stream,
@@ -246,13 +258,14 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* st
  *           parameters. Parameter p goes to slots[c] + N * o_p, its place in the
  *           group's parameter-major padded layout (tide_plan_map's param_major
  *           at rank 0), rows in order; the padding rows after it are not
- *           written. Pass grads'[c * P + p] = slots[c] + N * o_p to the reduce.
+ *           written. The reduce then reads the table tide_plan_slot_grads
+ *           builds (grads'[c * P + p] = slots[c] + N * o_p).
  *   engine: TIDE_ENGINE_KERNEL: one copy kernel for all (c, p), 16-byte
  *           accesses when every pointer of a parameter is 4-byte aligned;
  *           TIDE_ENGINE_RUNTIME: one hipMemcpyAsync per (c, p);
- *           TIDE_ENGINE_SDMA: the same copies on the DMA engines, leaving the
- *           compute units free (on MI355X about 60 GB/s on one stream, some
- *           100x slower than the kernel: the local copy belongs on the CUs).
+ *           TIDE_ENGINE_SDMA: the same copies on the DMA engines, spread over
+ *           all of them, leaving the compute units free; host-synchronous
+ *           (see tide_engine).
  *   launch: rank_begin / rank_end restrict the copy to those ranks' rows (rank r
  *           holds rows [r R_p, (r + 1) R_p)), so staging and the reduce can be
  *           pipelined by rank range; FULL, or BUDGETED with place_blocks
@@ -269,6 +282,23 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* st
 tide_status tide_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* grads,
                                   uint16_t* const* slots, void* stream, int32_t engine,
                                   const tide_launch* launch);
+
+/*
+ * The reduce-scatter's gradient table for gradients staged into slots by
+ * tide_stage_grads_bf16: grads[c * P + p] = slots[c] + N * o_p (L * P entries,
+ * a caller array). slots: L device pointers. Host-only; no pointer is
+ * dereferenced. Errors: INVALID_ARG (NULL arrays or slot pointers).
+ */
+tide_status tide_plan_slot_grads(const tide_plan* plan, uint16_t* const* slots,
+                                 const uint16_t** grads);
+
+/*
+ * DMA engines TIDE_ENGINE_SDMA spreads its copies over on HIP device `device`
+ * (queried from the HSA runtime on first use, then cached). Host-only.
+ * Errors: INVALID_ARG (not a device), UNSUPPORTED (no such engines, or the HSA
+ * agent of the device cannot be identified).
+ */
+tide_status tide_dma_engine_count(int32_t device, int32_t* engines);
 
 /*
  * Prepared calls. A training step issues the same collectives on the same

@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     counted,
     decode_trace,
     diag_occupy,
+    dma_engine_count,
     grads_table,
     landing_sum_fp32,
     landing_trace_records,

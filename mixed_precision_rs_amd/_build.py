@@ -7,8 +7,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtide.so")
-SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "plan.cpp")]
-HEADERS = [os.path.join(CSRC, "tide_internal.hpp"), os.path.join(ROOT, "include", "tide.h")]
+SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "plan.cpp"),
+           os.path.join(CSRC, "sdma.cpp")]
+HEADERS = [os.path.join(CSRC, "tide_internal.hpp"), os.path.join(CSRC, "sdma.hpp"),
+           os.path.join(ROOT, "include", "tide.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -42,7 +44,9 @@ def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
             raise RuntimeError("hipcc failed for %s:\n%s%s" % (src, r.stdout, r.stderr))
         objs.append(obj)
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    # The DMA-engine path calls the HSA runtime directly.
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs,
+           "-L/opt/rocm/lib", "-lhsa-runtime64"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s%s" % (r.stdout, r.stderr))

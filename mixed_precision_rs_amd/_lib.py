@@ -34,7 +34,8 @@ EXPORTS = ["tide_plan_create", "tide_plan_destroy", "tide_plan_dims", "tide_plan
            "tide_plan_trace_records", "tide_landing_trace_records", "tide_diag_occupy",
            "tide_plan_event_count", "tide_prepare_reduce_scatter_bf16_fp32",
            "tide_prepare_allgather_place_stage", "tide_prepare_stage_grads_bf16",
-           "tide_call_enqueue", "tide_call_destroy"]
+           "tide_call_enqueue", "tide_call_destroy", "tide_plan_slot_grads",
+           "tide_dma_engine_count"]
 
 
 class TideError(RuntimeError):
@@ -180,6 +181,8 @@ def _load():
     lib.tide_call_destroy.restype = None
     lib.tide_diag_occupy.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.tide_plan_slot_grads.argtypes = [ctypes.c_void_p, _VPP, _VPP]
+    lib.tide_dma_engine_count.argtypes = [ctypes.c_int32, _I32P]
     lib.tide_status_string.argtypes = [ctypes.c_int]
     lib.tide_status_string.restype = ctypes.c_char_p
     lib.tide_last_error_detail.argtypes = []
@@ -192,7 +195,8 @@ def _load():
               "tide_latin_square", "tide_stage_grads_bf16", "tide_plan_trace_records",
               "tide_landing_trace_records", "tide_diag_occupy", "tide_plan_event_count",
               "tide_prepare_reduce_scatter_bf16_fp32", "tide_prepare_allgather_place_stage",
-              "tide_prepare_stage_grads_bf16", "tide_call_enqueue"):
+              "tide_prepare_stage_grads_bf16", "tide_call_enqueue", "tide_plan_slot_grads",
+              "tide_dma_engine_count"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -481,13 +485,23 @@ def _slots_arg(plan: Plan, slots: Sequence[object]) -> None:
 
 
 def slot_grads_table(plan: Plan, slots: Sequence[object]) -> PointerTable:
-    """The reduce's L*P gradient table reading the staged slots: entry c*P + p
-    is slots[c] + N * o_p (addresses; keeps the slot tensors alive)."""
+    """The reduce's L*P gradient table reading the staged slots, as
+    tide_plan_slot_grads builds it (keeps the slot tensors alive)."""
     _slots_arg(plan, slots)
-    offs = [plan.N * plan.param(p)[4] * 2 for p in range(plan.P)]
-    tab = PointerTable([_ptr(slots[c]) + offs[p] for c in range(plan.L) for p in range(plan.P)])
-    tab.refs = list(slots)
+    sa = (ctypes.c_void_p * plan.L)(*[_ptr(t) for t in slots])
+    n = plan.L * plan.P
+    arr = (ctypes.c_void_p * max(n, 1))()
+    _check(_load().tide_plan_slot_grads(plan.handle, sa, arr), "tide_plan_slot_grads")
+    tab = PointerTable([])
+    tab.refs, tab.n, tab.arr = list(slots), n, arr
     return tab
+
+
+def dma_engine_count(device: int = 0) -> int:
+    """DMA engines the SDMA engine path spreads its copies over (tide_dma_engine_count)."""
+    n = ctypes.c_int32()
+    _check(_load().tide_dma_engine_count(int(device), ctypes.byref(n)), "tide_dma_engine_count")
+    return int(n.value)
 
 
 class Call:

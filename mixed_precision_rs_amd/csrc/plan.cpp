@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "tide.h"
+#include "sdma.hpp"
 #include "tide_internal.hpp"
 
 using namespace tide;
@@ -561,6 +562,45 @@ tide_status refuse_capture(hipStream_t stream) {
     return TIDE_OK;
 }
 
+// The DMA-engine path waits on the host for the stream and for its copies, so
+// it cannot be recorded into a graph.
+tide_status refuse_capture_dma(hipStream_t stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    TIDE_HIP_TRY(hipStreamIsCapturing(stream, &cs));
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(TIDE_ERR_UNSUPPORTED,
+                    "the stream is capturing a graph; the DMA-engine path waits on the host and "
+                    "cannot be captured (capture the kernel engine's prepared call instead)");
+    return TIDE_OK;
+}
+
+// Run linear copies on the DMA engines of the stream's device (host-synchronous).
+tide_status run_dma(hipStream_t stream, const std::vector<DmaCopy>& copies) {
+    tide_status st = refuse_capture_dma(stream);
+    if (st != TIDE_OK) return st;
+    int dev;
+    st = stream_device(stream, &dev);
+    if (st != TIDE_OK) return st;
+    std::string err;
+    st = dma_copies(dev, stream, copies, nullptr, &err);
+    if (st != TIDE_OK) return fail(st, "%s", err.c_str());
+    return TIDE_OK;
+}
+
+// Append a copy, merging it into the previous one when both sides continue it.
+void add_copy(std::vector<DmaCopy>& v, void* dst, const void* src, uint64_t bytes) {
+    if (bytes == 0) return;
+    if (!v.empty()) {
+        DmaCopy& b = v.back();
+        if (static_cast<char*>(b.dst) + b.bytes == dst &&
+            static_cast<const char*>(b.src) + b.bytes == src) {
+            b.bytes += bytes;
+            return;
+        }
+    }
+    v.push_back(DmaCopy{dst, src, bytes});
+}
+
 // A counted call needs `need` entries; checked before anything is enqueued.
 tide_status check_counts(const tide_launch& l, int64_t need) {
     if (l.write_counts && l.write_counts_elems < need)
@@ -771,9 +811,6 @@ tide_status prep_place(const tide_plan* plan, const uint16_t* shards, int64_t sh
         engine != TIDE_ENGINE_SDMA)
         return fail(TIDE_ERR_INVALID_ARG, "engine %d is not KERNEL (0), RUNTIME (1) or SDMA (2)",
                     engine);
-    if (engine == TIDE_ENGINE_SDMA)
-        return fail(TIDE_ERR_UNSUPPORTED,
-                    "the placement has no DMA-engine path (no compute-unit-free strided copy)");
     if (l.write_counts && engine != TIDE_ENGINE_KERNEL)
         return fail(TIDE_ERR_INVALID_ARG, "write counts need the kernel engine");
     st = check_counts(l, (int64_t)plan->N * plan->S);
@@ -1102,6 +1139,26 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* sh
             }
             return TIDE_OK;
         }
+        if (engine == TIDE_ENGINE_SDMA) {
+            // One linear copy per (parameter, rank) piece: the piece's true
+            // rows, from its place in the (rotated) rank-major buffer to rows
+            // r * R_p.. of the parameter.
+            const tide_launch& l = pr.l;
+            const int64_t N = plan->N;
+            std::vector<DmaCopy> cp;
+            for (int32_t p = 0; p < plan->P; ++p) {
+                const ParamInfo& q = plan->prm[p];
+                if (q.valid == 0) continue;
+                for (int64_t r = l.rank_begin; r < l.rank_end; ++r) {
+                    const int64_t v = std::min(q.s, q.valid - r * q.s);
+                    if (v <= 0) break;
+                    add_copy(cp, params[p] + r * q.s,
+                             shards + ((r - first_rank + N) % N) * shard_stride + q.o,
+                             (uint64_t)v * 2);
+                }
+            }
+            return run_dma(stream, cp);
+        }
         return run_eager(plan, pr, stream);
     } catch (const std::bad_alloc&) {
         return fail(TIDE_ERR_NO_MEMORY, "host allocation failed");
@@ -1121,22 +1178,29 @@ tide_status tide_stage_grads_bf16(const tide_plan* plan, const uint16_t* const* 
         if (engine != TIDE_ENGINE_KERNEL) {
             // One contiguous copy per (contributor, parameter): the rows of
             // ranks [rank_begin, rank_end) are one run on both sides.
-            const hipMemcpyKind kind = engine == TIDE_ENGINE_SDMA ? hipMemcpyDeviceToDeviceNoCU
-                                                                   : hipMemcpyDeviceToDevice;
             const int32_t P = plan->P, L = plan->L;
             const size_t np = (size_t)P * L;
             const uint16_t* const* ts = reinterpret_cast<const uint16_t* const*>(pr.table.data());
             uint16_t* const* td =
                 reinterpret_cast<uint16_t* const*>(pr.table.data() + np * sizeof(void*));
+            std::vector<DmaCopy> cp;
             for (int32_t p = 0; p < P; ++p) {
                 const ParamInfo& q = plan->prm[p];
                 const int64_t lo = (int64_t)pr.l.rank_begin * q.s;
                 const int64_t hi = std::min((int64_t)pr.l.rank_end * q.s, q.valid);
                 if (hi <= lo) continue;
-                for (int32_t c = 0; c < L; ++c)
-                    TIDE_HIP_TRY(hipMemcpyAsync(td[(size_t)p * L + c] + lo, ts[(size_t)p * L + c] + lo,
-                                                (size_t)(hi - lo) * 2, kind, stream));
+                for (int32_t c = 0; c < L; ++c) {
+                    if (engine == TIDE_ENGINE_SDMA)
+                        add_copy(cp, td[(size_t)p * L + c] + lo, ts[(size_t)p * L + c] + lo,
+                                 (uint64_t)(hi - lo) * 2);
+                    else
+                        TIDE_HIP_TRY(hipMemcpyAsync(td[(size_t)p * L + c] + lo,
+                                                    ts[(size_t)p * L + c] + lo,
+                                                    (size_t)(hi - lo) * 2,
+                                                    hipMemcpyDeviceToDevice, stream));
+                }
             }
+            if (engine == TIDE_ENGINE_SDMA) return run_dma(stream, cp);
             return TIDE_OK;
         }
         return run_eager(plan, pr, stream);
@@ -1439,6 +1503,31 @@ const char* tide_status_string(tide_status s) {
 const char* tide_last_error_detail(void) { return g_detail.c_str(); }
 
 int32_t tide_version(void) { return (1 << 16) | 0; }
+
+tide_status tide_plan_slot_grads(const tide_plan* plan, uint16_t* const* slots,
+                                 const uint16_t** grads) {
+    if (!plan || !grads) return fail(TIDE_ERR_INVALID_ARG, "NULL argument");
+    if (plan->P > 0 && !slots) return fail(TIDE_ERR_INVALID_ARG, "slots is NULL");
+    for (int32_t c = 0; c < plan->L && plan->P > 0; ++c) {
+        if (!slots[c]) return fail(TIDE_ERR_INVALID_ARG, "slots[%d] is NULL", c);
+        for (int32_t p = 0; p < plan->P; ++p)
+            grads[(size_t)c * plan->P + p] = slots[c] + (int64_t)plan->N * plan->prm[p].o;
+    }
+    return TIDE_OK;
+}
+
+tide_status tide_dma_engine_count(int32_t device, int32_t* engines) {
+    if (!engines) return fail(TIDE_ERR_INVALID_ARG, "engines is NULL");
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n)
+        return fail(TIDE_ERR_INVALID_ARG, "device %d is not a HIP device", device);
+    std::string err;
+    int e = 0;
+    tide_status st = dma_engine_count(device, &e, &err);
+    if (st != TIDE_OK) return fail(st, "%s", err.c_str());
+    *engines = e;
+    return TIDE_OK;
+}
 
 tide_status tide_plan_event_count(const tide_plan* plan, int64_t* events) {
     if (!plan || !events) return fail(TIDE_ERR_INVALID_ARG, "NULL argument");

@@ -156,8 +156,13 @@ def test_compute_calls_validate_before_enqueue(tide):
         "TIDE_ERR_INVALID_ARG"
     assert _status(lambda: ag(plan, shards + 1, params, stream=0)) == "TIDE_ERR_ALIGNMENT"
     assert _status(lambda: ag(plan, shards, params, stream=0, engine=5)) == "TIDE_ERR_INVALID_ARG"
-    assert _status(lambda: ag(plan, shards, params, stream=0, engine="sdma")) == \
-        "TIDE_ERR_UNSUPPORTED"                # no compute-unit-free strided copy
+    # The DMA-engine path validates the same way before it touches the GPU;
+    # with valid arguments it needs one (here: TIDE_ERR_HIP, nothing copied).
+    assert _status(lambda: ag(plan, shards, params, stream=0, engine="sdma")) == "TIDE_ERR_HIP"
+    assert _status(lambda: ag(plan, shards, [params[0], params[0], params[2]], stream=0,
+                              engine="sdma")) == "TIDE_ERR_INVALID_ARG"
+    assert _status(lambda: ag(plan, shards + 1, params, stream=0, engine="sdma")) == \
+        "TIDE_ERR_ALIGNMENT"
     assert _status(lambda: ag(plan, shards, [params[0], params[0], params[2]], stream=0)) == \
         "TIDE_ERR_INVALID_ARG"                # two parameters overlap
     assert _status(lambda: ag(plan, shards, [shards + 4, params[1], params[2]], stream=0)) == \
@@ -359,3 +364,24 @@ def test_binding_checks_tensor_arguments(tide):
         tide.counted(tide.Launch(), torch.zeros(8, dtype=torch.int64))
     with pytest.raises(ValueError, match="at least 33"):
         tide.diag_occupy(11, 64, 0, 10, buf, stream=0)
+
+
+def test_slot_grads_table(tide):
+    """tide_plan_slot_grads: entry c * P + p is slots[c] + N * o_p (bytes: 2 per element)."""
+    shapes = [(8, 4), (4, 4), (12, 4), (3, 5)]
+    N, L = 4, 3
+    plan = tide.plan_create(shapes, N, L)
+    slots = [FAKE + 0x10000000 * c for c in range(L)]
+    lib = tide.lib()
+    import ctypes
+    sa = (ctypes.c_void_p * L)(*slots)
+    arr = (ctypes.c_void_p * (L * plan.P))()
+    assert lib.tide_plan_slot_grads(plan.handle, sa, arr) == 0
+    o = [plan.param(p)[4] for p in range(plan.P)]
+    assert o == [0, 2 * 4, 3 * 4, 6 * 4]          # R_p * K_p prefix: 2, 1, 3 rows of 4
+    for c in range(L):
+        for p in range(plan.P):
+            assert arr[c * plan.P + p] == slots[c] + N * o[p] * 2
+    sa[1] = None
+    assert lib.tide_plan_slot_grads(plan.handle, sa, arr) == 1      # INVALID_ARG
+
