@@ -206,6 +206,33 @@ tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t*
                                           const tide_launch* launch);
 
 /*
+ * The level-1 reduce-scatter of tide_reduce_scatter_bf16_fp32, for callers
+ * that cannot allocate device memory (code under graph capture, tight serving
+ * loops, harnesses that forbid allocation): it calls no hipMalloc, hipFree or
+ * other allocating routine, on any call. Same arguments, checks and result,
+ * bit for bit, as tide_reduce_scatter_bf16_fp32 (sharing its kernel).
+ *   - Its per-call tables (per-parameter layout, the tile prefix, the L * P
+ *     gradient pointers and flags) live in a fixed 1 MiB device array of the
+ *     library, one per GPU, held until the process ends. A group whose tables
+ *     need more (about P * (44 + 8 L) bytes) is refused with
+ *     TIDE_ERR_INVALID_ARG before anything is enqueued.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's tables: calls that overlap on one GPU (different streams, or
+ *     different host threads with no ordering between them) race. Calls
+ *     ordered on one stream do not.
+ *   - The tables are uploaded with a host-to-device copy on `stream` from
+ *     pageable memory, which the runtime performs synchronously; the upload
+ *     is skipped when they equal what the array already holds.
+ *   - Tiles are walked in parameter order (the eager call groups small pieces
+ *     rank by rank), so small-piece groups may run a little slower.
+ *   - A capturing stream is refused (TIDE_ERR_UNSUPPORTED).
+ */
+tide_status tide_reduce_scatter_bf16_fp32_noalloc(const tide_plan* plan,
+                                                  const uint16_t* const* grads, float* out,
+                                                  int64_t out_stride, void* stream,
+                                                  const tide_launch* launch);
+
+/*
  * All-gather placement, bf16.
  *   shards: device pointer to N rank-major bf16 shards, shard r at
  *       shards + r * shard_stride (shard_stride >= S), 2-byte aligned. Read only;

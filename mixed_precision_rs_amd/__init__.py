@@ -38,6 +38,7 @@ from ._lib import (  # noqa: F401
     prepare_stage_grads_bf16,
     rd_schedule,
     reduce_scatter_bf16_fp32,
+    reduce_scatter_bf16_fp32_noalloc,
     slot_grads_table,
     stage_grads_bf16,
     trace_buffer,

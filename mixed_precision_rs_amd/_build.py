@@ -8,7 +8,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtide.so")
 SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "plan.cpp"),
-           os.path.join(CSRC, "sdma.cpp")]
+           os.path.join(CSRC, "sdma.cpp"), os.path.join(CSRC, "noalloc.hip")]
 HEADERS = [os.path.join(CSRC, "tide_internal.hpp"), os.path.join(CSRC, "sdma.hpp"),
            os.path.join(ROOT, "include", "tide.h")]
 

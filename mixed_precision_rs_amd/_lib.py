@@ -35,7 +35,7 @@ EXPORTS = ["tide_plan_create", "tide_plan_destroy", "tide_plan_dims", "tide_plan
            "tide_plan_event_count", "tide_prepare_reduce_scatter_bf16_fp32",
            "tide_prepare_allgather_place_stage", "tide_prepare_stage_grads_bf16",
            "tide_call_enqueue", "tide_call_destroy", "tide_plan_slot_grads",
-           "tide_dma_engine_count"]
+           "tide_dma_engine_count", "tide_reduce_scatter_bf16_fp32_noalloc"]
 
 
 class TideError(RuntimeError):
@@ -182,6 +182,9 @@ def _load():
     lib.tide_diag_occupy.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     lib.tide_plan_slot_grads.argtypes = [ctypes.c_void_p, _VPP, _VPP]
+    lib.tide_reduce_scatter_bf16_fp32_noalloc.argtypes = [ctypes.c_void_p, _VPP, ctypes.c_void_p,
+                                                          ctypes.c_int64, ctypes.c_void_p,
+                                                          ctypes.POINTER(Launch)]
     lib.tide_dma_engine_count.argtypes = [ctypes.c_int32, _I32P]
     lib.tide_status_string.argtypes = [ctypes.c_int]
     lib.tide_status_string.restype = ctypes.c_char_p
@@ -196,7 +199,7 @@ def _load():
               "tide_landing_trace_records", "tide_diag_occupy", "tide_plan_event_count",
               "tide_prepare_reduce_scatter_bf16_fp32", "tide_prepare_allgather_place_stage",
               "tide_prepare_stage_grads_bf16", "tide_call_enqueue", "tide_plan_slot_grads",
-              "tide_dma_engine_count"):
+              "tide_dma_engine_count", "tide_reduce_scatter_bf16_fp32_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -412,6 +415,25 @@ def reduce_scatter_bf16_fp32(plan: Plan, grads: Sequence[Sequence[object]], out,
         ctypes.byref(launch) if launch is not None else None)
     _check(st, "tide_reduce_scatter_bf16_fp32")
     _record(flat + [out], sobj)
+
+
+def reduce_scatter_bf16_fp32_noalloc(plan: Plan, grads: Sequence[Sequence[object]], out,
+                                     out_stride: Optional[int] = None, stream=None,
+                                     launch: Optional[Launch] = None) -> None:
+    """reduce_scatter_bf16_fp32 through the entry point that allocates no
+    device memory (tide_reduce_scatter_bf16_fp32_noalloc). The binding only
+    marshals; tensors passed in were allocated by the caller beforehand."""
+    tab = grads if isinstance(grads, PointerTable) else grads_table(plan, grads)
+    if tab.n != plan.L * plan.P:
+        raise ValueError("pointer table holds %d entries, expected L*P=%d" % (tab.n, plan.L * plan.P))
+    stride = plan.S if out_stride is None else int(out_stride)
+    _tensor_arg(out, "float32", "out", min_numel=_shards_elems(plan, stride))
+    sh, sobj = _stream_handle(stream)
+    st = _load().tide_reduce_scatter_bf16_fp32_noalloc(
+        plan.handle, tab.arr, _ptr(out), stride, sh,
+        ctypes.byref(launch) if launch is not None else None)
+    _check(st, "tide_reduce_scatter_bf16_fp32_noalloc")
+    _record(tab.refs + [out], sobj)
 
 
 def allgather_place(plan: Plan, shards, params: Sequence[object],

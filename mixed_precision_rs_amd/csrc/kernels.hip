@@ -222,6 +222,31 @@ __device__ __forceinline__ void trace_end(tide_trace_rec* trace, int64_t base, u
     }
 }
 
+// The tile record of reduce tile t when no tile table exists (the
+// allocation-free entry point): `hdr` = {P, cum[0..P]}, cum[p] the reduce
+// tiles of the parameters before p over the launch's rank range, in
+// parameter order. Tile t belongs to the last parameter p with cum[p] <= t
+// and starts kTile * (t - cum[p]) past the vector-aligned start of that
+// parameter's range: the records a tile table would hold, in parameter order.
+template <int64_t kTile>
+__device__ __forceinline__ TileRec derive_tile(const int64_t* __restrict__ hdr,
+                                               const ParamDev* __restrict__ params, int32_t rb,
+                                               int64_t t) {
+    const int64_t* cum = hdr + 1;
+    int64_t lo = 0, hi = hdr[0];
+    while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (cum[mid] <= t) lo = mid; else hi = mid;
+    }
+    const int64_t s = params[lo].s;
+    const int64_t first = (int64_t)rb * s;
+    TileRec r;
+    r.idx0 = first - first % kVec + (t - cum[lo]) * kTile;
+    r.p = (int32_t)lo;
+    r.r0 = (int32_t)(r.idx0 / s);
+    return r;
+}
+
 // Misaligned destinations through LDS (see the reduce's interior path).
 #ifndef TIDE_RS_LDS_ALIGN
 #define TIDE_RS_LDS_ALIGN 1
@@ -231,7 +256,7 @@ __device__ __forceinline__ void trace_end(tide_trace_rec* trace, int64_t base, u
 // LT > 0: L known at compile time (fully unrolled); LT == 0: runtime L.
 // A workgroup of NT threads is NT / kThreads independent quarters of kThreads
 // threads; each quarter walks its own tiles (no barrier between quarters).
-template <int LT, int NT, bool CNT>
+template <int LT, int NT, bool CNT, bool DERIVED = false>
 __global__ __launch_bounds__(NT) void reduce_kernel(
     const TileRec* __restrict__ tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb, int32_t re,
     const ParamDev* __restrict__ params, const uint16_t* const* __restrict__ ptrs,
@@ -256,9 +281,13 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
     const bool one_each = kSubs == 1 && (int64_t)gridDim.x == tile_hi - tile_lo;
     for (int64_t t = tile_lo + (int64_t)blockIdx.x * kSubs + sub; t < tile_hi;
          t += (int64_t)gridDim.x * kSubs) {
-        const TileRec rec =
-            tiles[one_each ? tile_lo + xcd_tile<TIDE_XCD_CHUNK_RS>(t - tile_lo, tile_hi - tile_lo)
-                           : t];
+        const int64_t ti =
+            one_each ? tile_lo + xcd_tile<TIDE_XCD_CHUNK_RS>(t - tile_lo, tile_hi - tile_lo) : t;
+        TileRec rec;
+        if constexpr (DERIVED)
+            rec = derive_tile<kTileR>(reinterpret_cast<const int64_t*>(tiles), params, rb, ti);
+        else
+            rec = tiles[ti];
         const ParamDev pd = params[rec.p];
         const uint16_t* const* g = ptrs + (int64_t)rec.p * L;
         const bool vec = (flags[rec.p] & kFlagVector) != 0;
@@ -807,7 +836,7 @@ hipError_t launch_landing_t(int M, int grid, int threads, size_t lds, hipStream_
     return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, lds, stream);
 }
 
-template <int LT>
+template <int LT, bool DERIVED>
 hipError_t launch_reduce_t(int L, int grid, int threads, size_t lds, hipStream_t stream,
                            const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                            int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
@@ -818,26 +847,25 @@ hipError_t launch_reduce_t(int L, int grid, int threads, size_t lds, hipStream_t
     // Counted calls (debug) take the runtime-L kernel with counting compiled in.
     const void* fn =
         counts ? (threads == kFatThreads
-                      ? reinterpret_cast<const void*>(&reduce_kernel<0, kFatThreads, true>)
-                      : reinterpret_cast<const void*>(&reduce_kernel<0, kThreads, true>))
+                      ? reinterpret_cast<const void*>(&reduce_kernel<0, kFatThreads, true, DERIVED>)
+                      : reinterpret_cast<const void*>(&reduce_kernel<0, kThreads, true, DERIVED>))
                : (threads == kFatThreads
-                      ? reinterpret_cast<const void*>(&reduce_kernel<LT, kFatThreads, false>)
-                      : reinterpret_cast<const void*>(&reduce_kernel<LT, kThreads, false>));
+                      ? reinterpret_cast<const void*>(&reduce_kernel<LT, kFatThreads, false, DERIVED>)
+                      : reinterpret_cast<const void*>(&reduce_kernel<LT, kThreads, false, DERIVED>));
     return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, lds, stream);
 }
 
-}  // namespace
-
-hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t stream,
-                         const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
-                         int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
-                         const uint32_t* flags, float* out, int64_t out_stride,
-                         tide_trace_rec* trace, int64_t trace_base, uint32_t* counts) {
+template <bool DERIVED>
+hipError_t launch_reduce_l(int L, int grid, int threads, size_t lds, hipStream_t stream,
+                           const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
+                           int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
+                           const uint32_t* flags, float* out, int64_t out_stride,
+                           tide_trace_rec* trace, int64_t trace_base, uint32_t* counts) {
 #define TIDE_REDUCE_CASE(n)                                                                   \
     case n:                                                                                   \
-        return launch_reduce_t<n>(L, grid, threads, lds, stream, tiles, tile_lo, tile_hi, rb, \
-                                  re, params, ptrs, flags, out, out_stride, trace, trace_base, \
-                                  counts);
+        return launch_reduce_t<n, DERIVED>(L, grid, threads, lds, stream, tiles, tile_lo,     \
+                                           tile_hi, rb, re, params, ptrs, flags, out,         \
+                                           out_stride, trace, trace_base, counts);
     switch (L) {
         TIDE_REDUCE_CASE(1)
         TIDE_REDUCE_CASE(2)
@@ -848,11 +876,34 @@ hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t s
         TIDE_REDUCE_CASE(7)
         TIDE_REDUCE_CASE(8)
         default:
-            return launch_reduce_t<0>(L, grid, threads, lds, stream, tiles, tile_lo, tile_hi, rb,
-                                      re, params, ptrs, flags, out, out_stride, trace, trace_base,
-                                      counts);
+            return launch_reduce_t<0, DERIVED>(L, grid, threads, lds, stream, tiles, tile_lo,
+                                               tile_hi, rb, re, params, ptrs, flags, out,
+                                               out_stride, trace, trace_base, counts);
     }
 #undef TIDE_REDUCE_CASE
+}
+
+}  // namespace
+
+hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t stream,
+                         const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
+                         int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
+                         const uint32_t* flags, float* out, int64_t out_stride,
+                         tide_trace_rec* trace, int64_t trace_base, uint32_t* counts) {
+    return launch_reduce_l<false>(L, grid, threads, lds, stream, tiles, tile_lo, tile_hi, rb, re,
+                                  params, ptrs, flags, out, out_stride, trace, trace_base, counts);
+}
+
+hipError_t launch_reduce_derived(int L, int grid, int threads, size_t lds, hipStream_t stream,
+                                 const int64_t* tile_prefix, int64_t tile_lo, int64_t tile_hi,
+                                 int32_t rb, int32_t re, const ParamDev* params,
+                                 const uint16_t* const* ptrs, const uint32_t* flags, float* out,
+                                 int64_t out_stride, tide_trace_rec* trace, int64_t trace_base,
+                                 uint32_t* counts) {
+    return launch_reduce_l<true>(L, grid, threads, lds, stream,
+                                 reinterpret_cast<const TileRec*>(tile_prefix), tile_lo, tile_hi,
+                                 rb, re, params, ptrs, flags, out, out_stride, trace, trace_base,
+                                 counts);
 }
 
 hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
@@ -965,13 +1016,18 @@ hipError_t allow_dynamic_lds(int L, size_t lds) {
                          reinterpret_cast<const void*>(&place_kernel<kFatThreads, true>),
                          reinterpret_cast<const void*>(&stage_kernel<kFatThreads, false>),
                          reinterpret_cast<const void*>(&stage_kernel<kFatThreads, true>),
-                         reinterpret_cast<const void*>(&reduce_kernel<0, kFatThreads, true>)};
+                         reinterpret_cast<const void*>(&reduce_kernel<0, kFatThreads, true>),
+                         reinterpret_cast<const void*>(&reduce_kernel<0, kFatThreads, true, true>)};
     for (const void* f : fns) {
         hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
 #define TIDE_LDS_CASE(n)                                                                      \
     case n: {                                                                                 \
+        hipError_t e = hipFuncSetAttribute(                                                   \
+            reinterpret_cast<const void*>(&reduce_kernel<n, kFatThreads, false, true>),       \
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                            \
+        if (e != hipSuccess) return e;                                                        \
         return hipFuncSetAttribute(reinterpret_cast<const void*>(&reduce_kernel<n, kFatThreads, false>), \
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);     \
     }

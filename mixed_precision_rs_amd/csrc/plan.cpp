@@ -1089,6 +1089,114 @@ tide_status tide_reduce_scatter_bf16_fp32(const tide_plan* plan, const uint16_t*
     }
 }
 
+}  // extern "C"
+
+namespace {
+
+// What the allocation-free reduce-scatter last wrote into each device's
+// scratch, so that an unchanged table is not uploaded again (the upload is
+// from pageable memory, which the runtime performs synchronously).
+std::mutex g_noalloc_mu;
+std::map<int, std::vector<char>> g_noalloc_image;
+bool g_noalloc_lds[64][65] = {};
+
+size_t align_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+tide_status tide_reduce_scatter_bf16_fp32_noalloc(const tide_plan* plan,
+                                                  const uint16_t* const* grads, float* out,
+                                                  int64_t out_stride, void* stream_v,
+                                                  const tide_launch* launch) {
+    try {
+        Prepared pr;
+        tide_status st = prep_reduce(plan, grads, out, out_stride, launch, &pr);
+        if (st != TIDE_OK || pr.empty) return st;
+        const tide_launch& l = pr.l;
+        const int32_t P = plan->P, L = plan->L;
+        const bool fat = l.mode == TIDE_LAUNCH_BUDGETED;
+        // Scratch image: ParamDev[P] | {P, cum[0..P]} | pointers[P * L] | flags[P].
+        const size_t off_hdr = align_up((size_t)P * sizeof(ParamDev), 16);
+        const size_t off_ptrs = align_up(off_hdr + ((size_t)P + 2) * sizeof(int64_t), 16);
+        const size_t off_flags = off_ptrs + (size_t)P * L * sizeof(void*);
+        const size_t total = off_flags + (size_t)P * sizeof(uint32_t);
+        if (total > kScratchBytes)
+            return fail(TIDE_ERR_INVALID_ARG,
+                        "the group's tables need %zu bytes, more than the %zu-byte fixed scratch of "
+                        "the allocation-free reduce-scatter (about P * (44 + 8 L) bytes are needed)",
+                        total, kScratchBytes);
+        std::vector<char> img(total, 0);
+        ParamDev* pd = reinterpret_cast<ParamDev*>(img.data());
+        int64_t* hdr = reinterpret_cast<int64_t*>(img.data() + off_hdr);
+        hdr[0] = P;
+        int64_t* cum = hdr + 1;
+        cum[0] = 0;
+        const int64_t tile = tile_elems(0, fat);
+        for (int32_t p = 0; p < P; ++p) {
+            const ParamInfo& q = plan->prm[p];
+            pd[p].s = q.s;
+            pd[p].o = q.o;
+            pd[p].valid = q.valid;
+            pd[p].pad = 0;
+            int64_t n = 0;
+            if (q.s > 0) {   // the tiles build_tiles makes for this parameter
+                const int64_t lo = (int64_t)l.rank_begin * q.s, hi = (int64_t)l.rank_end * q.s;
+                if (hi > lo) n = (hi - (lo - lo % kVec) + tile - 1) / tile;
+            }
+            cum[p + 1] = cum[p] + n;
+        }
+        std::memcpy(img.data() + off_ptrs, pr.table.data(), pr.table.size());
+        const int64_t ntiles = cum[P];
+        st = check_trace(l, launch_records(plan, 0, l, ntiles));
+        if (st != TIDE_OK) return st;
+        if (ntiles == 0) return TIDE_OK;
+        hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+        st = refuse_capture(stream);
+        if (st != TIDE_OK) return st;
+        int dev;
+        st = stream_device(stream, &dev);
+        if (st != TIDE_OK) return st;
+        if (dev < 0 || dev >= 64) return fail(TIDE_ERR_UNSUPPORTED, "device %d beyond 63", dev);
+        DeviceGuard guard(dev);
+        if (guard.status() != hipSuccess) return hip_fail(guard.status(), "hipSetDevice");
+        void* base = nullptr;
+        TIDE_HIP_TRY(scratch_address(dev, &base));
+        {
+            std::lock_guard<std::mutex> lock(g_noalloc_mu);
+            if (fat) {
+                const int key = L <= 8 ? L : 0;
+                if (!g_noalloc_lds[dev][key]) {
+                    TIDE_HIP_TRY(allow_dynamic_lds(key, kBudgetLds));
+                    g_noalloc_lds[dev][key] = true;
+                }
+            }
+            std::vector<char>& last = g_noalloc_image[dev];
+            if (last != img) {
+                TIDE_HIP_TRY(hipMemcpyAsync(base, img.data(), total, hipMemcpyHostToDevice, stream));
+                last.swap(img);
+            }
+        }
+        const char* b = static_cast<const char*>(base);
+        const ParamDev* dparams = reinterpret_cast<const ParamDev*>(b);
+        const int64_t* dhdr = reinterpret_cast<const int64_t*>(b + off_hdr);
+        const uint16_t* const* dptrs = reinterpret_cast<const uint16_t* const*>(b + off_ptrs);
+        const uint32_t* dflags = reinterpret_cast<const uint32_t*>(b + off_flags);
+        return for_each_launch(plan, 0, l, ntiles,
+                               [&](int grid, int threads, size_t lds, int64_t lo, int64_t hi,
+                                   int64_t tb) {
+            return launch_reduce_derived(L, grid, threads, lds, stream, dhdr, lo, hi, l.rank_begin,
+                                         l.rank_end, dparams, dptrs, dflags, out, out_stride,
+                                         l.trace, tb, l.write_counts);
+        });
+    } catch (const std::bad_alloc&) {
+        return fail(TIDE_ERR_NO_MEMORY, "host allocation failed");
+    } catch (...) {
+        return fail(TIDE_ERR_INVALID_ARG, "unexpected exception");
+    }
+}
+
 tide_status tide_allgather_place(const tide_plan* plan, const uint16_t* shards,
                                  int64_t shard_stride, uint16_t* const* params, void* stream_v,
                                  int32_t engine, const tide_launch* launch) {

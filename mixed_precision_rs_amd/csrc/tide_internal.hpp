@@ -120,6 +120,16 @@ hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t s
                          const uint32_t* flags, float* out, int64_t out_stride,
                          tide_trace_rec* trace, int64_t trace_base, uint32_t* counts);
 
+// The same reduce with no tile table: tile_prefix points at {P, cum[0..P]},
+// cum[p] = reduce tiles of the parameters before p over ranks [rb, re) (the
+// kernel derives each tile's record from it, in parameter order).
+hipError_t launch_reduce_derived(int L, int grid, int threads, size_t lds, hipStream_t stream,
+                                 const int64_t* tile_prefix, int64_t tile_lo, int64_t tile_hi,
+                                 int32_t rb, int32_t re, const ParamDev* params,
+                                 const uint16_t* const* ptrs, const uint32_t* flags, float* out,
+                                 int64_t out_stride, tide_trace_rec* trace, int64_t trace_base,
+                                 uint32_t* counts);
+
 hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
                         const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                         int32_t re, const ParamDev* params, uint16_t* const* ptrs,
@@ -155,6 +165,12 @@ hipError_t launch_landing(int M, int grid, int threads, size_t lds, hipStream_t 
 hipError_t launch_occupy(int grid, int threads, size_t lds, hipStream_t stream, int64_t spin_ticks,
                          tide_trace_rec* trace);
 hipError_t allow_dynamic_lds_landing(int M, size_t lds);
+
+// Bytes of the fixed device scratch the allocation-free reduce-scatter keeps
+// its per-call tables in (noalloc.hip), and its device address on HIP
+// device `dev` (looked up once per device, with that device current).
+constexpr size_t kScratchBytes = (size_t)1 << 20;
+hipError_t scratch_address(int dev, void** out);
 
 // Allow `lds` bytes of dynamic LDS on every kernel variant for L contributors.
 hipError_t allow_dynamic_lds(int L, size_t lds);

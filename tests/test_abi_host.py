@@ -385,3 +385,19 @@ def test_slot_grads_table(tide):
     sa[1] = None
     assert lib.tide_plan_slot_grads(plan.handle, sa, arr) == 1      # INVALID_ARG
 
+
+def test_noalloc_refuses_groups_beyond_its_scratch(tide):
+    """The allocation-free reduce-scatter keeps its tables in a fixed 1 MiB
+    device array: a group that needs more is refused on the host, before
+    anything touches the GPU; a small group passes validation (and then needs
+    a GPU: TIDE_ERR_HIP here)."""
+    big = [(2, 3)] * 3000                           # 3000 * (44 + 8 * 40) bytes > 1 MiB
+    plan = tide.plan_create(big, 2, 40)
+    grads = [[FAKE + 0x100000 * (c * 3000 + p) for p in range(3000)] for c in range(40)]
+    out = FAKE - 0x10000000
+    rs = tide.reduce_scatter_bf16_fp32_noalloc
+    assert _status(lambda: rs(plan, grads, out, stream=0)) == "TIDE_ERR_INVALID_ARG"
+    small = tide.plan_create([(8, 4), (4, 4)], 4, 2)
+    g2 = [[FAKE + 0x100000 * (c * 2 + p) for p in range(2)] for c in range(2)]
+    assert _status(lambda: rs(small, g2, out, stream=0)) == "TIDE_ERR_HIP"
+    assert _status(lambda: rs(small, g2, out + 2, stream=0)) == "TIDE_ERR_ALIGNMENT"
