@@ -157,12 +157,9 @@ __device__ __forceinline__ void store4(const Span& t, const ParamDev& pd, int64_
 // walks runs of C consecutive tiles and a cache line shared by two
 // neighbouring tiles goes through one L2 rather than two. The mapping is a
 // bijection on the first multiple of kXcds * C tiles and the identity on the
-// rest. Measured on MI355X: +2% for the placement (whose bf16 source runs
-// start at arbitrary 2-byte offsets), -2% for the reduce, so only the
-// placement uses it.
-#ifndef TIDE_XCD_CHUNK_RS
-#define TIDE_XCD_CHUNK_RS 0
-#endif
+// rest (C = 1 is the identity). Measured on MI355X: +2% for the placement
+// (whose bf16 source runs start at arbitrary 2-byte offsets); for the reduce
+// the host picks C per call (reduce_xcd_log2 in plan.cpp).
 #ifndef TIDE_XCD_CHUNK_AG
 #define TIDE_XCD_CHUNK_AG 64
 #endif
@@ -174,6 +171,13 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t n) {
     if (b >= full) return b;
     const int64_t xcd = b % kXcds, j = b / kXcds;
     return ((j / C) * kXcds + xcd) * C + j % C;
+}
+// The same with C = 2^lc chosen at run time.
+__device__ __forceinline__ int64_t xcd_tile_rt(int64_t b, int64_t n, int lc) {
+    const int64_t full = n >> (3 + lc) << (3 + lc);
+    if (b >= full) return b;
+    const int64_t xcd = b & (kXcds - 1), j = b >> 3;
+    return ((((j >> lc) << 3) + xcd) << lc) + (j & ((int64_t(1) << lc) - 1));
 }
 
 // Write one wave's run of kHalf fp32 results: lane l holds a[0..3] for flat
@@ -261,7 +265,8 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
     const TileRec* __restrict__ tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb, int32_t re,
     const ParamDev* __restrict__ params, const uint16_t* const* __restrict__ ptrs,
     const uint32_t* __restrict__ flags, int Lrt, float* __restrict__ out, int64_t out_stride,
-    tide_trace_rec* __restrict__ trace, int64_t trace_base, uint32_t* __restrict__ counts) {
+    tide_trace_rec* __restrict__ trace, int64_t trace_base, uint32_t* __restrict__ counts,
+    int32_t xcd_lc) {
     const uint64_t t_begin = trace_begin(trace);
     constexpr int kSubs = NT / kThreads;
     // Budgeted (fat) workgroups walk longer tiles with more loads in flight:
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
     for (int64_t t = tile_lo + (int64_t)blockIdx.x * kSubs + sub; t < tile_hi;
          t += (int64_t)gridDim.x * kSubs) {
         const int64_t ti =
-            one_each ? tile_lo + xcd_tile<TIDE_XCD_CHUNK_RS>(t - tile_lo, tile_hi - tile_lo) : t;
+            one_each ? tile_lo + xcd_tile_rt(t - tile_lo, tile_hi - tile_lo, xcd_lc) : t;
         TileRec rec;
         if constexpr (DERIVED)
             rec = derive_tile<kTileR>(reinterpret_cast<const int64_t*>(tiles), params, rb, ti);
@@ -841,9 +846,10 @@ hipError_t launch_reduce_t(int L, int grid, int threads, size_t lds, hipStream_t
                            const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                            int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
                            const uint32_t* flags, float* out, int64_t out_stride,
-                           tide_trace_rec* trace, int64_t trace_base, uint32_t* counts) {
+                           tide_trace_rec* trace, int64_t trace_base, uint32_t* counts,
+                           int32_t xcd_lc) {
     void* args[] = {&tiles, &tile_lo, &tile_hi, &rb, &re, &params, &ptrs, &flags, &L, &out,
-                    &out_stride, &trace, &trace_base, &counts};
+                    &out_stride, &trace, &trace_base, &counts, &xcd_lc};
     // Counted calls (debug) take the runtime-L kernel with counting compiled in.
     const void* fn =
         counts ? (threads == kFatThreads
@@ -860,12 +866,13 @@ hipError_t launch_reduce_l(int L, int grid, int threads, size_t lds, hipStream_t
                            const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                            int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
                            const uint32_t* flags, float* out, int64_t out_stride,
-                           tide_trace_rec* trace, int64_t trace_base, uint32_t* counts) {
+                           tide_trace_rec* trace, int64_t trace_base, uint32_t* counts,
+                           int32_t xcd_lc) {
 #define TIDE_REDUCE_CASE(n)                                                                   \
     case n:                                                                                   \
         return launch_reduce_t<n, DERIVED>(L, grid, threads, lds, stream, tiles, tile_lo,     \
                                            tile_hi, rb, re, params, ptrs, flags, out,         \
-                                           out_stride, trace, trace_base, counts);
+                                           out_stride, trace, trace_base, counts, xcd_lc);
     switch (L) {
         TIDE_REDUCE_CASE(1)
         TIDE_REDUCE_CASE(2)
@@ -878,7 +885,7 @@ hipError_t launch_reduce_l(int L, int grid, int threads, size_t lds, hipStream_t
         default:
             return launch_reduce_t<0, DERIVED>(L, grid, threads, lds, stream, tiles, tile_lo,
                                                tile_hi, rb, re, params, ptrs, flags, out,
-                                               out_stride, trace, trace_base, counts);
+                                               out_stride, trace, trace_base, counts, xcd_lc);
     }
 #undef TIDE_REDUCE_CASE
 }
@@ -889,9 +896,11 @@ hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t s
                          const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                          int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
                          const uint32_t* flags, float* out, int64_t out_stride,
-                         tide_trace_rec* trace, int64_t trace_base, uint32_t* counts) {
+                         tide_trace_rec* trace, int64_t trace_base, uint32_t* counts,
+                         int32_t xcd_lc) {
     return launch_reduce_l<false>(L, grid, threads, lds, stream, tiles, tile_lo, tile_hi, rb, re,
-                                  params, ptrs, flags, out, out_stride, trace, trace_base, counts);
+                                  params, ptrs, flags, out, out_stride, trace, trace_base, counts,
+                                  xcd_lc);
 }
 
 hipError_t launch_reduce_derived(int L, int grid, int threads, size_t lds, hipStream_t stream,
@@ -899,11 +908,11 @@ hipError_t launch_reduce_derived(int L, int grid, int threads, size_t lds, hipSt
                                  int32_t rb, int32_t re, const ParamDev* params,
                                  const uint16_t* const* ptrs, const uint32_t* flags, float* out,
                                  int64_t out_stride, tide_trace_rec* trace, int64_t trace_base,
-                                 uint32_t* counts) {
+                                 uint32_t* counts, int32_t xcd_lc) {
     return launch_reduce_l<true>(L, grid, threads, lds, stream,
                                  reinterpret_cast<const TileRec*>(tile_prefix), tile_lo, tile_hi,
                                  rb, re, params, ptrs, flags, out, out_stride, trace, trace_base,
-                                 counts);
+                                 counts, xcd_lc);
 }
 
 hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,

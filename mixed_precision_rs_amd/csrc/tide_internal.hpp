@@ -113,12 +113,14 @@ constexpr uint32_t kFlagVector = 1u;  // every pointer of this parameter allows 
 // record per workgroup at trace[trace_base + blockIdx.x]; counts, when not
 // null, gets one added per element written (reduce: at the output offset;
 // placement: at N * o_p + f; staging: at c * N * S + N * o_p + f; landing: at
-// b * S + f). Return the launch's hipError_t.
+// b * S + f). Return the launch's hipError_t. The reduce's full grid hands
+// tiles to the XCDs in runs of 2^xcd_lc (0: round robin, one tile each).
 hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t stream,
                          const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                          int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
                          const uint32_t* flags, float* out, int64_t out_stride,
-                         tide_trace_rec* trace, int64_t trace_base, uint32_t* counts);
+                         tide_trace_rec* trace, int64_t trace_base, uint32_t* counts,
+                         int32_t xcd_lc);
 
 // The same reduce with no tile table: tile_prefix points at {P, cum[0..P]},
 // cum[p] = reduce tiles of the parameters before p over ranks [rb, re) (the
@@ -128,7 +130,7 @@ hipError_t launch_reduce_derived(int L, int grid, int threads, size_t lds, hipSt
                                  int32_t rb, int32_t re, const ParamDev* params,
                                  const uint16_t* const* ptrs, const uint32_t* flags, float* out,
                                  int64_t out_stride, tide_trace_rec* trace, int64_t trace_base,
-                                 uint32_t* counts);
+                                 uint32_t* counts, int32_t xcd_lc);
 
 hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
                         const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
