@@ -185,10 +185,13 @@ tide_status tide_plan_map(const tide_plan* plan, int32_t r, int32_t p, int64_t* 
  * Level-1 reduce-scatter, bf16 in, fp32 out.
  *   grads[c * P + p]: device pointer to contributor c's bf16 gradient of parameter
  *       p, T_p x K_p contiguous, 2-byte aligned (may be NULL when T_p * K_p == 0).
- *       Read only; gradients are read in place, with no packed copy. Speed: a
- *       parameter is read with vector loads when all L of its gradients are
- *       4-byte aligned (separate device allocations are); otherwise it is
- *       summed element by element, with the same result.
+ *       Read only; gradients are read in place, with no packed copy. Speed:
+ *       gradients are read with vector loads; one that starts at 2 mod 4 bytes
+ *       (a view at an odd element offset) with dword-aligned loads and a
+ *       16-bit funnel shift, which also read, and discard, the 2 bytes before
+ *       its first element and after its last that share their aligned dwords.
+ *       A parameter with such a gradient from contributor 24 or later is
+ *       summed element by element. Every path gives the same result.
  *   out: device pointer to N fp32 shards; shard r starts at out + r * out_stride
  *       (out_stride >= S), 4-byte aligned; the buffer must span
  *       (N - 1) * out_stride + S elements.

@@ -34,6 +34,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+typedef uint32_t u32x3_a4 __attribute__((ext_vector_type(3), aligned(4)));
 typedef float f32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 // Pointers read from the per-call table are generic pointers to the compiler;
@@ -260,7 +261,11 @@ __device__ __forceinline__ TileRec derive_tile(const int64_t* __restrict__ hdr,
 // LT > 0: L known at compile time (fully unrolled); LT == 0: runtime L.
 // A workgroup of NT threads is NT / kThreads independent quarters of kThreads
 // threads; each quarter walks its own tiles (no barrier between quarters).
-template <int LT, int NT, bool CNT, bool DERIVED = false>
+// SHIFTED: the variant that also reads gradients starting at 2 mod 4 bytes
+// with vector loads (dword-aligned loads and a funnel shift). Its extra
+// registers would cost the common, all-aligned case a resident wave per SIMD
+// (81 instead of 80 VGPRs), so the host uses it only for calls that need it.
+template <int LT, int NT, bool CNT, bool DERIVED, bool SHIFTED>
 __global__ __launch_bounds__(NT) void reduce_kernel(
     const TileRec* __restrict__ tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb, int32_t re,
     const ParamDev* __restrict__ params, const uint16_t* const* __restrict__ ptrs,
@@ -295,7 +300,9 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
             rec = tiles[ti];
         const ParamDev pd = params[rec.p];
         const uint16_t* const* g = ptrs + (int64_t)rec.p * L;
-        const bool vec = (flags[rec.p] & kFlagVector) != 0;
+        const uint32_t fl = flags[rec.p];
+        const bool vec = (fl & kFlagVector) != 0;
+        const uint32_t odd = SHIFTED ? fl >> kOddShift : 0u;   // contributors at 2 mod 4 bytes
         const Span tr{rec.idx0, rec.idx0 - (int64_t)rec.r0 * pd.s, (int64_t)rb * pd.s,
                       (int64_t)re * pd.s, rec.r0};
         const int64_t end = min(tr.idx0 + kTileR, tr.hi);
@@ -313,13 +320,32 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
                 constexpr int kCUnroll = LT > 0 ? LT : 1;
 #pragma unroll kCUnroll
                 for (int c = 0; c < L; ++c) {
-                    const TIDE_GLOBAL u32x2_a4* gc = gbl<u32x2_a4>(g[c] + fh);
                     u32x2 v[kUR][2];
+                    if (odd & (1u << c)) {
+                        // Contributor c starts at 2 mod 4 bytes: the lane's 4
+                        // elements f..f+3 lie in the 3 dwords from element
+                        // f - 1 (f is a multiple of 4, so f - 1 starts a
+                        // dword); every dword read holds an element of the
+                        // step's valid range, or the one before it, or the
+                        // one after it in the same dword. Wave-uniform.
+                        const TIDE_GLOBAL u32x3_a4* gq = gbl<u32x3_a4>(g[c] + fh - 1);
 #pragma unroll
-                    for (int u = 0; u < kUR; ++u)
+                        for (int u = 0; u < kUR; ++u)
 #pragma unroll
-                        for (int h = 0; h < 2; ++h)
-                            v[u][h] = TIDE_LD(gc + (u * kStep + h * kHalf) / 4);
+                            for (int h = 0; h < 2; ++h) {
+                                const u32x3_a4 w = TIDE_LD(reinterpret_cast<const TIDE_GLOBAL u32x3_a4*>(
+                                    reinterpret_cast<const TIDE_GLOBAL uint16_t*>(gq) + u * kStep + h * kHalf));
+                                v[u][h][0] = __builtin_amdgcn_alignbit(w[1], w[0], 16);
+                                v[u][h][1] = __builtin_amdgcn_alignbit(w[2], w[1], 16);
+                            }
+                    } else {
+                        const TIDE_GLOBAL u32x2_a4* gc = gbl<u32x2_a4>(g[c] + fh);
+#pragma unroll
+                        for (int u = 0; u < kUR; ++u)
+#pragma unroll
+                            for (int h = 0; h < 2; ++h)
+                                v[u][h] = TIDE_LD(gc + (u * kStep + h * kHalf) / 4);
+                    }
 #pragma unroll
                     for (int u = 0; u < kUR; ++u) {
 #pragma unroll
@@ -407,7 +433,7 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
                 for (int u = 0; u < kUR; ++u) {
                     const int64_t fu = f0 + (int64_t)u * kStep;
                     const bool whole = fu >= tr.lo && fu + kVec <= end;
-                    if (whole && vec && fu + kVec <= pd.valid) {
+                    if (whole && vec && odd == 0 && fu + kVec <= pd.valid) {
                         float a[2][4];
                         constexpr int kCUnroll = LT > 0 ? LT : 1;
 #pragma unroll kCUnroll
@@ -841,23 +867,30 @@ hipError_t launch_landing_t(int M, int grid, int threads, size_t lds, hipStream_
     return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, lds, stream);
 }
 
+template <int LT, bool DERIVED, bool SHIFTED>
+const void* reduce_fn(int threads, bool counted) {
+    // Counted calls (debug) take the runtime-L kernel with counting and the
+    // shifted loads compiled in.
+    if (counted)
+        return threads == kFatThreads
+                   ? reinterpret_cast<const void*>(&reduce_kernel<0, kFatThreads, true, DERIVED, true>)
+                   : reinterpret_cast<const void*>(&reduce_kernel<0, kThreads, true, DERIVED, true>);
+    return threads == kFatThreads
+               ? reinterpret_cast<const void*>(&reduce_kernel<LT, kFatThreads, false, DERIVED, SHIFTED>)
+               : reinterpret_cast<const void*>(&reduce_kernel<LT, kThreads, false, DERIVED, SHIFTED>);
+}
+
 template <int LT, bool DERIVED>
 hipError_t launch_reduce_t(int L, int grid, int threads, size_t lds, hipStream_t stream,
                            const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                            int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
                            const uint32_t* flags, float* out, int64_t out_stride,
                            tide_trace_rec* trace, int64_t trace_base, uint32_t* counts,
-                           int32_t xcd_lc) {
+                           int32_t xcd_lc, bool shifted) {
     void* args[] = {&tiles, &tile_lo, &tile_hi, &rb, &re, &params, &ptrs, &flags, &L, &out,
                     &out_stride, &trace, &trace_base, &counts, &xcd_lc};
-    // Counted calls (debug) take the runtime-L kernel with counting compiled in.
-    const void* fn =
-        counts ? (threads == kFatThreads
-                      ? reinterpret_cast<const void*>(&reduce_kernel<0, kFatThreads, true, DERIVED>)
-                      : reinterpret_cast<const void*>(&reduce_kernel<0, kThreads, true, DERIVED>))
-               : (threads == kFatThreads
-                      ? reinterpret_cast<const void*>(&reduce_kernel<LT, kFatThreads, false, DERIVED>)
-                      : reinterpret_cast<const void*>(&reduce_kernel<LT, kThreads, false, DERIVED>));
+    const void* fn = shifted ? reduce_fn<LT, DERIVED, true>(threads, counts != nullptr)
+                             : reduce_fn<LT, DERIVED, false>(threads, counts != nullptr);
     return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, lds, stream);
 }
 
@@ -867,12 +900,13 @@ hipError_t launch_reduce_l(int L, int grid, int threads, size_t lds, hipStream_t
                            int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
                            const uint32_t* flags, float* out, int64_t out_stride,
                            tide_trace_rec* trace, int64_t trace_base, uint32_t* counts,
-                           int32_t xcd_lc) {
+                           int32_t xcd_lc, bool shifted) {
 #define TIDE_REDUCE_CASE(n)                                                                   \
     case n:                                                                                   \
         return launch_reduce_t<n, DERIVED>(L, grid, threads, lds, stream, tiles, tile_lo,     \
                                            tile_hi, rb, re, params, ptrs, flags, out,         \
-                                           out_stride, trace, trace_base, counts, xcd_lc);
+                                           out_stride, trace, trace_base, counts, xcd_lc,     \
+                                           shifted);
     switch (L) {
         TIDE_REDUCE_CASE(1)
         TIDE_REDUCE_CASE(2)
@@ -885,7 +919,8 @@ hipError_t launch_reduce_l(int L, int grid, int threads, size_t lds, hipStream_t
         default:
             return launch_reduce_t<0, DERIVED>(L, grid, threads, lds, stream, tiles, tile_lo,
                                                tile_hi, rb, re, params, ptrs, flags, out,
-                                               out_stride, trace, trace_base, counts, xcd_lc);
+                                               out_stride, trace, trace_base, counts, xcd_lc,
+                                               shifted);
     }
 #undef TIDE_REDUCE_CASE
 }
@@ -897,10 +932,10 @@ hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t s
                          int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
                          const uint32_t* flags, float* out, int64_t out_stride,
                          tide_trace_rec* trace, int64_t trace_base, uint32_t* counts,
-                         int32_t xcd_lc) {
+                         int32_t xcd_lc, bool shifted) {
     return launch_reduce_l<false>(L, grid, threads, lds, stream, tiles, tile_lo, tile_hi, rb, re,
                                   params, ptrs, flags, out, out_stride, trace, trace_base, counts,
-                                  xcd_lc);
+                                  xcd_lc, shifted);
 }
 
 hipError_t launch_reduce_derived(int L, int grid, int threads, size_t lds, hipStream_t stream,
@@ -908,11 +943,11 @@ hipError_t launch_reduce_derived(int L, int grid, int threads, size_t lds, hipSt
                                  int32_t rb, int32_t re, const ParamDev* params,
                                  const uint16_t* const* ptrs, const uint32_t* flags, float* out,
                                  int64_t out_stride, tide_trace_rec* trace, int64_t trace_base,
-                                 uint32_t* counts, int32_t xcd_lc) {
+                                 uint32_t* counts, int32_t xcd_lc, bool shifted) {
     return launch_reduce_l<true>(L, grid, threads, lds, stream,
                                  reinterpret_cast<const TileRec*>(tile_prefix), tile_lo, tile_hi,
                                  rb, re, params, ptrs, flags, out, out_stride, trace, trace_base,
-                                 counts, xcd_lc);
+                                 counts, xcd_lc, shifted);
 }
 
 hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
@@ -1025,20 +1060,25 @@ hipError_t allow_dynamic_lds(int L, size_t lds) {
                          reinterpret_cast<const void*>(&place_kernel<kFatThreads, true>),
                          reinterpret_cast<const void*>(&stage_kernel<kFatThreads, false>),
                          reinterpret_cast<const void*>(&stage_kernel<kFatThreads, true>),
-                         reinterpret_cast<const void*>(&reduce_kernel<0, kFatThreads, true>),
-                         reinterpret_cast<const void*>(&reduce_kernel<0, kFatThreads, true, true>)};
+                         reinterpret_cast<const void*>(&reduce_kernel<0, kFatThreads, true, false, true>),
+                         reinterpret_cast<const void*>(&reduce_kernel<0, kFatThreads, true, true, true>)};
     for (const void* f : fns) {
         hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
 #define TIDE_LDS_CASE(n)                                                                      \
     case n: {                                                                                 \
-        hipError_t e = hipFuncSetAttribute(                                                   \
-            reinterpret_cast<const void*>(&reduce_kernel<n, kFatThreads, false, true>),       \
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                            \
-        if (e != hipSuccess) return e;                                                        \
-        return hipFuncSetAttribute(reinterpret_cast<const void*>(&reduce_kernel<n, kFatThreads, false>), \
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);     \
+        const void* fat[] = {                                                                 \
+            reinterpret_cast<const void*>(&reduce_kernel<n, kFatThreads, false, false, false>), \
+            reinterpret_cast<const void*>(&reduce_kernel<n, kFatThreads, false, false, true>), \
+            reinterpret_cast<const void*>(&reduce_kernel<n, kFatThreads, false, true, false>), \
+            reinterpret_cast<const void*>(&reduce_kernel<n, kFatThreads, false, true, true>)}; \
+        for (const void* f : fat) {                                                           \
+            hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                                               (int)lds);                                     \
+            if (e != hipSuccess) return e;                                                    \
+        }                                                                                     \
+        return hipSuccess;                                                                    \
     }
     switch (L) {
         TIDE_LDS_CASE(1)

@@ -787,6 +787,7 @@ struct Prepared {
     float* out = nullptr;             // op 0
     int64_t out_stride = 0;
     int32_t xcd_lc = 0;               // op 0: full-grid XCD run length (log2)
+    bool shifted = false;             // op 0: some gradient starts at 2 mod 4 bytes
     const uint16_t* shards = nullptr; // op 1
     int64_t shard_stride = 0, shard_elems = 0;
     int32_t first_rank = 0;
@@ -839,7 +840,13 @@ tide_status prep_reduce(const tide_plan* plan, const uint16_t* const* grads, flo
             if (!g) return fail(TIDE_ERR_INVALID_ARG, "grads[%d] (c=%d, p=%d) is NULL", c * P + p, c, p);
             const uintptr_t a = reinterpret_cast<uintptr_t>(g);
             if (a & 1) return fail(TIDE_ERR_ALIGNMENT, "grads[%d] is not 2-byte aligned", c * P + p);
-            if (a & 3) f &= ~kFlagVector;        // multi-dword loads need dword alignment only
+            // Multi-dword loads need dword alignment only; a gradient at 2 mod 4
+            // bytes is read with dword-aligned loads and a funnel shift.
+            if (a & 3) {
+                if (c < kMaxOddShift) f |= 1u << (kOddShift + c);
+                else f &= ~kFlagVector;
+            }
+            if ((f & kFlagVector) && (f >> kOddShift)) pr->shifted = true;
             const Range in{a, a + (uintptr_t)q.valid * 2, c * P + p};
             if (overlaps(in, w))
                 return fail(TIDE_ERR_INVALID_ARG, "grads[%d] overlaps the output", c * P + p);
@@ -1027,7 +1034,7 @@ tide_status launch_prepared(const tide_plan* plan, const Prepared& pr, const Dev
                                    int64_t tb) {
             return launch_reduce(L, grid, threads, lds, stream, tt->dev, lo, hi, l.rank_begin,
                                  l.rank_end, ds->params, dptrs, dflags, pr.out, pr.out_stride,
-                                 l.trace, tb, l.write_counts, pr.xcd_lc);
+                                 l.trace, tb, l.write_counts, pr.xcd_lc, pr.shifted);
         });
     }
     if (pr.op == 1) {
@@ -1240,7 +1247,7 @@ tide_status tide_reduce_scatter_bf16_fp32_noalloc(const tide_plan* plan,
                                    int64_t tb) {
             return launch_reduce_derived(L, grid, threads, lds, stream, dhdr, lo, hi, l.rank_begin,
                                          l.rank_end, dparams, dptrs, dflags, out, out_stride,
-                                         l.trace, tb, l.write_counts, pr.xcd_lc);
+                                         l.trace, tb, l.write_counts, pr.xcd_lc, pr.shifted);
         });
     } catch (const std::bad_alloc&) {
         return fail(TIDE_ERR_NO_MEMORY, "host allocation failed");

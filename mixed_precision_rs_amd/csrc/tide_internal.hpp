@@ -106,6 +106,12 @@ static_assert(sizeof(ParamDev) == 32, "ParamDev layout");
 
 // Per-parameter flag bits of the per-call table.
 constexpr uint32_t kFlagVector = 1u;  // every pointer of this parameter allows 16-byte vector access
+// Reduce only: bit kOddShift + c set when contributor c's gradient starts at
+// 2 mod 4 bytes; the interior steps read it with dword-aligned loads and a
+// 16-bit funnel shift (contributors 0 .. kMaxOddShift - 1; a parameter with a
+// later contributor at 2 mod 4 goes element by element).
+constexpr int kOddShift = 8;
+constexpr int kMaxOddShift = 24;
 
 // Launch wrappers (kernels.hip). threads is kThreads or kFatThreads; lds is
 // dynamic LDS reserved per workgroup (unused by the kernels: it only keeps
@@ -114,13 +120,15 @@ constexpr uint32_t kFlagVector = 1u;  // every pointer of this parameter allows 
 // null, gets one added per element written (reduce: at the output offset;
 // placement: at N * o_p + f; staging: at c * N * S + N * o_p + f; landing: at
 // b * S + f). Return the launch's hipError_t. The reduce's full grid hands
-// tiles to the XCDs in runs of 2^xcd_lc (0: round robin, one tile each).
+// tiles to the XCDs in runs of 2^xcd_lc (0: round robin, one tile each);
+// `shifted` selects the variant that reads gradients at 2 mod 4 bytes with
+// vector loads (needed when any flag word carries kOddShift bits).
 hipError_t launch_reduce(int L, int grid, int threads, size_t lds, hipStream_t stream,
                          const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,
                          int32_t re, const ParamDev* params, const uint16_t* const* ptrs,
                          const uint32_t* flags, float* out, int64_t out_stride,
                          tide_trace_rec* trace, int64_t trace_base, uint32_t* counts,
-                         int32_t xcd_lc);
+                         int32_t xcd_lc, bool shifted);
 
 // The same reduce with no tile table: tile_prefix points at {P, cum[0..P]},
 // cum[p] = reduce tiles of the parameters before p over ranks [rb, re) (the
@@ -130,7 +138,7 @@ hipError_t launch_reduce_derived(int L, int grid, int threads, size_t lds, hipSt
                                  int32_t rb, int32_t re, const ParamDev* params,
                                  const uint16_t* const* ptrs, const uint32_t* flags, float* out,
                                  int64_t out_stride, tide_trace_rec* trace, int64_t trace_base,
-                                 uint32_t* counts, int32_t xcd_lc);
+                                 uint32_t* counts, int32_t xcd_lc, bool shifted);
 
 hipError_t launch_place(int grid, int threads, size_t lds, hipStream_t stream,
                         const TileRec* tiles, int64_t tile_lo, int64_t tile_hi, int32_t rb,

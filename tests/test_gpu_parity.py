@@ -153,9 +153,10 @@ def test_misaligned_destinations(tide, orc, out_off):
 
 def test_gradients_at_dword_offsets(tide, orc):
     """Gradients 4-byte aligned but not 16-byte aligned (offsets of 2, 4 and 6
-    elements, mixed per contributor and parameter) still take the vector loads;
-    2-byte offsets take the element path. Both must give the oracle's bits, at
-    aligned and misaligned output strides and over a rank subset."""
+    elements, mixed per contributor and parameter) take the vector loads;
+    2-byte offsets take the dword-aligned loads with a funnel shift. Both must
+    give the oracle's bits, at aligned and misaligned output strides and over
+    a rank subset."""
     shapes = [(512, 1024), (300, 520), (70, 1), (1000, 3), (9, 4096)]
     N, L = 8, 8
     grads = host_grads(shapes, L, seed=77)
@@ -165,6 +166,54 @@ def test_gradients_at_dword_offsets(tide, orc):
             say("gradient offsets %s, stride S+%d, ranks %s" % (name, stride_extra, rr))
             run_case(tide, orc, shapes, N, L, grads, stride_extra=stride_extra, grad_offs=offs,
                      rank_range=rr, check_ag=False)
+
+
+def _tight_view(bits, shape, off):
+    """A bf16 view of `bits` starting `off` elements into a buffer that ends
+    exactly where the view ends."""
+    n = int(np.prod(shape))
+    buf = torch.full((n + off,), 0, dtype=torch.int16, device=dev())
+    buf[off:].copy_(torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).to(dev()))
+    return buf.view(torch.bfloat16)[off:].view(shape)
+
+
+@pytest.mark.parametrize("kind", ["full", "budgeted", "noalloc", "prepared"])
+@pytest.mark.parametrize("L", [8, 11, 26])
+def test_gradients_at_every_element_offset(tide, orc, kind, L):
+    """Every contributor's gradients at element offsets 0..7, so at 2 mod 4
+    bytes among others: the vector path reads those with dword-aligned loads
+    and a 16-bit funnel shift (contributors 0..23; a parameter with a later
+    one at 2 mod 4 goes element by element). The views end exactly at the end
+    of their buffers. Full grid, budgeted, the allocation-free entry point and
+    prepared calls; compile-time L = 8 and run-time L = 11 and 26."""
+    shapes = [(512, 1024), (300, 520), (70, 1), (1000, 3), (9, 4096)]
+    N = 8
+    grads = host_grads(shapes, L, seed=91 + L)
+    offs = [[(c + 3 * p) % 8 for p in range(len(shapes))] for c in range(L)]
+    g_dev = [[_tight_view(grads[c][p], (t, k), offs[c][p]) for p, (t, k) in enumerate(shapes)]
+             for c in range(L)]
+    plan = tide.plan_create(shapes, N, L)
+    want = orc.reduce_scatter(shapes, N, L, grads).reshape(-1)
+    for stride_extra in (0, 1):
+        stride = plan.S + stride_extra
+        out = torch.full((N * stride,), float(SENTINEL_F32), dtype=torch.float32, device=dev())
+        say("gradient offsets 0..7, L=%d, %s, stride S+%d" % (L, kind, stride_extra))
+        if kind == "full":
+            tide.reduce_scatter_bf16_fp32(plan, g_dev, out, out_stride=stride)
+        elif kind == "budgeted":
+            tide.reduce_scatter_bf16_fp32(plan, g_dev, out, out_stride=stride,
+                                          launch=tide.budgeted(max_launch_us=20))
+        elif kind == "noalloc":
+            tide.reduce_scatter_bf16_fp32_noalloc(plan, g_dev, out, out_stride=stride)
+        else:
+            call = tide.prepare_reduce_scatter_bf16_fp32(plan, g_dev, out, out_stride=stride)
+            call.enqueue()
+            torch.cuda.synchronize()
+            call.close()
+        torch.cuda.synchronize()
+        got = bits_of(out).reshape(N, stride)
+        same_f32(got[:, :plan.S], want.reshape(N, plan.S), "offsets 0..7 (%s, L=%d)" % (kind, L))
+        assert np.all(got[:, plan.S:] == SENTINEL_F32)
 
 
 @pytest.mark.parametrize("off", [0, 1])
