@@ -231,33 +231,51 @@ def gpu_clocks():
         return None
 
 
-def copy_ceiling_gbps(torch, nbytes=4 << 30, iters=10):
-    """Read+write GB/s of a plain device-to-device copy (practical ceiling)."""
-    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+def ceilings(torch, tide, nbytes=4 << 30, nsrc=8, reps=5):
+    """Practical HBM ceilings from the library's own streaming kernels
+    (tide_diag_stream; 128-thread workgroups, non-temporal accesses, the
+    reduce's launch shape): pure read, pure write, copy, and the reduce's own
+    access pattern with no layout logic (8 separately allocated bf16 sources
+    read with 8-byte loads, the fp32 sum stored with 16-byte stores: 4 bytes
+    read per byte written at L = 8). GB/s of bytes moved, median of `reps`."""
+    a = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
     b = torch.empty_like(a)
-    b.copy_(a)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(iters):
-        b.copy_(a)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / iters
-    del a, b
-    return 2 * nbytes / (ms / 1e3) / 1e9
+    n3 = nbytes // (2 * nsrc) // 1024 * 1024           # elements per source
+    srcs = [torch.zeros(n3, dtype=torch.bfloat16, device="cuda") for _ in range(nsrc)]
+    d3 = torch.empty(n3, dtype=torch.float32, device="cuda")
+    cases = {"read": (0, [a], b, nbytes, nbytes), "write": (1, [], b, nbytes, nbytes),
+             "copy": (2, [a], b, nbytes, 2 * nbytes),
+             "reduce_pattern": (3, srcs, d3, n3, (2 * nsrc + 4) * n3)}
+    res = {}
+    for name, (kind, ss, dst, n, moved) in cases.items():
+        tide.diag_stream(kind, ss, dst, n)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            tide.diag_stream(kind, ss, dst, n)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        res[name + "_GBps"] = round(moved / (statistics.median(ts) / 1e3) / 1e9, 1)
+    del a, b, srcs, d3
+    torch.cuda.empty_cache()
+    return res
 
 
-def victim_slowdown(torch, tide, plan, grads, out, shards, params, launch, gs, cs, reps=3, nb=4):
-    """Slowdown of a 256x8192x8192 bf16 GEMM while the reduce-scatter +
+def victim_slowdown(torch, tide, plan, grads, out, shards, params, launch, gs, cs, reps=3, nb=4,
+                    M=256):
+    """Slowdown of an Mx8192x8192 bf16 GEMM (M = 256: the pages' victim, which
+    hipBLASLt runs as 128 workgroups, half the CUs) while the reduce-scatter +
     placement run on another stream (median GEMM time, concurrent vs alone).
 
     The GEMMs cycle through `nb` different B matrices (nb * 128 MiB, more than
     the 256 MB Infinity Cache), so neither measurement finds B cached from the
     previous GEMM: both read it from HBM, as a training step's GEMMs do."""
-    A = torch.randn(256, 8192, device="cuda", dtype=torch.bfloat16)
+    A = torch.randn(M, 8192, device="cuda", dtype=torch.bfloat16)
     Bs = [torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16) for _ in range(nb)]
-    C = torch.empty(256, 8192, device="cuda", dtype=torch.bfloat16)
+    C = torch.empty(M, 8192, device="cuda", dtype=torch.bfloat16)
     for i in range(20):
         torch.matmul(A, Bs[i % nb], out=C)
     torch.cuda.synchronize()
@@ -308,6 +326,40 @@ def victim_slowdown(torch, tide, plan, grads, out, shards, params, launch, gs, c
             "collective_ms": round(statistics.median(r[1] for r in res), 3),
             "gemms_counted": int(statistics.median(r[2] for r in res)),
             "gemms_counted_are": res[0][3] + " the collective window"}
+
+
+def fence_study(torch, tide, plan, grads, out, shards, params, gs, cs):
+    """GEMM-victim slowdown under budgeted launch variants (workgroup lifetime
+    300 / 100 / 50 us, LDS fence on and off), for the pages' victim (M = 256:
+    128 hipBLASLt workgroups, half the CUs) and for one that fills the GPU in
+    one wave (M = 4096: 256 persistent workgroups of 256 threads, one per CU,
+    66.5 KB of LDS and 256 VGPRs each), with each variant's collective time
+    alone (median of 3)."""
+    variants = {"full_grid": tide.Launch()}
+    for us in (300, 100, 50):
+        variants["budgeted_16_4_%dus_fence" % us] = tide.budgeted(max_launch_us=us)
+        variants["budgeted_16_4_%dus_no_fence" % us] = tide.budgeted(
+            max_launch_us=us, flags=tide.FLAG_NO_LDS_FENCE)
+    res = {}
+    for name, launch in variants.items():
+        ts = []
+        for _ in range(4):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            tide.reduce_scatter_bf16_fp32(plan, grads, out, launch=launch)
+            tide.allgather_place(plan, shards, params, launch=launch)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        entry = {"collective_ms_alone": round(statistics.median(ts[1:]), 3),
+                 "launches": plan.launch_count(0, launch) + plan.launch_count(1, launch)}
+        for M in (256, 4096):
+            log("bench: fence study M=%d %s" % (M, name))
+            entry["victim_M%d" % M] = victim_slowdown(torch, tide, plan, grads, out, shards, params,
+                                                       launch, gs, cs, M=M)
+        res[name] = entry
+    return res
 
 
 def occupancy_probe(torch, tide, plan, grads, out, shards, params, gs, cs, probes=500,
@@ -684,14 +736,17 @@ def main():
     ap.add_argument("--placement-engine", default="kernel", choices=["kernel", "sdma", "runtime"],
                     help="engine of the placement in the timed step (default: the kernel)")
     ap.add_argument("--parts", action="store_true",
-                    help="also time the runtime-copy placement, the stage placement, the "
-                         "landing sum and a plain copy")
+                    help="also time the runtime-copy placement, the stage placement and the "
+                         "landing sum")
     ap.add_argument("--victim", action="store_true",
                     help="GEMM-victim slowdown of this workload, budgeted and full grid")
     ap.add_argument("--stock", action="store_true",
                     help="also time the stock FSDP2 path (chunk_cat pack + sum, split_with_sizes_copy)")
     ap.add_argument("--slot-reuse", action="store_true",
                     help="also time the Slot-Reuse staging and the reduce reading the slots")
+    ap.add_argument("--fence-study", action="store_true",
+                    help="GEMM-victim slowdown for budgeted variants (LDS fence on/off, shorter "
+                         "launches) with a half-GPU and a full-GPU victim")
     ap.add_argument("--occupancy", action="store_true",
                     help="trace where budgeted workgroups run, beside GEMM-shaped occupants")
     ap.add_argument("--graph", action="store_true",
@@ -792,9 +847,11 @@ def main():
         parts["placement_runtime_copy_ms"] = round(sd, 4)
         parts["placement_runtime_copy_GBps"] = round(ag_bytes / (sd / 1e3) / 1e9, 1)
         log("bench: runtime-copy placement %.3f ms" % sd)
-        # The practical ceiling of a plain 4 GiB device-to-device copy.
-        parts["plain_copy_GBps"] = round(copy_ceiling_gbps(torch), 1)
-        log("bench: plain copy %.1f GB/s" % parts["plain_copy_GBps"])
+    # Practical ceilings in the same run, from the library's streaming kernels.
+    parts["ceilings"] = ceilings(torch, tide)
+    parts["ceilings"]["reduce_over_its_pattern"] = round(
+        t["reduce_GBps_mean"] / parts["ceilings"]["reduce_pattern_GBps"], 4)
+    log("bench: ceilings %s" % json.dumps(parts["ceilings"]))
 
     # Two side streams, created once: a GEMM (or occupant) stream and a
     # collective stream. Reusing them keeps every measurement on the same pair
@@ -838,6 +895,11 @@ def main():
                   "full_grid": victim_slowdown(torch, tide, plan, grads, out, shards, params,
                                                tide.Launch(), gs, cs)}
         log("bench: victim %s" % json.dumps(victim))
+
+    fence = None
+    if args.fence_study:
+        fence = fence_study(torch, tide, plan, grads, out, shards, params, gs, cs)
+        log("bench: fence study %s" % json.dumps(fence))
 
     cpu = None
     orc = None
@@ -911,6 +973,8 @@ def main():
         line["slot_reuse"] = slot
     if occ is not None:
         line["occupancy_probe"] = occ
+    if fence is not None:
+        line["fence_study"] = fence
     if graph is not None:
         line["prepared_and_graph"] = graph
     print(json.dumps(line), flush=True)

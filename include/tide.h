@@ -119,8 +119,11 @@ typedef struct tide_launch {
     int32_t place_blocks;    /* BUDGETED: workgroups of each placement or landing launch (0 -> 4;
                                 at most 65536) */
     int32_t max_launch_us;   /* BUDGETED: work per launch sized so a workgroup lives about
-                                this long (0 -> 300). Each launch is a separate kernel; no
-                                workgroup ever waits on another. */
+                                this long (0 -> 50). Each launch is a separate kernel; no
+                                workgroup ever waits on another. A GEMM that fills the GPU
+                                with one workgroup per CU slows by about this life over its
+                                own duration (each CU a collective workgroup holds delays
+                                one of its workgroups until then). */
     int32_t rank_begin;      /* first rank whose shard is processed (default 0) */
     int32_t rank_end;        /* one past the last rank; 0 -> N */
     int32_t flags;           /* TIDE_FLAG_* */
@@ -460,6 +463,23 @@ tide_status tide_landing_trace_records(int32_t L, int32_t M, int64_t S, int32_t 
  */
 tide_status tide_diag_occupy(int32_t workgroups, int32_t threads, int32_t lds_bytes,
                              int64_t spin_ticks, tide_trace_rec* trace, void* stream);
+
+/*
+ * Diagnostic bandwidth ceilings: the access patterns of the path with no
+ * layout logic, in this library's own kernels (128-thread workgroups,
+ * non-temporal accesses), for timing against the real kernels.
+ *   kind 0: read n bytes from srcs[0] (16-byte aligned; dst receives nothing
+ *           in practice but must be a valid 16-byte-aligned device pointer);
+ *   kind 1: write n bytes of zeros to dst;
+ *   kind 2: copy n bytes from srcs[0] to dst;
+ *   kind 3: the reduce's pattern: dst[i] = sum over c < nsrc, in order, of the
+ *           widened bf16 srcs[c][i], for i < n (n elements; srcs 4-byte
+ *           aligned, nsrc in [1, 8]; dst holds n fp32).
+ * n is a multiple of 2048 (kinds 0-2, bytes) or 1024 (kind 3, elements).
+ * Async on `stream`. Errors: INVALID_ARG, ALIGNMENT, HIP.
+ */
+tide_status tide_diag_stream(int32_t kind, const void* const* srcs, int32_t nsrc, void* dst,
+                             int64_t n, void* stream);
 
 /* HIP events the plan holds across its devices: per-call table uploads, the
  * readers of each table slot (one per stream with pending work), and the pool

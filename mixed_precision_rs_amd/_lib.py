@@ -35,7 +35,7 @@ EXPORTS = ["tide_plan_create", "tide_plan_destroy", "tide_plan_dims", "tide_plan
            "tide_plan_event_count", "tide_prepare_reduce_scatter_bf16_fp32",
            "tide_prepare_allgather_place_stage", "tide_prepare_stage_grads_bf16",
            "tide_call_enqueue", "tide_call_destroy", "tide_plan_slot_grads",
-           "tide_dma_engine_count", "tide_reduce_scatter_bf16_fp32_noalloc"]
+           "tide_dma_engine_count", "tide_reduce_scatter_bf16_fp32_noalloc", "tide_diag_stream"]
 
 
 class TideError(RuntimeError):
@@ -112,7 +112,7 @@ def decode_trace(buf, records: int):
             "t_end": a[:, 2].view(np.uint64)}
 
 
-def budgeted(reduce_blocks=16, place_blocks=4, max_launch_us=300, **kw) -> Launch:
+def budgeted(reduce_blocks=16, place_blocks=4, max_launch_us=50, **kw) -> Launch:
     return Launch(mode=LAUNCH_BUDGETED, reduce_blocks=reduce_blocks, place_blocks=place_blocks,
                   max_launch_us=max_launch_us, **kw)
 
@@ -186,6 +186,8 @@ def _load():
                                                           ctypes.c_int64, ctypes.c_void_p,
                                                           ctypes.POINTER(Launch)]
     lib.tide_dma_engine_count.argtypes = [ctypes.c_int32, _I32P]
+    lib.tide_diag_stream.argtypes = [ctypes.c_int32, _VPP, ctypes.c_int32, ctypes.c_void_p,
+                                     ctypes.c_int64, ctypes.c_void_p]
     lib.tide_status_string.argtypes = [ctypes.c_int]
     lib.tide_status_string.restype = ctypes.c_char_p
     lib.tide_last_error_detail.argtypes = []
@@ -199,7 +201,8 @@ def _load():
               "tide_landing_trace_records", "tide_diag_occupy", "tide_plan_event_count",
               "tide_prepare_reduce_scatter_bf16_fp32", "tide_prepare_allgather_place_stage",
               "tide_prepare_stage_grads_bf16", "tide_call_enqueue", "tide_plan_slot_grads",
-              "tide_dma_engine_count", "tide_reduce_scatter_bf16_fp32_noalloc"):
+              "tide_dma_engine_count", "tide_reduce_scatter_bf16_fp32_noalloc",
+              "tide_diag_stream"):
         getattr(lib, f).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -645,6 +648,16 @@ def diag_occupy(workgroups: int, threads: int, lds_bytes: int, spin_ticks: int, 
     _check(_load().tide_diag_occupy(workgroups, threads, lds_bytes, spin_ticks, _ptr(trace), sh),
            "tide_diag_occupy")
     _record([trace], sobj)
+
+
+def diag_stream(kind: int, srcs: Sequence[object], dst, n: int, stream=None) -> None:
+    """tide_diag_stream: bandwidth-ceiling kernels (0 read, 1 write, 2 copy,
+    3 the reduce's access pattern over len(srcs) bf16 sources)."""
+    sa = (ctypes.c_void_p * max(len(srcs), 1))(*[_ptr(t) for t in srcs])
+    sh, sobj = _stream_handle(stream)
+    _check(_load().tide_diag_stream(int(kind), sa, len(srcs), _ptr(dst), int(n), sh),
+           "tide_diag_stream")
+    _record(list(srcs) + [dst], sobj)
 
 
 def latin_square(M: int, L: int, dst_node: int, src_node: int):

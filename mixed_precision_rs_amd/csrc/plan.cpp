@@ -69,12 +69,20 @@ class DeviceGuard {
     hipError_t status_ = hipSuccess;
 };
 
-// Defaults of the CU-budgeted mode: 16 summing + 4 landing blocks living
-// 0.2-0.4 ms each (page 1 "Why does a communication kernel slow a matrix
-// multiply by 69%?"; page 3 Table 4 "TIDE, training 16+4").
+// Defaults of the CU-budgeted mode: 16 summing + 4 landing blocks (page 1
+// "Why does a communication kernel slow a matrix multiply by 69%?"; page 3
+// Table 4 "TIDE, training 16+4"). The pages' blocks live 0.2-0.4 ms; here a
+// budgeted workgroup lives about 50 us. On MI355X hipBLASLt runs the bf16
+// GEMMs of M >= 512 (N = K = 8192) as 256 persistent workgroups, one per CU:
+// a CU held by a collective workgroup delays that GEMM workgroup until the
+// collective's ends, so the GEMM slows by about the collective workgroup's
+// life over the GEMM's. Measured with a 0.4 ms M = 4096 GEMM beside the Wan
+// block: 28% at 300 us, 7.6% at 100 us, 2.2% at 50 us (the pages' 256-row
+// victim, 128 workgroups: 1.2% at either length). The collective alone takes
+// 17% longer at 50 us (more launches).
 constexpr int kDefaultReduceBlocks = 16;
 constexpr int kDefaultPlaceBlocks = 4;
-constexpr int kDefaultMaxLaunchUs = 300;
+constexpr int kDefaultMaxLaunchUs = 50;
 // Budgeted launches use fat workgroups (kFatThreads) that reserve most of
 // their CU's LDS, so no other kernel's workgroup (a GEMM's, typically) shares
 // the CU with them: the concurrent kernel's workgroups are placed on the many
@@ -1725,6 +1733,33 @@ tide_status tide_plan_trace_records(const tide_plan* plan, int32_t op, const tid
     } catch (...) {
         return fail(TIDE_ERR_INVALID_ARG, "unexpected exception");
     }
+}
+
+tide_status tide_diag_stream(int32_t kind, const void* const* srcs, int32_t nsrc, void* dst,
+                             int64_t n, void* stream_v) {
+    if (kind < 0 || kind > 3) return fail(TIDE_ERR_INVALID_ARG, "kind %d not in 0..3", kind);
+    const int64_t unit = kind == 3 ? (int64_t)kStep : (int64_t)kThreads * 16;
+    if (n < 0 || n % unit) return fail(TIDE_ERR_INVALID_ARG, "n = %lld is not a multiple of %lld",
+                                       (long long)n, (long long)unit);
+    const int need = kind == 1 ? 0 : kind == 3 ? nsrc : 1;
+    if (kind == 3 && (nsrc < 1 || nsrc > kStreamMaxSrcs))
+        return fail(TIDE_ERR_INVALID_ARG, "nsrc = %d not in [1, %d]", nsrc, kStreamMaxSrcs);
+    if (need > 0 && !srcs) return fail(TIDE_ERR_INVALID_ARG, "srcs is NULL");
+    StreamSrcs sp{};
+    for (int i = 0; i < need; ++i) {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(srcs[i]);
+        if (!a) return fail(TIDE_ERR_INVALID_ARG, "srcs[%d] is NULL", i);
+        if (a & (kind == 3 ? 3 : 15)) return fail(TIDE_ERR_ALIGNMENT, "srcs[%d] misaligned", i);
+        sp.p[i] = srcs[i];
+    }
+    if (!dst) return fail(TIDE_ERR_INVALID_ARG, "dst is NULL");
+    if (reinterpret_cast<uintptr_t>(dst) & 15) return fail(TIDE_ERR_ALIGNMENT, "dst is not 16-byte aligned");
+    const int64_t units = n / unit;
+    if (units == 0) return TIDE_OK;
+    const int grid = (int)std::min<int64_t>(units, kFullGridCap);
+    TIDE_HIP_TRY(launch_stream(kind, grid, reinterpret_cast<hipStream_t>(stream_v), sp,
+                               kind == 3 ? nsrc : 1, dst, units));
+    return TIDE_OK;
 }
 
 tide_status tide_diag_occupy(int32_t workgroups, int32_t threads, int32_t lds_bytes,

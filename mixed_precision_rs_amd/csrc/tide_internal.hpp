@@ -171,6 +171,13 @@ hipError_t launch_landing(int M, int grid, int threads, size_t lds, hipStream_t 
                           int64_t tiles_per_shard, int64_t tile_lo, int64_t tile_hi,
                           int32_t accumulate, int32_t scalar, tide_trace_rec* trace,
                           int64_t trace_base, uint32_t* counts);
+// Bandwidth-ceiling kernels (tide_diag_stream): sources by value.
+constexpr int kStreamMaxSrcs = 8;
+struct StreamSrcs {
+    const void* p[kStreamMaxSrcs];
+};
+hipError_t launch_stream(int kind, int grid, hipStream_t stream, const StreamSrcs& srcs,
+                         int32_t nsrc, void* dst, int64_t units);
 // Diagnostic occupant (tide_diag_occupy).
 hipError_t launch_occupy(int grid, int threads, size_t lds, hipStream_t stream, int64_t spin_ticks,
                          tide_trace_rec* trace);
