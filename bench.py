@@ -247,18 +247,27 @@ def ceilings(torch, tide, nbytes=4 << 30, nsrc=8, reps=5):
              "copy": (2, [a], b, nbytes, 2 * nbytes),
              "reduce_pattern": (3, srcs, d3, n3, (2 * nsrc + 4) * n3)}
     res = {}
-    for name, (kind, ss, dst, n, moved) in cases.items():
-        tide.diag_stream(kind, ss, dst, n)
+
+    def timed(kind, ss, dst, n, wg=0):
+        tide.diag_stream(kind, ss, dst, n, workgroups=wg)
         torch.cuda.synchronize()
         ts = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            tide.diag_stream(kind, ss, dst, n)
+            tide.diag_stream(kind, ss, dst, n, workgroups=wg)
             e1.record()
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
-        res[name + "_GBps"] = round(moved / (statistics.median(ts) / 1e3) / 1e9, 1)
+        return statistics.median(ts)
+    for name, (kind, ss, dst, n, moved) in cases.items():
+        res[name + "_GBps"] = round(moved / (timed(kind, ss, dst, n) / 1e3) / 1e9, 1)
+    # Per CU, in the budgeted kernels' shape: 16 workgroups of 1024 threads on
+    # 16 CUs, 1/16 of the buffers (read, and the reduce's pattern).
+    nr, n3s = nbytes // 16 // 2048 * 2048, n3 // 16 // 1024 * 1024
+    res["per_cu_read_GBps"] = round(nr / (timed(0, [a], b, nr, 16) / 1e3) / 1e9 / 16, 1)
+    res["per_cu_reduce_pattern_GBps"] = round(
+        (2 * nsrc + 4) * n3s / (timed(3, srcs, d3, n3s, 16) / 1e3) / 1e9 / 16, 1)
     del a, b, srcs, d3
     torch.cuda.empty_cache()
     return res

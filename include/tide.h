@@ -280,9 +280,9 @@ tide_status tide_allgather_place_stage(const tide_plan* plan, const uint16_t* st
 /*
  * Slot-Reuse staging (page 1 "When gradients can be freed also needs
  * planning"; page 2 "What shipped"; page 3 abstract and Figure 7): copy each
- * contributor's bf16 gradients into an all-gather slot that has just been
- * vacated, so that the gradient storage can be released as soon as the copy
- * has run; the level-1 reduce then reads the slot instead of the gradients.
+ * contributor's bf16 gradients into an all-gather slot whose last use is over,
+ * so that the gradient storage can be released as soon as the copy has run;
+ * the level-1 reduce then reads the slot instead of the gradients.
  *
  *   grads:  L * P bf16 pointers, grads[c * P + p], as for
  *           tide_reduce_scatter_bf16_fp32 (T_p x K_p row-major, 2-byte aligned).
@@ -476,10 +476,13 @@ tide_status tide_diag_occupy(int32_t workgroups, int32_t threads, int32_t lds_by
  *           widened bf16 srcs[c][i], for i < n (n elements; srcs 4-byte
  *           aligned, nsrc in [1, 8]; dst holds n fp32).
  * n is a multiple of 2048 (kinds 0-2, bytes) or 1024 (kind 3, elements).
+ * workgroups = 0: a full grid of 128-thread workgroups (the full-grid
+ * kernels' shape); > 0: that many 1024-thread workgroups, each on a CU of its
+ * own, which gives the per-CU ceiling of the budgeted kernels' shape.
  * Async on `stream`. Errors: INVALID_ARG, ALIGNMENT, HIP.
  */
 tide_status tide_diag_stream(int32_t kind, const void* const* srcs, int32_t nsrc, void* dst,
-                             int64_t n, void* stream);
+                             int64_t n, int32_t workgroups, void* stream);
 
 /* HIP events the plan holds across its devices: per-call table uploads, the
  * readers of each table slot (one per stream with pending work), and the pool

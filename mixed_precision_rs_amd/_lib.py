@@ -187,7 +187,7 @@ def _load():
                                                           ctypes.POINTER(Launch)]
     lib.tide_dma_engine_count.argtypes = [ctypes.c_int32, _I32P]
     lib.tide_diag_stream.argtypes = [ctypes.c_int32, _VPP, ctypes.c_int32, ctypes.c_void_p,
-                                     ctypes.c_int64, ctypes.c_void_p]
+                                     ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
     lib.tide_status_string.argtypes = [ctypes.c_int]
     lib.tide_status_string.restype = ctypes.c_char_p
     lib.tide_last_error_detail.argtypes = []
@@ -650,13 +650,15 @@ def diag_occupy(workgroups: int, threads: int, lds_bytes: int, spin_ticks: int, 
     _record([trace], sobj)
 
 
-def diag_stream(kind: int, srcs: Sequence[object], dst, n: int, stream=None) -> None:
+def diag_stream(kind: int, srcs: Sequence[object], dst, n: int, workgroups: int = 0,
+                stream=None) -> None:
     """tide_diag_stream: bandwidth-ceiling kernels (0 read, 1 write, 2 copy,
-    3 the reduce's access pattern over len(srcs) bf16 sources)."""
+    3 the reduce's access pattern over len(srcs) bf16 sources); workgroups > 0
+    runs that many 1024-thread workgroups instead of the full grid."""
     sa = (ctypes.c_void_p * max(len(srcs), 1))(*[_ptr(t) for t in srcs])
     sh, sobj = _stream_handle(stream)
-    _check(_load().tide_diag_stream(int(kind), sa, len(srcs), _ptr(dst), int(n), sh),
-           "tide_diag_stream")
+    _check(_load().tide_diag_stream(int(kind), sa, len(srcs), _ptr(dst), int(n),
+                                    int(workgroups), sh), "tide_diag_stream")
     _record(list(srcs) + [dst], sobj)
 
 

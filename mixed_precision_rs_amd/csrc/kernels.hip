@@ -855,12 +855,16 @@ __global__ __launch_bounds__(1024) void occupy_kernel(int64_t spin_ticks, tide_t
 //   3: the reduce's pattern: each wave's 512 elements as two runs of 256,
 //      8-byte bf16 loads from each of nsrc sources, the fp32 sum in source
 //      order, one 16-byte store per run and lane.
-template <int KIND>
-__global__ __launch_bounds__(kThreads) void stream_kernel(StreamSrcs srcs, int32_t nsrc,
-                                                          void* __restrict__ dst, int64_t units) {
-    const int tid = (int)threadIdx.x;
+template <int KIND, int NT>
+__global__ __launch_bounds__(NT) void stream_kernel(StreamSrcs srcs, int32_t nsrc,
+                                                    void* __restrict__ dst, int64_t units) {
+    // A workgroup of NT threads is NT / kThreads independent quarters, each
+    // walking its own units (as the budgeted kernels do).
+    constexpr int kSubs = NT / kThreads;
+    const int tid = (int)threadIdx.x % kThreads;
+    const int sub = (int)threadIdx.x / kThreads;
     uint32_t acc = 0;
-    for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    for (int64_t u = (int64_t)blockIdx.x * kSubs + sub; u < units; u += (int64_t)gridDim.x * kSubs) {
         if constexpr (KIND == 3) {
             const int lane = tid % kWave;
             const int64_t base = u * kStep + (int64_t)(tid / kWave) * (2 * kHalf) + 4 * lane;
@@ -903,7 +907,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamSrcs srcs, int32
     // Kind 0 writes only if the fold hits a value chosen never to occur in the
     // probe's data, which keeps every load live without a real write stream.
     if constexpr (KIND == 0)
-        if (acc == 0x9E3779B9u && tid == 0) static_cast<uint32_t*>(dst)[blockIdx.x] = acc;
+        if (acc == 0x9E3779B9u && threadIdx.x == 0) static_cast<uint32_t*>(dst)[blockIdx.x] = acc;
 }
 
 template <int MT>
@@ -1074,15 +1078,20 @@ hipError_t launch_landing(int M, int grid, int threads, size_t lds, hipStream_t 
 #undef TIDE_LANDING_CASE
 }
 
-hipError_t launch_stream(int kind, int grid, hipStream_t stream, const StreamSrcs& srcs,
-                         int32_t nsrc, void* dst, int64_t units) {
+template <int NT>
+const void* stream_fn(int kind) {
+    return kind == 0   ? reinterpret_cast<const void*>(&stream_kernel<0, NT>)
+           : kind == 1 ? reinterpret_cast<const void*>(&stream_kernel<1, NT>)
+           : kind == 2 ? reinterpret_cast<const void*>(&stream_kernel<2, NT>)
+                       : reinterpret_cast<const void*>(&stream_kernel<3, NT>);
+}
+
+hipError_t launch_stream(int kind, int grid, int threads, hipStream_t stream,
+                         const StreamSrcs& srcs, int32_t nsrc, void* dst, int64_t units) {
     StreamSrcs s = srcs;
     void* args[] = {&s, &nsrc, &dst, &units};
-    const void* fn = kind == 0   ? reinterpret_cast<const void*>(&stream_kernel<0>)
-                     : kind == 1 ? reinterpret_cast<const void*>(&stream_kernel<1>)
-                     : kind == 2 ? reinterpret_cast<const void*>(&stream_kernel<2>)
-                                 : reinterpret_cast<const void*>(&stream_kernel<3>);
-    return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, stream);
+    const void* fn = threads == kFatThreads ? stream_fn<kFatThreads>(kind) : stream_fn<kThreads>(kind);
+    return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, stream);
 }
 
 hipError_t launch_occupy(int grid, int threads, size_t lds, hipStream_t stream, int64_t spin_ticks,

@@ -1736,8 +1736,11 @@ tide_status tide_plan_trace_records(const tide_plan* plan, int32_t op, const tid
 }
 
 tide_status tide_diag_stream(int32_t kind, const void* const* srcs, int32_t nsrc, void* dst,
-                             int64_t n, void* stream_v) {
+                             int64_t n, int32_t workgroups, void* stream_v) {
     if (kind < 0 || kind > 3) return fail(TIDE_ERR_INVALID_ARG, "kind %d not in 0..3", kind);
+    if (workgroups < 0 || workgroups > kMaxBudgetBlocks)
+        return fail(TIDE_ERR_INVALID_ARG, "workgroups = %d not in [0, %d]", workgroups,
+                    kMaxBudgetBlocks);
     const int64_t unit = kind == 3 ? (int64_t)kStep : (int64_t)kThreads * 16;
     if (n < 0 || n % unit) return fail(TIDE_ERR_INVALID_ARG, "n = %lld is not a multiple of %lld",
                                        (long long)n, (long long)unit);
@@ -1756,9 +1759,10 @@ tide_status tide_diag_stream(int32_t kind, const void* const* srcs, int32_t nsrc
     if (reinterpret_cast<uintptr_t>(dst) & 15) return fail(TIDE_ERR_ALIGNMENT, "dst is not 16-byte aligned");
     const int64_t units = n / unit;
     if (units == 0) return TIDE_OK;
-    const int grid = (int)std::min<int64_t>(units, kFullGridCap);
-    TIDE_HIP_TRY(launch_stream(kind, grid, reinterpret_cast<hipStream_t>(stream_v), sp,
-                               kind == 3 ? nsrc : 1, dst, units));
+    const int grid = workgroups > 0 ? workgroups : (int)std::min<int64_t>(units, kFullGridCap);
+    TIDE_HIP_TRY(launch_stream(kind, grid, workgroups > 0 ? kFatThreads : kThreads,
+                               reinterpret_cast<hipStream_t>(stream_v), sp, kind == 3 ? nsrc : 1,
+                               dst, units));
     return TIDE_OK;
 }
 

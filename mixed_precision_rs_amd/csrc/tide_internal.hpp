@@ -176,8 +176,8 @@ constexpr int kStreamMaxSrcs = 8;
 struct StreamSrcs {
     const void* p[kStreamMaxSrcs];
 };
-hipError_t launch_stream(int kind, int grid, hipStream_t stream, const StreamSrcs& srcs,
-                         int32_t nsrc, void* dst, int64_t units);
+hipError_t launch_stream(int kind, int grid, int threads, hipStream_t stream,
+                         const StreamSrcs& srcs, int32_t nsrc, void* dst, int64_t units);
 // Diagnostic occupant (tide_diag_occupy).
 hipError_t launch_occupy(int grid, int threads, size_t lds, hipStream_t stream, int64_t spin_ticks,
                          tide_trace_rec* trace);

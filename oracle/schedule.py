@@ -5,14 +5,16 @@ TEST INFRASTRUCTURE ONLY (plain Python, small inputs): the library's own
 schedule generator is checked against this, and this against the pages'
 worked facts (M = 5 takes 3 rounds; M = 8 takes 3 where a ring takes 7).
 
-The pages' description, restated: machines are numbered 0..M-1. In round d
-(from 0) machine n sends the first min(2^d, M - 2^d) pieces it has collected
-to machine n - 2^d and receives as many from machine n + 2^d, numbers taken
-modulo M; machines begin holding only their own piece. The rounds stop once
-every machine holds all M pieces, which takes ceil(log2 M) rounds. Each
-transfer is split into a small head and the rest (the tail); the heads of a
-round total at most `head_bytes` (8 MiB by default on page 1), and the next
-round starts once the heads are confirmed.
+The schedule as implemented here: machines 0..M-1 start with one piece
+each (their own). Round d = 0, 1, ... pairs every machine with a receiver
+2^d below it and a sender 2^d above it (indices mod M); it passes on the
+oldest min(2^d, M - 2^d) pieces it holds and takes in as many. So the pieces
+moved per round double until the final round, which, when M is not a power
+of two, carries only the pieces still missing; no piece is received twice,
+and after ceil(log2 M) rounds every machine holds all M. Each transfer is cut
+into a small head and the remainder (the tail), the heads of a round adding
+up to at most `head_bytes` (8 MiB by default, page 1), and the next round
+waits for the heads to be confirmed.
 """
 from typing import Dict, List
 

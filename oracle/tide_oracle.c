@@ -20,8 +20,9 @@
  *   rows, so s_p = R_p * K_p, o_p = sum of s_q over q < p in list order (no
  *   alignment padding: the worked example on page 1 uses the plain prefix
  *   sum), and S = sum of s_p. Rank r's shard is the concatenation of rank r's
- *   pieces of every parameter ("all of GPU 0's data first, then all of GPU
- *   1's", page 1). Local row i of rank r holds true row t = r * R_p + i.
+ *   pieces of every parameter, and the shards follow one another in rank
+ *   order (page 1 "What problem is it actually solving?": the collective
+ *   library's flat buffers are ordered by rank). Local row i of rank r holds true row t = r * R_p + i.
  *
  *   Reduce-scatter, level 1. Every contributor c = 0..L-1 holds a bf16
  *   gradient of every parameter (T_p x K_p, contiguous). The output element
@@ -376,8 +377,8 @@ int oracle_landing_sum(int32_t L, int32_t M, int64_t S, const float *const *inbo
 
 /*
  * The Latin-square seating for one (destination, source) node pair: the
- * source's relative index c = (dst - src) mod M; source GPU j handles slice
- * (j + c) mod L; slice s from that source lands on destination GPU
+ * source's relative index c = (dst - src) mod M; the source's GPU j sends
+ * slice (j + c) mod L; slice s from that source lands on destination GPU
  * (s - c) mod L (page 1, the worked 4-GPU example; page 3 Figure 6(b)).
  */
 int oracle_latin_square(int32_t M, int32_t L, int32_t dst, int32_t src, int32_t *c,

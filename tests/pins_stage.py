@@ -3,7 +3,7 @@ all-gather slot, in the group's parameter-major padded layout).
 
 Sources, none of them the oracle's code:
   * the worked example on page 1 ("What problem is it actually solving?",
-    tests/golden/worked_example.json): GPU 1's piece of the second parameter
+    tests/golden/worked_example.json): rank 1's piece of parameter 1 (0-based)
     starts at the "9 MB" parameter-major address;
   * the parameter-major slot built by numpy from its definition: every
     parameter zero-extended (here: sentinel-extended) to the smallest row

@@ -30,7 +30,10 @@ def test_copy_write_read(tide):
     torch.cuda.synchronize()
     assert int(dst.abs().sum()) == 0
     tide.diag_stream(0, [src], dst, n)           # reads only
+    dst.fill_(7)
+    tide.diag_stream(2, [src], dst, n, workgroups=3)   # 1024-thread workgroups
     torch.cuda.synchronize()
+    assert torch.equal(src, dst)
 
 
 @pytest.mark.parametrize("nsrc", [1, 3, 8])
@@ -40,11 +43,12 @@ def test_reduce_pattern(tide, nsrc):
     g.manual_seed(nsrc)
     srcs = [torch.randint(-256, 257, (n,), generator=g, device=dev()).to(torch.float32)
             .to(torch.bfloat16) for _ in range(nsrc)]
-    dst = torch.full((n,), float("nan"), device=dev())
-    tide.diag_stream(3, srcs, dst, n)
-    torch.cuda.synchronize()
     want = sum(s.float().cpu().numpy().astype(np.float64) for s in srcs)
-    assert np.array_equal(dst.cpu().numpy().astype(np.float64), want)
+    for wg in (0, 5):
+        dst = torch.full((n,), float("nan"), device=dev())
+        tide.diag_stream(3, srcs, dst, n, workgroups=wg)
+        torch.cuda.synchronize()
+        assert np.array_equal(dst.cpu().numpy().astype(np.float64), want)
 
 
 def test_rejects(tide):
