@@ -36,7 +36,13 @@
  *   - Pointer arrays (grads, params) are host arrays, read during the call
  *     only. The pointers in them are device pointers.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). The
- *     device used is the stream's device. The compute calls only enqueue.
+ *     device used is the stream's device. The compute calls only enqueue,
+ *     except that the first call of a plan on a device, and the first for
+ *     each (operation, launch mode, rank range), builds the plan's small
+ *     device tables there with a synchronous allocation and upload (kept up
+ *     to 256 per device; past that, the least recently used one that no
+ *     prepared call holds is freed after the device has drained). The
+ *     TIDE_ENGINE_SDMA path is host-synchronous (see tide_engine).
  *   - A plan may be used from several threads and streams at once; it is
  *     immutable after creation except for internally locked caches.
  */

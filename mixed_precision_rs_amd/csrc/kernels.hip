@@ -849,12 +849,14 @@ __global__ __launch_bounds__(1024) void occupy_kernel(int64_t spin_ticks, tide_t
 // Bandwidth ceilings (tide_diag_stream): the access patterns of the path with
 // no layout logic. A unit is 128 threads x 16 bytes (kinds 0-2) or 1024
 // elements of every source (kind 3); workgroups walk units grid-stride.
-//   0: read 16 B per thread (non-temporal), folded so the loads stay live;
+//   0: read 16 B per thread and unit (non-temporal), folded so the loads
+//      stay live; kinds 0-2 keep up to kStreamDepth units per thread in flight;
 //   1: write 16 B of zeros per thread;
 //   2: copy 16 B per thread;
 //   3: the reduce's pattern: each wave's 512 elements as two runs of 256,
 //      8-byte bf16 loads from each of nsrc sources, the fp32 sum in source
 //      order, one 16-byte store per run and lane.
+constexpr int kStreamDepth = 4;
 template <int KIND, int NT>
 __global__ __launch_bounds__(NT) void stream_kernel(StreamSrcs srcs, int32_t nsrc,
                                                     void* __restrict__ dst, int64_t units) {
@@ -892,16 +894,29 @@ __global__ __launch_bounds__(NT) void stream_kernel(StreamSrcs srcs, int32_t nsr
                 TIDE_ST(x, gbl_mut<f32x4_a4>(static_cast<float*>(dst) + base + h * kHalf));
             }
         } else {
-            const int64_t e = u * kThreads + tid;        // 16-byte word
-            if constexpr (KIND == 0) {
-                const u32x4 x = TIDE_LD(gbl<u32x4>(srcs.p[0]) + e);
-                acc ^= x[0] ^ x[1] ^ x[2] ^ x[3];
-            } else if constexpr (KIND == 1) {
-                const u32x4 z = {0u, 0u, 0u, 0u};
-                TIDE_ST(z, gbl_mut<u32x4>(dst) + e);
-            } else {
-                TIDE_ST(TIDE_LD(gbl<u32x4>(srcs.p[0]) + e), gbl_mut<u32x4>(dst) + e);
+            // Up to kStreamDepth units per thread in flight (a budgeted
+            // workgroup walks many units; a full-grid one has a single unit).
+            const int64_t us = (int64_t)gridDim.x * kSubs;
+            u32x4 x[kStreamDepth];
+#pragma unroll
+            for (int k = 0; k < kStreamDepth; ++k) {
+                const int64_t uk = u + k * us;
+                if (KIND != 1 && uk < units) x[k] = TIDE_LD(gbl<u32x4>(srcs.p[0]) + uk * kThreads + tid);
             }
+#pragma unroll
+            for (int k = 0; k < kStreamDepth; ++k) {
+                const int64_t uk = u + k * us;
+                if (uk >= units) break;
+                if constexpr (KIND == 0) {
+                    acc ^= x[k][0] ^ x[k][3];
+                } else if constexpr (KIND == 1) {
+                    const u32x4 z = {0u, 0u, 0u, 0u};
+                    TIDE_ST(z, gbl_mut<u32x4>(dst) + uk * kThreads + tid);
+                } else {
+                    TIDE_ST(x[k], gbl_mut<u32x4>(dst) + uk * kThreads + tid);
+                }
+            }
+            u += (kStreamDepth - 1) * us;
         }
     }
     // Kind 0 writes only if the fold hits a value chosen never to occur in the

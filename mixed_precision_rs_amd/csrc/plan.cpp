@@ -139,7 +139,14 @@ constexpr int32_t kKnownFlags = TIDE_FLAG_SCALAR_PATH | TIDE_FLAG_NO_LDS_FENCE;
 struct TileTable {
     TileRec* dev = nullptr;
     int64_t count = 0;
+    uint64_t last_use = 0;   // DevState::use_clock at the last lookup
+    int64_t pins = 0;        // prepared calls that launch from it (never evicted while > 0)
 };
+
+// Tile tables kept per device (one per operation, launch mode and rank
+// range). Past this, the least recently used table no prepared call holds is
+// freed, after the device has drained (its kernels may still be reading it).
+constexpr size_t kMaxTileTables = 256;
 
 // A call that read a slot: the last such call on `stream` is marked by `ev`
 // (work on one stream completes in order, so one event per stream suffices).
@@ -162,6 +169,7 @@ struct DevState {
     int device = -1;
     ParamDev* params = nullptr;
     std::map<std::tuple<int, int, int>, TileTable> tiles;   // (op + 4 * budgeted, rank_begin, rank_end)
+    uint64_t use_clock = 0;
     size_t slot_cap = 0;
     char* ring_dev = nullptr;
     char* ring_host = nullptr;
@@ -195,13 +203,14 @@ struct ParamInfo {
 // Full-grid reduce tile order (the XCD runs of kernels.hip's xcd_tile_rt).
 // Interleaved in one process on MI355X, against one tile per XCD in turn:
 //  - groups whose destinations mostly start mid-line (the padding-stress
-//    group: an odd S) reduce 1.5-1.7% faster with runs of 64 tiles; a step's
-//    two partly written end lines are shared with the neighbouring steps,
-//    and in one run those neighbours go through the same L2;
+//    group: an odd S) reduce about 4% faster with runs of 128 tiles (64:
+//    +2.3%; 256 to 1024: as 128); a step's two partly written end lines are
+//    shared with the neighbouring steps, and in one run those neighbours go
+//    through the same L2;
 //  - groups of mostly small pieces (the Qwen MoE layer's 24,576-element
-//    expert pieces) 0.9% faster with runs of 16;
+//    expert pieces) about 1% faster with runs of 16 (8 and 32: slower);
 //  - groups of large, line-aligned pieces (Llama, Wan) 3% slower with either.
-constexpr int kXcdRunMisaligned = 6;    // log2 of 64 tiles
+constexpr int kXcdRunMisaligned = 7;    // log2 of 128 tiles
 constexpr int kXcdRunSmall = 4;         // log2 of 16 tiles
 constexpr int64_t kSmallPiece = 1 << 17;
 
@@ -403,11 +412,25 @@ tide_status get_tiles(const tide_plan* plan, DevState* ds, int op, int rb, int r
     auto key = std::make_tuple(op + (fat ? 4 : 0), rb, re);
     auto it = ds->tiles.find(key);
     if (it != ds->tiles.end()) {
+        it->second.last_use = ++ds->use_clock;
         *out = &it->second;
         return TIDE_OK;
     }
+    if (ds->tiles.size() >= kMaxTileTables) {
+        auto victim = ds->tiles.end();
+        for (auto v = ds->tiles.begin(); v != ds->tiles.end(); ++v)
+            if (v->second.pins == 0 && (victim == ds->tiles.end() ||
+                                        v->second.last_use < victim->second.last_use))
+                victim = v;
+        if (victim != ds->tiles.end()) {
+            TIDE_HIP_TRY(hipDeviceSynchronize());
+            TIDE_HIP_TRY(hipFree(victim->second.dev));
+            ds->tiles.erase(victim);
+        }
+    }
     std::vector<TileRec> t = build_tiles(plan, op, rb, re, fat);
     TileTable tt;
+    tt.last_use = ++ds->use_clock;
     tt.count = (int64_t)t.size();
     if (!t.empty()) {
         TIDE_HIP_TRY(hipMalloc(&tt.dev, t.size() * sizeof(TileRec)));
@@ -509,7 +532,7 @@ tide_status release_slot(DevState* ds, int slot, hipStream_t stream) {
 }
 
 // log2 of the full-grid reduce's XCD run length for output `out` with shard
-// stride `stride` over ranks [rb, re): runs of 64 when more than half of the
+// stride `stride` over ranks [rb, re): runs of 128 when more than half of the
 // output elements are in pieces whose destination starts mid-line (128 B),
 // of 16 when the group is mostly small pieces, else 0 (round robin). The
 // residue of a piece's start modulo 32 elements repeats with a period that
@@ -1104,7 +1127,7 @@ struct tide_call {
     Prepared pr;
     int device = -1;
     const DevState* ds = nullptr;
-    const TileTable* tt = nullptr;
+    TileTable* tt = nullptr;          // pinned in the plan's cache while the call lives
     void* dtab = nullptr;
 };
 
@@ -1123,6 +1146,7 @@ tide_status make_call(const tide_plan* plan, Prepared&& pr, tide_call** out) {
         if (st != TIDE_OK) return st;
         call->ds = ds;
         call->tt = tt;
+        ++tt->pins;
         if (tt->count > 0) {
             TIDE_HIP_TRY(hipMalloc(&call->dtab, call->pr.table.size()));
             hipError_t e = hipMemcpy(call->dtab, call->pr.table.data(), call->pr.table.size(),
@@ -1456,6 +1480,10 @@ tide_status tide_call_enqueue(const tide_call* call, void* stream_v) {
 
 void tide_call_destroy(tide_call* call) {
     if (!call) return;
+    if (call->tt) {
+        std::lock_guard<std::mutex> lock(call->plan->mu);
+        --call->tt->pins;
+    }
     if (call->dtab) {
         DeviceGuard guard(call->device);
         (void)hipFree(call->dtab);

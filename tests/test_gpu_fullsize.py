@@ -2,6 +2,10 @@
 benchmark times (full grid), plus the CU-budgeted mode on the DiT block.
 
 Checks, per workload:
+  * the whole output: every shard of the reduce-scatter (distinct
+    contributors, so a fold-order mistake would show) and every parameter the
+    placement wrote, against the oracle on the same bits, streamed by rank
+    range (oracle/check.py);
   * sampled pieces: for ranks {0, 1, N/2, N-1, two random} and a sample of
     parameters, the oracle recomputes the piece from the same input rows
     (fetched from the GPU at the oracle's own piece addresses) and the GPU's
@@ -11,8 +15,8 @@ Checks, per workload:
     output element equals L * f32(g) exactly in any summation order, so the
     WHOLE output is checked against a torch expression (pad + view) built from
     the oracle's layout;
-  * placement, kernel and runtime-copy engines: every parameter equals the
-    split-with-sizes view of the rank-major shards at the oracle's offsets.
+  * placement, kernel, runtime-copy and DMA engines: every parameter equals
+    the split-with-sizes view of the rank-major shards at the oracle's offsets.
 """
 import gc
 
@@ -142,7 +146,16 @@ def test_full_size(tide, orc, name):
     out.view(torch.int32).fill_(0x7FC0DEAD)
     tide.reduce_scatter_bf16_fp32(plan, grads, out)
     torch.cuda.synchronize()
-    say("%s: reduce-scatter done; checking sampled pieces" % name)
+    say("%s: reduce-scatter done; whole output and placement vs the oracle" % name)
+    from oracle import check
+    sh = device_rank_major_bits(cfg.N * S, seed=6)
+    params = [torch.empty((t, k), dtype=torch.bfloat16, device=dev()) for t, k in cfg.shapes]
+    tide.allgather_place(plan, sh, params)
+    torch.cuda.synchronize()
+    chk = check.whole_output(orc, cfg, S, grads, out, sh, params)
+    assert chk["reduce_scatter_bit_exact"] and chk["placement_bit_exact"], chk["first_mismatch"]
+    del sh, params
+    say("%s: checking sampled pieces" % name)
     _check_pieces(orc, cfg, grads, out, S, _sample_pieces(cfg, rng))
     say("%s: checking padding" % name)
     _check_padding(orc, cfg, out, S)
@@ -160,7 +173,7 @@ def test_full_size(tide, orc, name):
     _check_identical(tide, orc, cfg, grads0)
     del grads0
     _free()
-    for eng in ("kernel", "runtime"):
+    for eng in ("kernel", "runtime", "sdma"):
         say("%s: placement %s" % (name, eng))
         _check_place(tide, orc, cfg, eng)
     if name == "wan22_dit_block":

@@ -146,3 +146,35 @@ def test_prepared_step_in_a_graph(tide, orc, kind):
     del g
     for call in (st, rs, ag):
         call.close()
+
+
+def test_tile_cache_eviction_keeps_prepared_calls(tide, orc):
+    """More distinct rank ranges than the per-device tile-table cache holds
+    (256): older tables are freed after the device drains, while the table of
+    a live prepared call is kept. Every result equals the oracle's."""
+    shapes = [(130, 8), (17, 3), (64, 1)]
+    N, L = 64, 2
+    grads = host_grads(shapes, L, seed=8)
+    plan = tide.plan_create(shapes, N, L)
+    S = plan.S
+    g = [[to_dev_bf16(grads[c][p], (t, k)) for p, (t, k) in enumerate(shapes)] for c in range(L)]
+    want = orc.reduce_scatter(shapes, N, L, grads).reshape(-1)
+    pinned_out = torch.full((N * S,), float("nan"), device=dev())
+    call = tide.prepare_reduce_scatter_bf16_fp32(plan, g, pinned_out,
+                                                 launch=tide.Launch(rank_begin=5, rank_end=40))
+    ranges = [(a, b) for a in range(N) for b in range(a + 1, N + 1)][:300]
+    out = torch.full((N * S,), float("nan"), device=dev())
+    say("tile cache: %d distinct rank ranges" % len(ranges))
+    for i, (a, b) in enumerate(ranges):
+        tide.reduce_scatter_bf16_fp32(plan, g, out, launch=tide.Launch(rank_begin=a, rank_end=b))
+        if i % 50 == 49:
+            torch.cuda.synchronize()
+            got = bits_of(out)
+            assert np.array_equal(got[a * S: b * S].view(np.uint32), want[a * S: b * S].view(np.uint32))
+    torch.cuda.synchronize()
+    call.enqueue()
+    torch.cuda.synchronize()
+    got = bits_of(pinned_out)
+    assert np.array_equal(got[5 * S: 40 * S].view(np.uint32), want[5 * S: 40 * S].view(np.uint32))
+    assert np.all(np.isnan(got[: 5 * S])) and np.all(np.isnan(got[40 * S:]))
+    call.close()
