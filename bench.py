@@ -33,8 +33,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "effective HBM GB/s (and % of 8 TB/s) for bf16->fp32 layout RS + AG placement"
+# The kernels and the host code that decides their launch shape and tile
+# order: counter summaries are valid only for the code they were taken on.
 KERNEL_SOURCES = [os.path.join(ROOT, "mixed_precision_rs_amd", "csrc", f)
-                  for f in ("kernels.hip", "tide_internal.hpp")]
+                  for f in ("kernels.hip", "tide_internal.hpp", "plan.cpp")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -52,8 +54,8 @@ def code_text(src: str) -> str:
 
 
 def kernel_source_hash() -> str:
-    """sha256 of the kernel sources' code (comments excluded): counter
-    summaries taken on other kernel code are not used."""
+    """sha256 of the kernel and launch-policy sources' code (comments
+    excluded): counter summaries taken on other code are not used."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(f, encoding="utf-8") as fh:
