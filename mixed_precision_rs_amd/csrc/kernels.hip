@@ -158,11 +158,13 @@ __device__ __forceinline__ void store4(const Span& t, const ParamDev& pd, int64_
 // walks runs of C consecutive tiles and a cache line shared by two
 // neighbouring tiles goes through one L2 rather than two. The mapping is a
 // bijection on the first multiple of kXcds * C tiles and the identity on the
-// rest (C = 1 is the identity). Measured on MI355X: +2% for the placement
-// (whose bf16 source runs start at arbitrary 2-byte offsets); for the reduce
-// the host picks C per call (reduce_xcd_log2 in plan.cpp).
+// rest (C = 1 is the identity). The placement (whose bf16 source runs start
+// at arbitrary 2-byte offsets) uses runs of 128: interleaved on MI355X
+// against round robin, padding stress +1.3%, Llama +1.6%, Wan +1.4%, Qwen
+// +0% (16: slower everywhere; 256: Qwen -1%). For the reduce the host picks
+// C per call (reduce_xcd_log2 in plan.cpp).
 #ifndef TIDE_XCD_CHUNK_AG
-#define TIDE_XCD_CHUNK_AG 64
+#define TIDE_XCD_CHUNK_AG 128
 #endif
 constexpr int64_t kXcds = 8;
 template <int64_t C>
@@ -327,7 +329,11 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
                         // f - 1 (f is a multiple of 4, so f - 1 starts a
                         // dword); every dword read holds an element of the
                         // step's valid range, or the one before it, or the
-                        // one after it in the same dword. Wave-uniform.
+                        // one after it in the same dword. Wave-uniform. (An
+                        // 8-byte load per lane with the third dword taken
+                        // from the next lane over ds_bpermute measured 4%
+                        // slower on MI355X: each contributor then waits on
+                        // an LDS round trip after its load.)
                         const TIDE_GLOBAL u32x3_a4* gq = gbl<u32x3_a4>(g[c] + fh - 1);
 #pragma unroll
                         for (int u = 0; u < kUR; ++u)
