@@ -281,7 +281,18 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
     constexpr int64_t kTileR = NT == kFatThreads ? kRsTileFat : kRsTile;
     constexpr int kUR = NT == kFatThreads ? kRsUnrollFat : kRsUnroll;
     const int L = LT > 0 ? LT : Lrt;
-    const int sub = (int)threadIdx.x / kThreads;          // wave-uniform
+    // Wave-uniform, and in the shifted variant also provably so to the
+    // compiler (readfirstlane): the tile walk then runs in scalar registers
+    // and each contributor's choice of loads is a scalar branch, so the loads
+    // of all contributors are still issued before the first add waits (as
+    // exec-masked regions, each contributor waited for its loads in turn:
+    // 4.2 against 5.8 TB/s on MI355X for a group at 2 mod 4 bytes). The
+    // aligned variant keeps the plain form, which measured 1-8% faster there,
+    // and so do budgeted workgroups, where the scalar form runs out of SGPRs
+    // and spills for some L.
+    constexpr bool kUniform = SHIFTED && NT == kThreads;
+    const int sub = kUniform ? __builtin_amdgcn_readfirstlane((int)threadIdx.x / kThreads)
+                             : (int)threadIdx.x / kThreads;
     const int tid = (int)threadIdx.x % kThreads;
 #if TIDE_RS_LDS_ALIGN
     // Staging of one step for whole-line stores (full grid only; budgeted
@@ -313,7 +324,8 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
             const bool interior = vec && g0 >= tr.lo && g1 <= end;
             const int64_t f0 = g0 + (int64_t)tid * kVec;
             const int lane = tid % kWave;
-            const int64_t fw = g0 + (int64_t)(tid / kWave) * (2 * kHalf);   // wave's first index
+            const int wv = kUniform ? __builtin_amdgcn_readfirstlane(tid / kWave) : tid / kWave;
+            const int64_t fw = g0 + (int64_t)wv * (2 * kHalf);   // wave's first index
             const int64_t fh = fw + lane * 4;
             if (interior && g1 <= pd.valid) {
                 // All loads are independent of the adds: they are all issued
@@ -329,11 +341,10 @@ __global__ __launch_bounds__(NT) void reduce_kernel(
                         // f - 1 (f is a multiple of 4, so f - 1 starts a
                         // dword); every dword read holds an element of the
                         // step's valid range, or the one before it, or the
-                        // one after it in the same dword. Wave-uniform. (An
-                        // 8-byte load per lane with the third dword taken
-                        // from the next lane over ds_bpermute measured 4%
-                        // slower on MI355X: each contributor then waits on
-                        // an LDS round trip after its load.)
+                        // one after it in the same dword. Wave-uniform.
+                        // (Measured on MI355X and not kept: 8-byte loads with
+                        // the third dword from the next lane, over ds_bpermute
+                        // or a DPP wavefront shift, both slower.)
                         const TIDE_GLOBAL u32x3_a4* gq = gbl<u32x3_a4>(g[c] + fh - 1);
 #pragma unroll
                         for (int u = 0; u < kUR; ++u)
