@@ -15,8 +15,8 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--placement-engine kernel|sdma|runtime] [--parts] [--victim] [--stock]
-                  [--slot-reuse] [--occupancy] [--graph] [--no-cpu-baseline]
-                  [--no-per-config]
+                  [--slot-reuse] [--occupancy] [--graph] [--fence-study] [--offsets]
+                  [--no-cpu-baseline] [--no-per-config]
 """
 import argparse
 import hashlib
@@ -596,6 +596,48 @@ def time_steps(torch, tide, grp, launch, steps, warmup, engine="kernel"):
     }
 
 
+def offset_rates(torch, tide, grp, offsets=(0, 1, 2, 3), reps=8):
+    """Reduce rate with every gradient moved to `off` bf16 elements past an
+    allocation's start (2 mod 4 bytes for odd `off`: the realigning loads),
+    and whether each output equals the aligned call's bit for bit. One copy
+    of the gradients is held at a time."""
+    plan = grp.plan
+    tide.reduce_scatter_bf16_fp32(plan, grp.g_tab, grp.out)
+    ref = grp.out.clone()
+    res = {}
+    for off in offsets:
+        views = []
+        for c in range(grp.cfg.L):
+            row = []
+            for p, (t, k) in enumerate(grp.cfg.shapes):
+                buf = torch.empty(t * k + 8, dtype=torch.bfloat16, device="cuda")
+                v = buf[off:off + t * k].view(t, k)
+                v.copy_(grp.grads[c][p])
+                row.append(v)
+            views.append(row)
+        tab = tide.grads_table(plan, views)
+        grp.out.fill_(float("nan"))
+        tide.reduce_scatter_bf16_fp32(plan, tab, grp.out)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(grp.out.view(torch.int32), ref.view(torch.int32)))
+        ts = []
+        for _ in range(reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record()
+            tide.reduce_scatter_bf16_fp32(plan, tab, grp.out)
+            e[1].record()
+            torch.cuda.synchronize()
+            ts.append(e[0].elapsed_time(e[1]))
+        ms = statistics.median(ts)
+        res["+%d" % off] = {"reduce_ms_median": round(ms, 4),
+                            "reduce_GBps": round(grp.rs_bytes / (ms / 1e3) / 1e9, 1),
+                            "equals_aligned_output": same}
+        log("bench: gradients at +%d elements: %s" % (off, json.dumps(res["+%d" % off])))
+        del views, tab
+        torch.cuda.empty_cache()
+    return res
+
+
 def sdma_placement(torch, tide, grp, reps=3):
     """Host wall time of the placement on the DMA engines (the call returns
     once its copies are done; median of `reps` calls)."""
@@ -678,6 +720,9 @@ def main():
                     help="trace where budgeted workgroups run, beside GEMM-shaped occupants")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step as prepared calls, eager and replayed from a HIP graph")
+    ap.add_argument("--offsets", action="store_true",
+                    help="also time the reduce with all gradients at 0-3 elements past an "
+                         "allocation's start")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle (timing and whole-output checks)")
     ap.add_argument("--no-per-config", action="store_true",
@@ -823,6 +868,11 @@ def main():
                                                tide.Launch(), gs, cs)}
         log("bench: victim %s" % json.dumps(victim))
 
+    offs = None
+    if args.offsets:
+        log("bench: gradient offsets")
+        offs = offset_rates(torch, tide, grp)
+
     fence = None
     if args.fence_study:
         fence = fence_study(torch, tide, plan, grads, out, shards, params, gs, cs)
@@ -904,6 +954,8 @@ def main():
         line["occupancy_probe"] = occ
     if fence is not None:
         line["fence_study"] = fence
+    if offs is not None:
+        line["gradient_offsets"] = offs
     if graph is not None:
         line["prepared_and_graph"] = graph
     print(json.dumps(line), flush=True)
