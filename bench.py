@@ -189,8 +189,71 @@ def ceilings(torch, tide, nbytes=4 << 30, nsrc=8, reps=5):
     return res
 
 
-def victim_slowdown(torch, tide, plan, grads, out, shards, params, launch, gs, cs, reps=3, nb=4,
-                    M=256):
+class SidePair:
+    """Two side streams, `gs` for a GEMM (or occupant) and `cs` for the
+    collective, that run at the same time. HIP maps streams onto a few
+    hardware queues (GPU_MAX_HW_QUEUES), and two streams on one queue run their
+    work one after the other. On MI355X a pair that ran concurrently when it
+    was made ran every GEMM of the victim protocol after the collective had
+    ended, minutes later in the same process. So `ensure()` checks the pair
+    again before each measurement and replaces it once it has become serial.
+    The check: a tiny kernel on gs completes while a 2 ms occupant
+    (tide_diag_occupy, one workgroup) still runs on cs. Under counter
+    collection, which serialises every kernel, no pair passes; after one
+    failed search `concurrent` stays False and no more streams are made."""
+
+    def __init__(self, torch, tide, tries=8, spin_us=2000):
+        self.torch, self.tide, self.tries, self.spin_us = torch, tide, tries, spin_us
+        self.trace = torch.zeros(3, dtype=torch.int64, device="cuda")
+        self.x = torch.zeros(1024, device="cuda")
+        self.x.add_(1.0)                         # kernels loaded before any timing
+        tide.diag_occupy(1, 64, 0, 100, self.trace)
+        torch.cuda.synchronize()
+        self.gs = self.cs = None
+        self.concurrent = False
+        self.searched_in_vain = False
+        self.pairs_made = 0
+        self.ensure()
+
+    def lag_ms(self):
+        torch = self.torch
+        lags = []
+        for _ in range(2):
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(self.cs)
+            self.tide.diag_occupy(1, 64, 0, self.spin_us * 100, self.trace, stream=self.cs)
+            with torch.cuda.stream(self.gs):
+                self.x.add_(1.0)
+                e1.record(self.gs)
+            torch.cuda.synchronize()
+            lags.append(e0.elapsed_time(e1))
+        return min(lags)          # a pair on one queue lags by the whole occupant every time
+
+    def ensure(self):
+        limit = 0.5 * self.spin_us / 1e3
+        if self.gs is not None and (self.searched_in_vain or self.lag_ms() < limit):
+            return self.concurrent
+        for _ in range(self.tries):
+            self.gs, self.cs = self.torch.cuda.Stream(), self.torch.cuda.Stream()
+            self.pairs_made += 1
+            lag = self.lag_ms()
+            if lag < limit:
+                log("bench: side stream pair %d runs concurrently (other stream done %.3f ms after "
+                    "the occupant started)" % (self.pairs_made - 1, lag))
+                self.concurrent = True
+                return True
+            log("bench: side stream pair %d runs serially (%.3f ms)" % (self.pairs_made - 1, lag))
+        log("bench: no concurrent pair of side streams in %d tries (kernels serialised, e.g. by "
+            "counter collection); GEMM-victim results will show streams_concurrent = false" % self.tries)
+        self.concurrent = False
+        self.searched_in_vain = True
+        return False
+
+
+def victim_slowdown(torch, tide, plan, grads, out, shards, params, launch, pair, reps=3, nb=4,
+                    M=256, attempts=3):
     """Slowdown of an Mx8192x8192 bf16 GEMM (M = 256: the pages' victim, which
     hipBLASLt runs as 128 workgroups, half the CUs) while the reduce-scatter +
     placement run on another stream (median GEMM time, concurrent vs alone).
@@ -206,6 +269,7 @@ def victim_slowdown(torch, tide, plan, grads, out, shards, params, launch, gs, c
     torch.cuda.synchronize()
 
     def gemm_times(n):
+        gs = pair.gs
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(n)]
         with torch.cuda.stream(gs):
@@ -215,6 +279,7 @@ def victim_slowdown(torch, tide, plan, grads, out, shards, params, launch, gs, c
                 b.record(gs)
         return evs
 
+    pair.ensure()
     alone = gemm_times(200)
     torch.cuda.synchronize()
     t_alone = statistics.median(a.elapsed_time(b) for a, b in alone)
@@ -222,26 +287,45 @@ def victim_slowdown(torch, tide, plan, grads, out, shards, params, launch, gs, c
     # GEMMs that run entirely inside the collective's window; if none does
     # (a full-grid collective is shorter than its queueing delay), count those
     # that overlap the window at all.
+    # When a repetition's first GEMM starts late (in the second half of the
+    # window), the pair is checked again: if it has become serial it is
+    # replaced and the repetition repeated; if it still runs concurrently, the
+    # GEMMs waited for CUs (as beside the full grid) and the repetition counts.
     res = []
+    tries = 0
     for _ in range(reps):
-        torch.cuda.synchronize()
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        cs.wait_stream(torch.cuda.current_stream())
-        c0.record(cs)
-        tide.reduce_scatter_bf16_fp32(plan, grads, out, stream=cs, launch=launch)
-        tide.allgather_place(plan, shards, params, stream=cs, launch=launch)
-        c1.record(cs)
-        evs = gemm_times(400)
-        torch.cuda.synchronize()
-        win = c0.elapsed_time(c1)
-        spans = [(c0.elapsed_time(a_), c0.elapsed_time(b_)) for a_, b_ in evs]
+        for _ in range(attempts):
+            tries += 1
+            pair.ensure()
+            cs = pair.cs
+            torch.cuda.synchronize()
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            cs.wait_stream(torch.cuda.current_stream())
+            c0.record(cs)
+            tide.reduce_scatter_bf16_fp32(plan, grads, out, stream=cs, launch=launch)
+            tide.allgather_place(plan, shards, params, stream=cs, launch=launch)
+            c1.record(cs)
+            evs = gemm_times(400)
+            torch.cuda.synchronize()
+            win = c0.elapsed_time(c1)
+            spans = [(c0.elapsed_time(a_), c0.elapsed_time(b_)) for a_, b_ in evs]
+            overlapped = pair.concurrent
+            if spans[0][0] < 0.5 * win or not pair.concurrent:
+                break
+            made = pair.pairs_made
+            pair.ensure()
+            if pair.pairs_made == made:
+                break
+            overlapped = False           # this repetition ran on the pair just replaced
+            log("bench: victim repetition ran on a serial stream pair (first GEMM at %.2f ms of a "
+                "%.2f ms window); repeated on a new pair" % (spans[0][0], win))
         inside = [e - s for s, e in spans if s >= 0 and e <= win]
         kind = "inside"
         if not inside:
             inside = [e - s for s, e in spans if s < win and e > 0]
             kind = "overlapping"
         if inside:
-            res.append((statistics.median(inside), win, len(inside), kind))
+            res.append((statistics.median(inside), win, len(inside), kind, overlapped))
     del A, Bs, C
     if not res:
         return {"gemm_ms_alone": round(t_alone, 4), "note": "no GEMM overlapped the collective"}
@@ -250,10 +334,11 @@ def victim_slowdown(torch, tide, plan, grads, out, shards, params, launch, gs, c
             "slowdown_pct": round(100.0 * (conc / t_alone - 1.0), 2),
             "collective_ms": round(statistics.median(r[1] for r in res), 3),
             "gemms_counted": int(statistics.median(r[2] for r in res)),
-            "gemms_counted_are": res[0][3] + " the collective window"}
+            "gemms_counted_are": res[0][3] + " the collective window",
+            "streams_concurrent": all(r[4] for r in res), "repetitions_run": tries}
 
 
-def fence_study(torch, tide, plan, grads, out, shards, params, gs, cs):
+def fence_study(torch, tide, plan, grads, out, shards, params, pair):
     """GEMM-victim slowdown under budgeted launch variants (workgroup lifetime
     300 / 100 / 50 us, LDS fence on and off), for the pages' victim (M = 256:
     128 hipBLASLt workgroups, half the CUs) and for one that fills the GPU in
@@ -282,12 +367,12 @@ def fence_study(torch, tide, plan, grads, out, shards, params, gs, cs):
         for M in (256, 4096):
             log("bench: fence study M=%d %s" % (M, name))
             entry["victim_M%d" % M] = victim_slowdown(torch, tide, plan, grads, out, shards, params,
-                                                       launch, gs, cs, M=M)
+                                                       launch, pair, M=M)
         res[name] = entry
     return res
 
 
-def occupancy_probe(torch, tide, plan, grads, out, shards, params, gs, cs, probes=500,
+def occupancy_probe(torch, tide, plan, grads, out, shards, params, pair, probes=500,
                     probe_wgs=128, probe_threads=256, probe_lds=42496, probe_us=40):
     """Where the budgeted collective's workgroups run, how long they live, and
     whether GEMM-shaped occupants (the 256x8192x8192 GEMM's hipBLASLt kernel
@@ -314,6 +399,8 @@ def occupancy_probe(torch, tide, plan, grads, out, shards, params, gs, cs, probe
         n_rs, n_ag = plan.trace_records(0, b), plan.trace_records(1, b)
         t_rs, t_ag = tide.trace_buffer(n_rs), tide.trace_buffer(n_ag)
         t_pr = tide.trace_buffer(probes * probe_wgs)
+        pair.ensure()
+        gs, cs = pair.gs, pair.cs
         torch.cuda.synchronize()
         cs.wait_stream(torch.cuda.current_stream())
         gs.wait_stream(torch.cuda.current_stream())
@@ -653,7 +740,7 @@ def sdma_placement(torch, tide, grp, reps=3):
             "engines": tide.dma_engine_count(torch.cuda.current_device())}
 
 
-def per_config_line(torch, tide, orc, name, args, gs, cs):
+def per_config_line(torch, tide, orc, name, args, pair):
     from oracle import check as oracle_check
     """Full-grid step, SDMA placement and the whole-output oracle check of one
     more group; for the Wan2.2 block also the budgeted GEMM-victim protocol."""
@@ -675,9 +762,9 @@ def per_config_line(torch, tide, orc, name, args, gs, cs):
         log("bench: per-config %s: GEMM victim" % name)
         res["victim_gemm_256x8192x8192"] = {
             "budgeted_16_4": victim_slowdown(torch, tide, grp.plan, grp.grads, grp.out, grp.shards,
-                                             grp.params, tide.budgeted(), gs, cs),
+                                             grp.params, tide.budgeted(), pair),
             "full_grid": victim_slowdown(torch, tide, grp.plan, grp.grads, grp.out, grp.shards,
-                                         grp.params, tide.Launch(), gs, cs)}
+                                         grp.params, tide.Launch(), pair)}
     if orc is not None:
         # The step's outputs are re-made with the kernel engine before the check.
         tide.reduce_scatter_bf16_fp32(grp.plan, grp.g_tab, grp.out)
@@ -825,11 +912,10 @@ def main():
         t["reduce_GBps_mean"] / parts["ceilings"]["reduce_pattern_GBps"], 4)
     log("bench: ceilings %s" % json.dumps(parts["ceilings"]))
 
-    # Two side streams, created once: a GEMM (or occupant) stream and a
-    # collective stream. Reusing them keeps every measurement on the same pair
-    # of hardware queues (streams created later may share a queue with an
-    # earlier one, which would serialise the two).
-    gs, cs = torch.cuda.Stream(), torch.cuda.Stream()
+    # Two side streams, a GEMM (or occupant) stream and a collective stream,
+    # checked to run concurrently before every measurement that needs them.
+    pair = SidePair(torch, tide)
+    parts["side_streams_concurrent"] = pair.concurrent
     graph = None
     if args.graph:
         log("bench: prepared calls and graph replay")
@@ -839,7 +925,7 @@ def main():
     occ = None
     if args.occupancy:
         log("bench: occupancy probe")
-        occ = occupancy_probe(torch, tide, plan, grads, out, shards, params, gs, cs)
+        occ = occupancy_probe(torch, tide, plan, grads, out, shards, params, pair)
         log("bench: occupancy %s" % json.dumps(occ))
 
     slot = None
@@ -860,12 +946,12 @@ def main():
     if args.victim:
         log("bench: GEMM victim, budgeted")
         victim = {"budgeted_16_4": victim_slowdown(torch, tide, plan, grads, out, shards, params,
-                                                   tide.budgeted(), gs, cs),
+                                                   tide.budgeted(), pair),
                   "budgeted_16_4_without_lds_reservation": victim_slowdown(
                       torch, tide, plan, grads, out, shards, params,
-                      tide.budgeted(flags=tide.FLAG_NO_LDS_FENCE), gs, cs),
+                      tide.budgeted(flags=tide.FLAG_NO_LDS_FENCE), pair),
                   "full_grid": victim_slowdown(torch, tide, plan, grads, out, shards, params,
-                                               tide.Launch(), gs, cs)}
+                                               tide.Launch(), pair)}
         log("bench: victim %s" % json.dumps(victim))
 
     offs = None
@@ -875,7 +961,7 @@ def main():
 
     fence = None
     if args.fence_study:
-        fence = fence_study(torch, tide, plan, grads, out, shards, params, gs, cs)
+        fence = fence_study(torch, tide, plan, grads, out, shards, params, pair)
         log("bench: fence study %s" % json.dumps(fence))
 
     cpu = None
@@ -903,7 +989,7 @@ def main():
         per_config = {}
         for name in ("llama70b_layer", "qwen3_moe_layer", "wan22_dit_block"):
             if name != cfg.name:
-                per_config[name] = per_config_line(torch, tide, orc, name, args, gs, cs)
+                per_config[name] = per_config_line(torch, tide, orc, name, args, pair)
         per_config["all_at_least_70pct"] = all(
             v["pct_of_8TBps"] >= 70.0 for v in per_config.values() if isinstance(v, dict)) and \
             100.0 * value / HBM_PEAK_GBPS >= 70.0
@@ -914,6 +1000,7 @@ def main():
             per_config["all_oracle_bit_exact"] = all(
                 v.get("oracle_bit_exact", False) for v in per_config.values() if isinstance(v, dict))
 
+    parts["side_stream_pairs_made"] = pair.pairs_made
     traffic = counter_traffic(cfg.name)
     clocks = gpu_clocks()
     line = {
