@@ -77,9 +77,9 @@ class DeviceGuard {
 // a CU held by a collective workgroup delays that GEMM workgroup until the
 // collective's ends, so the GEMM slows by about the collective workgroup's
 // life over the GEMM's. Measured with a 0.4 ms M = 4096 GEMM beside the Wan
-// block: 28% at 300 us, 7.6% at 100 us, 2.2% at 50 us (the pages' 256-row
-// victim, 128 workgroups: 1.2% at either length). The collective alone takes
-// 17% longer at 50 us (more launches).
+// block, three runs: 30-36% at 300 us, 8-10% at 100 us, 2.4-3.3% at 50 us
+// (the pages' 256-row victim, 128 workgroups: 0.2-1.9% at any of the three).
+// The collective alone takes 16% longer at 50 us (6x the launches).
 constexpr int kDefaultReduceBlocks = 16;
 constexpr int kDefaultPlaceBlocks = 4;
 constexpr int kDefaultMaxLaunchUs = 50;
