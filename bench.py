@@ -725,6 +725,29 @@ def offset_rates(torch, tide, grp, offsets=(0, 1, 2, 3), reps=8):
     return res
 
 
+def one_gpu_share(torch, tide, grp, reps=10):
+    """The reduce one GPU of an L-GPU node runs: its N / L ranks (here ranks
+    [0, N / L)), full grid, median of `reps` calls between HIP events on the
+    stream. (The placement is the whole group on every GPU, as in the step.)"""
+    cfg, plan = grp.cfg, grp.plan
+    share = max(1, cfg.N // cfg.L)
+    launch = tide.Launch(rank_begin=0, rank_end=share)
+    valid = sum(min(t * k, share * plan.param(p)[3]) for p, (t, k) in enumerate(cfg.shapes))
+    nbytes = 2 * cfg.L * valid + 4 * share * plan.S
+    tide.reduce_scatter_bf16_fp32(plan, grp.g_tab, grp.out, launch=launch)
+    ts = []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        tide.reduce_scatter_bf16_fp32(plan, grp.g_tab, grp.out, launch=launch)
+        e[1].record()
+        torch.cuda.synchronize()
+        ts.append(e[0].elapsed_time(e[1]))
+    ms = statistics.median(ts)
+    return {"ranks": [0, share], "reduce_bytes": nbytes, "reduce_ms_median": round(ms, 4),
+            "reduce_GBps": round(nbytes / (ms / 1e3) / 1e9, 1)}
+
+
 def sdma_placement(torch, tide, grp, reps=3):
     """Host wall time of the placement on the DMA engines (the call returns
     once its copies are done; median of `reps` calls)."""
@@ -859,6 +882,8 @@ def main():
         "reduce_launches_per_call": plan.launch_count(0, launch),
         "placement_launches_per_call": plan.launch_count(1, launch),
     }
+    parts["one_gpu_share"] = one_gpu_share(torch, tide, grp)
+    log("bench: one GPU's share %s" % json.dumps(parts["one_gpu_share"]))
     if args.placement_engine != "sdma":
         parts["placement_sdma"] = sdma_placement(torch, tide, grp)
         log("bench: SDMA placement %s" % json.dumps(parts["placement_sdma"]))
