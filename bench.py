@@ -1021,6 +1021,7 @@ def main():
         wv = per_config.get("wan22_dit_block", {}).get("victim_gemm_256x8192x8192")
         if wv and "slowdown_pct" in wv["budgeted_16_4"]:
             per_config["wan22_budgeted_gemm_slowdown_pct"] = wv["budgeted_16_4"]["slowdown_pct"]
+            per_config["wan22_victim_streams_concurrent"] = wv["budgeted_16_4"]["streams_concurrent"]
         if orc is not None:
             per_config["all_oracle_bit_exact"] = all(
                 v.get("oracle_bit_exact", False) for v in per_config.values() if isinstance(v, dict))
