@@ -483,8 +483,9 @@ tide_status tide_diag_occupy(int32_t workgroups, int32_t threads, int32_t lds_by
  *           aligned, nsrc in [1, 8]; dst holds n fp32).
  * n is a multiple of 2048 (kinds 0-2, bytes) or 1024 (kind 3, elements).
  * workgroups = 0: a full grid of 128-thread workgroups (the full-grid
- * kernels' shape); > 0: that many 1024-thread workgroups, each on a CU of its
- * own, which gives the per-CU ceiling of the budgeted kernels' shape.
+ * kernels' shape); > 0: that many 1024-thread workgroups, the budgeted
+ * kernels' shape (with fewer workgroups than CUs the dispatcher spreads them
+ * one to a CU, so the rate per workgroup is the per-CU ceiling).
  * Async on `stream`. Errors: INVALID_ARG, ALIGNMENT, HIP.
  */
 tide_status tide_diag_stream(int32_t kind, const void* const* srcs, int32_t nsrc, void* dst,
